@@ -1,0 +1,20 @@
+"""fp64 CPU oracle for MLA decode with weight absorption.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares
+no code with the HIP library and imports nothing from it.
+"""
+from .mla_oracle import (  # noqa: F401
+    rope_inverse_frequencies,
+    rope_rotate,
+    absorb_query,
+    reconstruct_keys,
+    reconstruct_values,
+    decode_sequence,
+    merge_partials,
+    value_up_projection,
+    mla_cache_elements_per_token,
+    mla_cache_bytes_per_token,
+    mha_cache_bytes_per_token,
+    gqa_cache_bytes_per_token,
+)
