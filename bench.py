@@ -1,0 +1,199 @@
+"""Benchmark of one MLA decode step (weight absorption, latent cache) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3_b64]
+
+A step is the whole hot path over one batch: append the step's own latents to
+the cache, absorb the query through W_UK (+ query RoPE), decode attention over
+the latent cache split into token-balanced work units, log-sum-exp combine of
+the partials, and the W_UV up-projection.  Inputs are seeded synthetic
+DeepSeek-V3-shaped tensors already resident in HBM when timing starts.
+
+Prints one JSON line: algorithmic GB/s of the step (value), decode tokens/s,
+the roofline of the dominant kernel (mla_decode) measured with HIP events on
+the launch stream, and the fp64 CPU oracle timed on a bounded sample of the
+same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="v3_b64")
+    ap.add_argument("--num-splits", type=int, default=0, help="0 = library default for the batch")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=16, help="heads of one sequence in the CPU sample")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(w, ctx):
+    """Bytes the method itself must move (no partials, padding or re-reads)."""
+    eb = 2 if w.dtype == "bf16" else 4
+    B, nq = w.batch, w.n_q
+    cache = int(ctx.sum()) * w.row * eb
+    q_in = B * nq * w.n_h * (w.d_nope + w.d_rope) * eb
+    q_abs = B * nq * w.n_h * (w.d_c + w.d_rope) * eb
+    wts = w.n_h * w.d_c * (w.d_nope + w.d_v) * eb
+    out = B * nq * w.n_h * w.d_v * 4
+    append = B * nq * w.row * eb * 2
+    u_lse = B * nq * w.n_h * (w.d_c + 1) * 4
+    return {"step": cache + q_in + wts + out + append, "decode": cache + q_abs + u_lse, "cache": cache}
+
+
+def decode_flops(w, ctx, pos):
+    """2 * rows * (d_c + d_rope + d_c) per visible (query, cached token) pair."""
+    import numpy as np
+    visible = np.minimum(pos + 1, ctx[:, None]).sum()
+    return int(visible) * w.n_h * 2 * (2 * w.d_c + w.d_rope)
+
+
+def cpu_baseline(w, heads_n):
+    """fp64 oracle on one sequence and a subset of its heads."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    ctx = W.context_lengths(w)
+    b = int(np.argmin(ctx)) if w.ctx is None else 0
+    heads = list(range(min(heads_n, w.n_h)))
+    rows = W.cache_rows(w, b, 0, int(ctx[b]))
+    wt, q = W.weights(w), W.queries(w)
+    pos = W.positions(w, ctx)
+    t0 = time.perf_counter()
+    oracle.decode_sequence(q["q_nope"][b], q["q_rope"][b], pos[b], rows["c_kv"], rows["k_rope_raw"],
+                           wt["w_uk"], wt["w_uv"], w.sm_scale, w.rope_base, heads=heads)
+    dt = time.perf_counter() - t0
+    eb = 2 if w.dtype == "bf16" else 4
+    # cache bytes the sample consumed, counted per head (the oracle's cost scales with heads)
+    sample_bytes = int(ctx[b]) * w.row * eb * len(heads) / w.n_h
+    return {"value": round(sample_bytes / dt / 1e9, 6), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"sequence {b} (ctx {int(ctx[b])}), {len(heads)} of {w.n_h} heads, fp64 reconstruct-then-"
+                      f"attend; GB/s = cache bytes x heads/{w.n_h} / {dt:.2f} s",
+            "seconds": round(dt, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); multi-GPU sharding of this "
+              f"path is a design note, not a measured configuration.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import mla_latent_kv_02_amd as mla
+    import workloads as W
+    from mla_latent_kv_02_amd.plan import default_num_splits
+    from mla_latent_kv_02_amd.step import DecodeStep
+    from workloads.device import stage
+
+    w = W.get(args.workload)
+    log(f"staging {w.name}: {w.description}")
+    t0 = time.perf_counter()
+    st = stage(w)
+    log(f"staged in {time.perf_counter() - t0:.1f} s")
+    ctx, pos = st["ctx_host"], st["positions_host"]
+    num_splits = args.num_splits or default_num_splits(int(ctx.sum()), w.n_q, w.n_h)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    step = DecodeStep(st["dims"], w.batch, w.n_q, num_splits, tdt)
+
+    # the step's own latents: the last n_q rows of every sequence (raw, before rotation)
+    seq_ids = np.repeat(np.arange(w.batch, dtype=np.int32), w.n_q)
+    tok = pos.reshape(-1).astype(np.int32)
+    raw = torch.empty((len(seq_ids), w.row), dtype=tdt, device="cuda")
+    if w.dtype == "bf16":
+        table = torch.from_numpy(W.normal_table_bf16_bits().view(np.int16)).cuda()
+        sd, td = torch.from_numpy(seq_ids).cuda(), torch.from_numpy(tok).cuda()
+        W.fill_cache_rows_device(w, sd.data_ptr(), td.data_ptr(), len(seq_ids), table.data_ptr(), raw.data_ptr(),
+                                 torch.cuda.current_stream().cuda_stream)
+    else:
+        rows = [W.cache_rows(w, int(b), int(t), int(t) + 1) for b, t in zip(seq_ids, tok)]
+        raw.copy_(torch.from_numpy(np.concatenate([np.concatenate([r["c_kv"], r["k_rope_raw"]], 1) for r in rows])))
+        sd, td = torch.from_numpy(seq_ids).cuda(), torch.from_numpy(tok).cuda()
+    new_tokens = (sd, td, raw[:, :w.d_c], raw[:, w.d_c:])
+
+    stream = torch.cuda.current_stream()
+    d = st["dims"]
+
+    def run_step(ev=None):
+        mla.mla_cache_append(d, st["cache"], *new_tokens)
+        mla.mla_absorb_q(d, st["q_nope"], st["q_rope"], st["positions"], st["w_uk"], step.q_lat, step.q_pe)
+        if ev is not None:
+            ev[0].record(stream)
+        mla.mla_decode(d, step.q_lat, step.q_pe, st["cache"], st["positions"], num_splits, step.u_part,
+                       step.lse_part)
+        if ev is not None:
+            ev[1].record(stream)
+        mla.mla_combine(d, st["cache"].ctx_lens, num_splits, step.u_part, step.lse_part, step.u, step.lse)
+        mla.mla_out_proj(d, step.u, st["w_uv"], step.out)
+
+    log(f"num_splits={num_splits}; warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for k in range(args.steps):
+        run_step(evs[k])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_step = start.elapsed_time(end) / args.steps
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_avg = sum(dec_ms) / len(dec_ms)
+    log(f"step {ms_step * 1e3:.1f} us (wall {wall / args.steps * 1e6:.1f} us); decode kernel avg "
+        f"{dec_avg * 1e3:.1f} us (min {min(dec_ms) * 1e3:.1f})")
+
+    nbytes = algorithmic_bytes(w, ctx)
+    flops = decode_flops(w, ctx, pos)
+    value = nbytes["step"] / (ms_step * 1e-3) / 1e9
+    achieved = nbytes["decode"] / (dec_avg * 1e-3) / 1e9
+    result = {
+        "metric": "MLA decode latent-cache GB/s + tokens/s (DeepSeek-V3 shapes), % of roofline",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic (seeded Philox N(0,1) latents/queries, "
+        "N(0,1/d_c) weights)",
+        "config": {"workload": w.name, "description": w.description, "batch": w.batch, "n_q": w.n_q,
+                   "n_h": w.n_h, "d_c": w.d_c, "d_rope": w.d_rope, "d_nope": w.d_nope, "d_v": w.d_v,
+                   "context_tokens": int(ctx.sum()), "block_size": w.block_size, "num_splits": num_splits},
+        "tokens_per_s": round(w.batch * w.n_q / (ms_step * 1e-3), 1),
+        "kv_tokens_per_s": round(float(ctx.sum()) / (ms_step * 1e-3), 1),
+        "step_bytes": nbytes["step"],
+        "roofline": {"kernel": "mla_decode (decode_mfma_kernel)", "bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": nbytes["decode"], "avg_launch_us": round(dec_avg * 1e3, 3),
+                     "mfma_tflops": round(flops / (dec_avg * 1e-3) / 1e12, 2),
+                     "mfma_frac": round(flops / (dec_avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on a CPU sample")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

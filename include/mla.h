@@ -1,0 +1,163 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) Multi-Head Latent Attention decode
+ * library: one decode step with weight absorption over a latent KV cache.
+ *
+ * Pages cited (by title):
+ *   [Huny]    "Multi-Head Latent Attention(MLA) 아키텍처 해부: Low-Rank 압축부터
+ *             Decoupled RoPE·Weight Absorption(행렬 흡수)과 KV Cache 93% 절감
+ *             원리까지", Huny's Dev Blog.
+ *   [Tbr8]    "DeepSeek MLA（多头潜在注意力）深度解析", tbr8.org.
+ *   [Ikmyung] the attention / MHA / GQA / DeepSeek MLA guide, ikmyungterran.us.
+ *
+ * The step, per sequence b, query token j and head i:
+ *   q_lat = q^C_i (W_i^UK)^T                     (key absorption, [Huny] §3.1)
+ *   q_pe  = RoPE(q^R_i, position)                (decoupled RoPE, [Huny] §2.2)
+ *   s_t   = scale * (q_lat . c_t + q_pe . k^R_t) for cached tokens t <= position
+ *                                                 ([Huny] §2.2 score split, §3.1)
+ *   a     = softmax(s)                           ([Ikmyung] §1.3-1.4)
+ *   u     = sum_t a_t c_t                        (value-side absorption, [Huny] §3.2)
+ *   o     = u W_i^UV                             ([Huny] §3.2)
+ * The cache row of token t is [c_t (d_c) | k^R_t (d_rope)]: the latent and the
+ * positional key shared by all heads, the latter stored already rotated to
+ * position t ([Huny] §2.2).  Keys and values are never materialised.
+ *
+ * Conventions for every entry point:
+ *   - All array arguments are DEVICE pointers to row-major arrays whose shape
+ *     is given in the comment; the caller owns all memory.  The library never
+ *     allocates, frees or synchronises; each call enqueues work on `stream`
+ *     (a hipStream_t passed as void*, NULL = default stream) and returns.
+ *   - Argument errors are found on the host before anything is enqueued and
+ *     return MLA_ERR_INVALID_ARG; a shape the compiled kernels do not cover
+ *     returns MLA_ERR_UNSUPPORTED; a failed launch returns MLA_ERR_HIP.
+ *   - Device-side contents (context lengths, positions, block ids) are the
+ *     caller's contract and are not checked: ctx_lens[b] >= 0, positions in
+ *     [0, ctx_lens[b]), block ids in [0, number of blocks).
+ *   - The library keeps no mutable global state; concurrent calls on
+ *     different streams are safe when their output buffers do not overlap.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1,
+  MLA_ERR_UNSUPPORTED = 2,
+  MLA_ERR_HIP = 3
+} mla_status_t;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype_t;
+
+/* Head geometry.  n_h query heads; d_c latent width; d_rope positional-key
+ * width (even); d_nope per-head content width of q/k; d_v per-head value
+ * width.  sm_scale = 0 selects 1/sqrt(d_nope + d_rope) (the q/k width,
+ * [Ikmyung] §1.3).  rope_base = 0 selects 10000.  RoPE rotates each pair of
+ * adjacent elements (2k, 2k+1) by position * rope_base^(-2k/d_rope). */
+typedef struct {
+  int32_t n_h, d_c, d_rope, d_nope, d_v;
+  float sm_scale;
+  float rope_base;
+} mla_dims_t;
+
+/* Latent cache ([Huny] §2.2; paging per [Tbr8] §6.1).
+ * Row of one token = d_c + d_rope elements of `dtype`: [c_kv | rotated k_rope].
+ *   Contiguous (block_size == 0): token t of sequence b is the row at element
+ *     offset b * seq_stride + t * (d_c + d_rope) of `data`.
+ *   Paged (block_size > 0): `data` is a pool [n_blocks][block_size][row];
+ *     token t of sequence b is row (t % block_size) of block
+ *     block_table[b * max_blocks + t / block_size].
+ * ctx_lens [B]: number of cached tokens of each sequence (the query tokens'
+ * own rows included).  `data` must be 16-byte aligned. */
+typedef struct {
+  mla_dtype_t dtype;
+  void *data;
+  int64_t seq_stride;          /* elements; contiguous layout only */
+  int32_t block_size;          /* 0 = contiguous */
+  const int32_t *block_table;  /* [B][max_blocks], paged layout only */
+  int32_t max_blocks;
+  const int32_t *ctx_lens;     /* [B] */
+} mla_cache_t;
+
+/* Key absorption and query RoPE ([Huny] §3.1, §2.2; [Tbr8] §5.3).
+ *   q_nope    [B][n_q][n_h][d_nope]   dtype dt
+ *   q_rope    [B][n_q][n_h][d_rope]   dtype dt, before rotation
+ *   positions [B][n_q]                int32, token position of each query
+ *   w_uk      [n_h][d_c][d_nope]      dtype dt (W_i^UK of head i)
+ *   q_lat     [B][n_q][n_h][d_c]      dtype dt, out: q^C_i (W_i^UK)^T
+ *   q_pe      [B][n_q][n_h][d_rope]   dtype dt, out: rotated q^R_i
+ * bf16 accumulates in fp32 and rounds the outputs to nearest even. */
+mla_status_t mla_absorb_q(const mla_dims_t *dims, int32_t B, int32_t n_q, mla_dtype_t dt,
+                          const void *q_nope, const void *q_rope, const int32_t *positions,
+                          const void *w_uk, void *q_lat, void *q_pe, void *stream);
+
+/* Number of partial slots mla_decode may write for a batch of B sequences
+ * split into num_splits token-balanced work units: num_splits + B - 1. */
+int64_t mla_num_partials(int32_t B, int32_t num_splits);
+
+/* Decode attention over the latent cache, split-KV ([Huny] §2.2, §3.1, §3.2).
+ * The tokens of all sequences, taken in order (sequence 0 first), are cut
+ * into num_splits consecutive ranges of ceil(sum ctx / num_splits) tokens;
+ * each range is one work unit.  Every (sequence, work unit) pair that shares
+ * tokens produces one partial: the softmax restricted to those tokens,
+ *   u_part[p][j][i][:] = sum_t a_t c_t / sum_t a_t,
+ *   lse_part[p][j][i]  = log sum_t exp(s_t)        (natural log),
+ * with u = 0, lse = -inf when no token of the range is visible to query j.
+ * Partials of sequence b occupy consecutive slots p in order of their token
+ * ranges; the slot layout is an implementation detail read by mla_combine.
+ *   q_lat     [B][n_q][n_h][d_c]      cache dtype (from mla_absorb_q)
+ *   q_pe      [B][n_q][n_h][d_rope]   cache dtype, rotated
+ *   positions [B][n_q]                query j of sequence b attends to tokens
+ *                                     t <= positions[b][j]
+ *   u_part    [mla_num_partials(B, num_splits)][n_q][n_h][d_c]  fp32, out
+ *   lse_part  [mla_num_partials(B, num_splits)][n_q][n_h]       fp32, out
+ * Requires 1 <= num_splits. */
+mla_status_t mla_decode(const mla_dims_t *dims, int32_t B, int32_t n_q, const void *q_lat,
+                        const void *q_pe, const mla_cache_t *cache, const int32_t *positions,
+                        int32_t num_splits, float *u_part, float *lse_part, void *stream);
+
+/* Log-sum-exp merge of the partials of each sequence (split-KV combine).
+ * With L = log sum_k exp(lse_k) over the partials k of (b, j, i):
+ *   u[b][j][i][:] = sum_k exp(lse_k - L) u_k,   lse[b][j][i] = L;
+ * u = 0, lse = -inf when every partial is empty.  ctx_lens and num_splits
+ * must be those given to mla_decode.
+ *   u   [B][n_q][n_h][d_c] fp32, out;  lse [B][n_q][n_h] fp32, out (may be NULL) */
+mla_status_t mla_combine(const mla_dims_t *dims, int32_t B, int32_t n_q, const int32_t *ctx_lens,
+                         int32_t num_splits, const float *u_part, const float *lse_part,
+                         float *u, float *lse, void *stream);
+
+/* Value up-projection o_i = u_i W_i^UV ([Huny] §3.2).
+ *   u    [B][n_q][n_h][d_c]   fp32
+ *   w_uv [n_h][d_c][d_v]      dtype w_dt
+ *   out  [B][n_q][n_h][d_v]   fp32, out
+ * With bf16 weights the fp32 u is split into a bf16 high part and a bf16
+ * residual and both are multiplied (fp32 accumulation). */
+mla_status_t mla_out_proj(const mla_dims_t *dims, int32_t B, int32_t n_q, const float *u,
+                          mla_dtype_t w_dt, const void *w_uv, float *out, void *stream);
+
+/* Write n new tokens into the cache: token k belongs to sequence seq_ids[k]
+ * at position positions[k]; its row becomes [c_kv_new[k] | RoPE(k_rope_new[k],
+ * positions[k])] ([Huny] §2.2: the positional key is cached rotated).  Inputs
+ * have the cache dtype; row k of c_kv_new starts at element k * c_kv_stride
+ * and row k of k_rope_new at element k * k_rope_stride.  The caller makes
+ * sure the destination rows exist (block table filled).  ctx_lens is not
+ * read or updated. */
+mla_status_t mla_cache_append(const mla_dims_t *dims, const mla_cache_t *cache, int32_t n,
+                              const int32_t *seq_ids, const int32_t *positions,
+                              const void *c_kv_new, int64_t c_kv_stride,
+                              const void *k_rope_new, int64_t k_rope_stride, void *stream);
+
+/* Static description of a status code. */
+const char *mla_status_string(mla_status_t status);
+
+/* Library version string. */
+const char *mla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_H */

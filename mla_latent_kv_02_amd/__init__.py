@@ -1,0 +1,24 @@
+"""MLA decode with weight absorption for MI355X (gfx950).
+
+The computation lives in libmla.so (C ABI in include/mla.h, HIP kernels in
+csrc/); this package is its thin Python binding.  Importing it does not load
+the library; the first call does, and fails loudly if it is not built.
+"""
+from ._binding import (  # noqa: F401
+    BF16,
+    EXPORTED,
+    F32,
+    LIB_PATH,
+    Dims,
+    LatentCache,
+    MlaError,
+    load_library,
+    mla_absorb_q,
+    mla_cache_append,
+    mla_combine,
+    mla_decode,
+    mla_num_partials,
+    mla_out_proj,
+)
+
+__version__ = "0.1.0"

@@ -1,0 +1,79 @@
+// Internal launchers: host-side entry points of the kernels (no validation;
+// the C ABI in mla_api.cpp checks every argument first).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla_device.h"
+
+namespace mla {
+
+struct DecodeParams {
+  const void* q_lat;
+  const void* q_pe;
+  CacheView cache;
+  const int32_t* ctx_lens;
+  const int32_t* positions;
+  float* u_part;
+  float* lse_part;
+  int B, n_q, n_h, d_c, d_rope, num_splits;
+  bool bf16;
+  float sm_scale;
+};
+
+// bf16 cache, d_c = 512, d_rope = 64, n_h % 32 == 0.
+hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
+int decode_mfma_smem_bytes();
+// Any dims, fp32 or bf16 cache (fp32 arithmetic).
+hipError_t launch_decode_generic(const DecodeParams& p, hipStream_t stream);
+
+struct CombineParams {
+  const int32_t* ctx_lens;
+  const float* u_part;
+  const float* lse_part;
+  float* u;
+  float* lse;
+  int B, n_q, n_h, d_c, num_splits;
+};
+hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+
+struct AbsorbParams {
+  const void* q_nope;
+  const void* q_rope;
+  const int32_t* positions;
+  const void* w_uk;
+  void* q_lat;
+  void* q_pe;
+  int B, n_q, n_h, d_c, d_rope, d_nope;
+  bool bf16;
+  float rope_base;
+};
+hipError_t launch_absorb(const AbsorbParams& p, hipStream_t stream);
+
+struct OutProjParams {
+  const float* u;
+  const void* w_uv;
+  float* out;
+  int B, n_q, n_h, d_c, d_v;
+  bool bf16;
+};
+hipError_t launch_out_proj(const OutProjParams& p, hipStream_t stream);
+
+struct AppendParams {
+  CacheView cache;
+  void* cache_data;
+  int n;
+  const int32_t* seq_ids;
+  const int32_t* positions;
+  const void* c_kv;
+  int64_t c_kv_stride;
+  const void* k_rope;
+  int64_t k_rope_stride;
+  int d_c, d_rope;
+  bool bf16;
+  float rope_base;
+};
+hipError_t launch_cache_append(const AppendParams& p, hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,149 @@
+// C ABI of the MLA decode library: argument validation and kernel dispatch.
+// Every check runs on the host before anything is enqueued.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/mla.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kMaxSplits = 1 << 20;
+
+bool dims_ok(const mla_dims_t* d) {
+  return d && d->n_h >= 1 && d->d_c >= 8 && d->d_c % 8 == 0 && d->d_rope >= 2 && d->d_rope % 8 == 0 &&
+         d->d_nope >= 1 && d->d_v >= 1 && d->n_h <= 65535 && d->d_c <= (1 << 16) &&
+         d->d_rope <= (1 << 16) && d->d_nope <= (1 << 16) && d->d_v <= (1 << 16) &&
+         isfinite(d->sm_scale) && d->sm_scale >= 0.f && isfinite(d->rope_base) && d->rope_base >= 0.f;
+}
+bool dtype_ok(mla_dtype_t t) { return t == MLA_F32 || t == MLA_BF16; }
+float scale_of(const mla_dims_t* d) {
+  return d->sm_scale > 0.f ? d->sm_scale : 1.0f / sqrtf((float)(d->d_nope + d->d_rope));
+}
+float base_of(const mla_dims_t* d) { return d->rope_base > 0.f ? d->rope_base : 10000.0f; }
+
+bool cache_ok(const mla_cache_t* c, const mla_dims_t* d) {
+  if (!c || !c->data || !c->ctx_lens || !dtype_ok(c->dtype)) return false;
+  if (reinterpret_cast<uintptr_t>(c->data) % 16) return false;
+  if (c->block_size < 0) return false;
+  if (c->block_size > 0) return c->block_table && c->max_blocks >= 1;
+  return c->seq_stride >= 0;
+}
+
+mla::CacheView view_of(const mla_cache_t* c, const mla_dims_t* d) {
+  mla::CacheView v;
+  v.data = c->data;
+  v.seq_stride = c->seq_stride;
+  v.block_table = c->block_table;
+  v.block_size = c->block_size;
+  v.max_blocks = c->max_blocks;
+  v.row = d->d_c + d->d_rope;
+  return v;
+}
+
+mla_status_t from_hip(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(mla_status_t s) {
+  switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MLA_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+const char* mla_version(void) { return "mla-mi355x 0.1.0 (gfx950)"; }
+
+int64_t mla_num_partials(int32_t B, int32_t num_splits) {
+  if (B < 0 || num_splits < 1) return -1;
+  return B == 0 ? 0 : (int64_t)num_splits + B - 1;
+}
+
+mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t B, int32_t n_q, mla_dtype_t dt,
+                          const void* q_nope, const void* q_rope, const int32_t* positions,
+                          const void* w_uk, void* q_lat, void* q_pe, void* stream) {
+  if (!dims_ok(dims) || B < 0 || n_q < 1 || !dtype_ok(dt)) return MLA_ERR_INVALID_ARG;
+  if (B == 0) return MLA_OK;
+  if (!q_nope || !q_rope || !positions || !w_uk || !q_lat || !q_pe) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)B * n_q > (1 << 24)) return MLA_ERR_UNSUPPORTED;
+  mla::AbsorbParams p;
+  p.q_nope = q_nope; p.q_rope = q_rope; p.positions = positions; p.w_uk = w_uk;
+  p.q_lat = q_lat; p.q_pe = q_pe;
+  p.B = B; p.n_q = n_q; p.n_h = dims->n_h; p.d_c = dims->d_c; p.d_rope = dims->d_rope;
+  p.d_nope = dims->d_nope; p.bf16 = dt == MLA_BF16; p.rope_base = base_of(dims);
+  if ((size_t)16 * p.d_nope * sizeof(float) > 64 * 1024) return MLA_ERR_UNSUPPORTED;
+  return from_hip(mla::launch_absorb(p, (hipStream_t)stream));
+}
+
+mla_status_t mla_decode(const mla_dims_t* dims, int32_t B, int32_t n_q, const void* q_lat,
+                        const void* q_pe, const mla_cache_t* cache, const int32_t* positions,
+                        int32_t num_splits, float* u_part, float* lse_part, void* stream) {
+  if (!dims_ok(dims) || B < 0 || n_q < 1 || num_splits < 1 || num_splits > kMaxSplits)
+    return MLA_ERR_INVALID_ARG;
+  if (B == 0) return MLA_OK;
+  if (!q_lat || !q_pe || !positions || !u_part || !lse_part || !cache_ok(cache, dims))
+    return MLA_ERR_INVALID_ARG;
+  if ((int64_t)n_q * dims->n_h > 65535) return MLA_ERR_UNSUPPORTED;
+  mla::DecodeParams p;
+  p.q_lat = q_lat; p.q_pe = q_pe; p.cache = view_of(cache, dims); p.ctx_lens = cache->ctx_lens;
+  p.positions = positions; p.u_part = u_part; p.lse_part = lse_part;
+  p.B = B; p.n_q = n_q; p.n_h = dims->n_h; p.d_c = dims->d_c; p.d_rope = dims->d_rope;
+  p.num_splits = num_splits; p.bf16 = cache->dtype == MLA_BF16; p.sm_scale = scale_of(dims);
+  const bool fast = p.bf16 && p.d_c == 512 && p.d_rope == 64 && p.n_h % 32 == 0;
+  if (fast) return from_hip(mla::launch_decode_mfma(p, (hipStream_t)stream));
+  if (p.d_c + p.d_rope > 2048 || p.d_c > 1024) return MLA_ERR_UNSUPPORTED;
+  return from_hip(mla::launch_decode_generic(p, (hipStream_t)stream));
+}
+
+mla_status_t mla_combine(const mla_dims_t* dims, int32_t B, int32_t n_q, const int32_t* ctx_lens,
+                         int32_t num_splits, const float* u_part, const float* lse_part, float* u,
+                         float* lse, void* stream) {
+  if (!dims_ok(dims) || B < 0 || n_q < 1 || num_splits < 1 || num_splits > kMaxSplits)
+    return MLA_ERR_INVALID_ARG;
+  if (B == 0) return MLA_OK;
+  if (!ctx_lens || !u_part || !lse_part || !u) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)n_q * dims->n_h > 65535 * 4) return MLA_ERR_UNSUPPORTED;
+  mla::CombineParams p;
+  p.ctx_lens = ctx_lens; p.u_part = u_part; p.lse_part = lse_part; p.u = u; p.lse = lse;
+  p.B = B; p.n_q = n_q; p.n_h = dims->n_h; p.d_c = dims->d_c; p.num_splits = num_splits;
+  return from_hip(mla::launch_combine(p, (hipStream_t)stream));
+}
+
+mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t B, int32_t n_q, const float* u,
+                          mla_dtype_t w_dt, const void* w_uv, float* out, void* stream) {
+  if (!dims_ok(dims) || B < 0 || n_q < 1 || !dtype_ok(w_dt)) return MLA_ERR_INVALID_ARG;
+  if (B == 0) return MLA_OK;
+  if (!u || !w_uv || !out) return MLA_ERR_INVALID_ARG;
+  if ((size_t)16 * dims->d_c * sizeof(float) > 64 * 1024) return MLA_ERR_UNSUPPORTED;
+  mla::OutProjParams p;
+  p.u = u; p.w_uv = w_uv; p.out = out;
+  p.B = B; p.n_q = n_q; p.n_h = dims->n_h; p.d_c = dims->d_c; p.d_v = dims->d_v;
+  p.bf16 = w_dt == MLA_BF16;
+  return from_hip(mla::launch_out_proj(p, (hipStream_t)stream));
+}
+
+mla_status_t mla_cache_append(const mla_dims_t* dims, const mla_cache_t* cache, int32_t n,
+                              const int32_t* seq_ids, const int32_t* positions,
+                              const void* c_kv_new, int64_t c_kv_stride, const void* k_rope_new,
+                              int64_t k_rope_stride, void* stream) {
+  if (!dims_ok(dims) || n < 0 || !cache_ok(cache, dims)) return MLA_ERR_INVALID_ARG;
+  if (n == 0) return MLA_OK;
+  if (!seq_ids || !positions || !c_kv_new || !k_rope_new) return MLA_ERR_INVALID_ARG;
+  if (c_kv_stride < dims->d_c || k_rope_stride < dims->d_rope) return MLA_ERR_INVALID_ARG;
+  mla::AppendParams p;
+  p.cache = view_of(cache, dims);
+  p.cache_data = cache->data;
+  p.n = n; p.seq_ids = seq_ids; p.positions = positions;
+  p.c_kv = c_kv_new; p.c_kv_stride = c_kv_stride; p.k_rope = k_rope_new; p.k_rope_stride = k_rope_stride;
+  p.d_c = dims->d_c; p.d_rope = dims->d_rope; p.bf16 = cache->dtype == MLA_BF16;
+  p.rope_base = base_of(dims);
+  return from_hip(mla::launch_cache_append(p, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,189 @@
+// Device-side helpers shared by the gfx950 kernels of the MLA decode library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ------------------------------------------------------------ bf16 <-> fp32
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+// Round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ __forceinline__ static float load(const float* p, int64_t i) { return p[i]; }
+  __device__ __forceinline__ static void store(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<uint16_t> {
+  __device__ __forceinline__ static float load(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+  __device__ __forceinline__ static void store(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+// --------------------------------------------------------- cache addressing
+struct CacheView {
+  const void* data;
+  int64_t seq_stride;        // elements (contiguous)
+  const int32_t* block_table;
+  int32_t block_size;        // 0 = contiguous
+  int32_t max_blocks;
+  int32_t row;               // elements per token row (d_c + d_rope)
+};
+
+// Element offset of the row of token t of sequence b.
+__device__ __forceinline__ int64_t cache_row_offset(const CacheView& c, int b, int t) {
+  if (c.block_size == 0) return (int64_t)b * c.seq_stride + (int64_t)t * c.row;
+  const int blk = c.block_table[(int64_t)b * c.max_blocks + t / c.block_size];
+  return ((int64_t)blk * c.block_size + (t % c.block_size)) * (int64_t)c.row;
+}
+
+// ------------------------------------------------------ split-KV work plan
+// The tokens of all sequences, in order, are cut into ranges of Q tokens
+// (Q = ceil(total / num_splits)); range w is work unit w.  Sequence b (prefix
+// P_b, length L_b > 0) meets work units P_b / Q .. (P_b + L_b - 1) / Q and owns
+// that many consecutive partial slots starting at slot_base(b), the sum of the
+// counts of the sequences before it.
+__device__ __forceinline__ int64_t plan_chunk(int64_t total, int num_splits) {
+  int64_t q = (total + num_splits - 1) / num_splits;
+  return q > 0 ? q : 1;
+}
+__device__ __forceinline__ int plan_parts(int64_t prefix, int64_t len, int64_t q) {
+  return len > 0 ? (int)((prefix + len - 1) / q - prefix / q + 1) : 0;
+}
+
+// Inclusive scan of one int64 per thread over a workgroup of NT threads
+// (NT a multiple of 64).  `scratch` holds NT/64 + 1 int64 values.  Returns the
+// inclusive prefix; *total receives the workgroup sum.
+template <int NT>
+__device__ __forceinline__ int64_t block_scan_incl(int64_t v, int64_t* scratch, int64_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int64_t o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  if (lane == 63) scratch[wave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int64_t run = 0;
+    for (int w = 0; w < NT / 64; ++w) { int64_t s = scratch[w]; scratch[w] = run; run += s; }
+    scratch[NT / 64] = run;
+  }
+  __syncthreads();
+  v += scratch[wave];
+  *total = scratch[NT / 64];
+  __syncthreads();
+  return v;
+}
+
+}  // namespace mla
+
+namespace mla {
+
+// LDS scratch used by the workgroup-level plan walk.
+template <int NT>
+struct PlanScratch {
+  int64_t scan[NT / 64 + 1];
+  int64_t prefix[NT];
+  int32_t len[NT];
+  int32_t slot[NT];
+  int32_t first, last;
+};
+
+// Calls f(b, t0, t1, slot) for every segment of work unit w: the tokens
+// t0..t1-1 of sequence b that fall into the unit, and the partial slot they
+// own.  Segments come in sequence order.  All NT threads of the workgroup
+// must call this together; f is called uniformly.
+template <int NT, typename F>
+__device__ void for_each_segment(const int32_t* __restrict__ ctx_lens, int B, int num_splits, int w,
+                                 PlanScratch<NT>* sc, F&& f) {
+  const int tid = threadIdx.x;
+  int64_t part = 0;
+  for (int b = tid; b < B; b += NT) part += ctx_lens[b];
+  int64_t total;
+  block_scan_incl<NT>(part, sc->scan, &total);
+  const int64_t q = plan_chunk(total, num_splits);
+  const int64_t a = (int64_t)w * q;
+  const int64_t e = a + q < total ? a + q : total;
+  if (a >= e) return;
+  int64_t run = 0, slot_run = 0;
+  for (int c0 = 0; c0 < B; c0 += NT) {
+    const int b = c0 + tid;
+    const int64_t len = b < B ? ctx_lens[b] : 0;
+    int64_t tot_len, tot_np;
+    const int64_t p = run + block_scan_incl<NT>(len, sc->scan, &tot_len) - len;
+    const int64_t np = plan_parts(p, len, q);
+    const int64_t sb = slot_run + block_scan_incl<NT>(np, sc->scan, &tot_np) - np;
+    if (tid == 0) { sc->first = NT; sc->last = -1; }
+    __syncthreads();
+    const bool hit = len > 0 && p < e && p + len > a;
+    sc->prefix[tid] = p;
+    sc->len[tid] = (int32_t)len;
+    sc->slot[tid] = (int32_t)(sb + (w - p / q));
+    if (hit) { atomicMin(&sc->first, tid); atomicMax(&sc->last, tid); }
+    __syncthreads();
+    const int first = sc->first, last = sc->last;
+    for (int k = first; k <= last; ++k) {
+      const int64_t pk = sc->prefix[k];
+      const int64_t lo = a > pk ? a : pk;
+      const int64_t hi = e < pk + sc->len[k] ? e : pk + sc->len[k];
+      const int slot = sc->slot[k];
+      __syncthreads();
+      f(c0 + k, (int)(lo - pk), (int)(hi - pk), slot);
+      __syncthreads();
+    }
+    run += tot_len;
+    slot_run += tot_np;
+    if (run >= e) break;
+  }
+}
+
+// For sequence b: first partial slot and number of partials (0 if empty).
+template <int NT>
+__device__ void plan_lookup(const int32_t* __restrict__ ctx_lens, int B, int num_splits, int b,
+                            PlanScratch<NT>* sc, int* slot_base, int* n_parts) {
+  const int tid = threadIdx.x;
+  int64_t part = 0;
+  for (int k = tid; k < B; k += NT) part += ctx_lens[k];
+  int64_t total;
+  block_scan_incl<NT>(part, sc->scan, &total);
+  const int64_t q = plan_chunk(total, num_splits);
+  int64_t run = 0, slot_run = 0;
+  for (int c0 = 0; c0 <= b; c0 += NT) {
+    const int k = c0 + tid;
+    const int64_t len = k < B ? ctx_lens[k] : 0;
+    int64_t tot_len, tot_np;
+    const int64_t p = run + block_scan_incl<NT>(len, sc->scan, &tot_len) - len;
+    const int64_t np = plan_parts(p, len, q);
+    const int64_t sb = slot_run + block_scan_incl<NT>(np, sc->scan, &tot_np) - np;
+    if (k == b) { sc->slot[0] = (int32_t)sb; sc->len[0] = (int32_t)np; }
+    run += tot_len;
+    slot_run += tot_np;
+  }
+  __syncthreads();
+  *slot_base = sc->slot[0];
+  *n_parts = sc->len[0];
+  __syncthreads();
+}
+
+}  // namespace mla

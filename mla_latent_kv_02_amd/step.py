@@ -1,0 +1,41 @@
+"""One MLA decode step as the sequence of library calls:
+
+    [cache_append of the new tokens] -> absorb_q -> decode -> combine -> out_proj
+
+``DecodeStep`` owns the intermediate buffers (q_lat, q_pe, the split-KV
+partials, u, lse) and the output, sized once for a batch shape, so that a
+step allocates nothing.  Every call goes through the C ABI.
+"""
+from __future__ import annotations
+
+from ._binding import (Dims, LatentCache, mla_absorb_q, mla_cache_append, mla_combine, mla_decode,
+                       mla_num_partials, mla_out_proj)
+
+
+class DecodeStep:
+    def __init__(self, dims: Dims, B: int, n_q: int, num_splits: int, dtype, device="cuda"):
+        import torch
+        self.dims, self.B, self.n_q, self.num_splits = dims, B, n_q, num_splits
+        slots = mla_num_partials(B, num_splits)
+        f32 = torch.float32
+        self.q_lat = torch.empty((B, n_q, dims.n_h, dims.d_c), dtype=dtype, device=device)
+        self.q_pe = torch.empty((B, n_q, dims.n_h, dims.d_rope), dtype=dtype, device=device)
+        self.u_part = torch.empty((slots, n_q, dims.n_h, dims.d_c), dtype=f32, device=device)
+        self.lse_part = torch.empty((slots, n_q, dims.n_h), dtype=f32, device=device)
+        self.u = torch.empty((B, n_q, dims.n_h, dims.d_c), dtype=f32, device=device)
+        self.lse = torch.empty((B, n_q, dims.n_h), dtype=f32, device=device)
+        self.out = torch.empty((B, n_q, dims.n_h, dims.d_v), dtype=f32, device=device)
+
+    def run(self, q_nope, q_rope, positions, w_uk, w_uv, cache: LatentCache, new_tokens=None, stream=None):
+        """``new_tokens`` = (seq_ids, positions, c_kv_new, k_rope_new) appends the
+        step's own latents to the cache first."""
+        d = self.dims
+        if new_tokens is not None:
+            mla_cache_append(d, cache, *new_tokens, stream=stream)
+        mla_absorb_q(d, q_nope, q_rope, positions, w_uk, self.q_lat, self.q_pe, stream=stream)
+        mla_decode(d, self.q_lat, self.q_pe, cache, positions, self.num_splits, self.u_part,
+                   self.lse_part, stream=stream)
+        mla_combine(d, cache.ctx_lens, self.num_splits, self.u_part, self.lse_part, self.u, self.lse,
+                    stream=stream)
+        mla_out_proj(d, self.u, w_uv, self.out, stream=stream)
+        return self.out

@@ -1,0 +1,134 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/mla.h declares, and rejects bad arguments on the host (before any
+HIP call, so these run on a machine without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mla_latent_kv_02_amd as mla
+from mla_latent_kv_02_amd import _binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bd.LIB_PATH):
+        pytest.skip("libmla.so not built")
+    return mla.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for fn in ("mla_absorb_q", "mla_decode", "mla_combine", "mla_out_proj", "mla_cache_append"):
+        assert fn in names
+    assert set(names) == set(bd.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(lib):
+    for code in range(4):
+        assert lib.mla_status_string(code)
+    assert b"unknown" in lib.mla_status_string(99)
+    assert b"gfx950" in lib.mla_version()
+
+
+def test_num_partials(lib):
+    assert lib.mla_num_partials(64, 256) == 319
+    assert lib.mla_num_partials(1, 1) == 1
+    assert lib.mla_num_partials(0, 8) == 0
+    assert lib.mla_num_partials(4, 0) == -1
+
+
+V3 = bd._Dims(128, 512, 64, 128, 128, 0.0, 0.0)
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: validation fails first
+
+
+def _cache(**kw):
+    c = dict(dtype=1, data=0x10000, seq_stride=576 * 16, block_size=0, block_table=None, max_blocks=0,
+             ctx_lens=0x20000)
+    c.update(kw)
+    return bd._Cache(c["dtype"], c["data"], c["seq_stride"], c["block_size"], c["block_table"],
+                     c["max_blocks"], c["ctx_lens"])
+
+
+@pytest.mark.parametrize("dims", [
+    None,
+    bd._Dims(0, 512, 64, 128, 128, 0, 0),      # no heads
+    bd._Dims(128, 500, 64, 128, 128, 0, 0),    # d_c not a multiple of 8
+    bd._Dims(128, 512, 63, 128, 128, 0, 0),    # odd d_rope
+    bd._Dims(128, 512, 64, 0, 128, 0, 0),      # d_nope = 0
+    bd._Dims(128, 512, 64, 128, 128, -1.0, 0),  # negative scale
+])
+def test_decode_rejects_bad_dims(lib, dims):
+    c = _cache()
+    d = None if dims is None else ctypes.byref(dims)
+    st = lib.mla_decode(d, 2, 1, FAKE, FAKE, ctypes.byref(c), FAKE, 4, FAKE, FAKE, None)
+    assert st == bd.MLA_ERR_INVALID_ARG
+
+
+def test_decode_rejects_bad_arguments(lib):
+    c = _cache()
+    ok_args = [ctypes.byref(V3), 2, 1, FAKE, FAKE, ctypes.byref(c), FAKE, 4, FAKE, FAKE, None]
+    for idx, bad in ((1, -1), (2, 0), (3, None), (4, None), (6, None), (7, 0), (7, -3), (8, None), (9, None)):
+        args = list(ok_args)
+        args[idx] = bad
+        assert lib.mla_decode(*args) == bd.MLA_ERR_INVALID_ARG, idx
+    # cache descriptor problems
+    for kw in (dict(data=None), dict(ctx_lens=None), dict(dtype=7), dict(block_size=-1),
+               dict(block_size=64, block_table=None), dict(block_size=64, block_table=0x30000, max_blocks=0),
+               dict(data=0x10008)):
+        cc = _cache(**kw)
+        args = list(ok_args)
+        args[5] = ctypes.byref(cc)
+        assert lib.mla_decode(*args) == bd.MLA_ERR_INVALID_ARG, kw
+    args = list(ok_args)
+    args[5] = None
+    assert lib.mla_decode(*args) == bd.MLA_ERR_INVALID_ARG
+
+
+def test_zero_batch_is_a_no_op(lib):
+    c = _cache()
+    assert lib.mla_decode(ctypes.byref(V3), 0, 1, None, None, ctypes.byref(c), None, 4, None, None, None) == 0
+    assert lib.mla_absorb_q(ctypes.byref(V3), 0, 1, 1, None, None, None, None, None, None, None) == 0
+    assert lib.mla_combine(ctypes.byref(V3), 0, 1, None, 4, None, None, None, None, None) == 0
+    assert lib.mla_out_proj(ctypes.byref(V3), 0, 1, None, 1, None, None, None) == 0
+
+
+def test_other_entry_points_reject_bad_arguments(lib):
+    d = ctypes.byref(V3)
+    assert lib.mla_absorb_q(d, 2, 1, 5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_absorb_q(d, 2, 0, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_absorb_q(d, 2, 1, 1, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_combine(d, 2, 1, FAKE, 0, FAKE, FAKE, FAKE, FAKE, None) == bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_combine(d, 2, 1, None, 4, FAKE, FAKE, FAKE, FAKE, None) == bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_combine(d, 2, 1, FAKE, 4, FAKE, FAKE, None, FAKE, None) == bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_out_proj(d, 2, 1, FAKE, 3, FAKE, FAKE, None) == bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_out_proj(d, 2, 1, None, 1, FAKE, FAKE, None) == bd.MLA_ERR_INVALID_ARG
+    c = _cache()
+    cr = ctypes.byref(c)
+    assert lib.mla_cache_append(d, cr, -1, FAKE, FAKE, FAKE, 512, FAKE, 64, None) == bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_cache_append(d, cr, 3, FAKE, FAKE, FAKE, 100, FAKE, 64, None) == bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_cache_append(d, cr, 3, None, FAKE, FAKE, 512, FAKE, 64, None) == bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_cache_append(d, cr, 0, None, None, None, 0, None, 0, None) == 0
+
+
+def test_binding_refuses_host_tensors(lib):
+    torch = pytest.importorskip("torch")
+    dims = mla.Dims(4, 64, 16, 32, 32)
+    x = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError):
+        mla.mla_out_proj(dims, x, torch.zeros(4, 64, 32), torch.zeros(1, 1, 4, 32))

@@ -1,0 +1,225 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Small cases that the oracle finishes in seconds, spanning several 64-token
+tiles, ragged tails, contexts of one token, two query tokens (causal within
+the pair), paged caches with NaN in every unused slot, many split counts and
+empty work units.  Tolerances: max vector relative error 1e-4 for fp32
+workloads and 1e-2 for bf16 workloads (the bf16 path rounds q_lat, the
+rotated positional key and the softmax weights to bf16 as MFMA operands and
+accumulates in fp32).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from tests._metrics import scalar_err, vec_rel_err
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _tol(w):
+    return 1e-4 if w.dtype == "f32" else 1e-2
+
+
+def _run(st, num_splits):
+    import mla_latent_kv_02_amd as mla
+    from mla_latent_kv_02_amd.step import DecodeStep
+    w = st["workload"]
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    step = DecodeStep(st["dims"], w.batch, w.n_q, num_splits, tdt)
+    step.run(st["q_nope"], st["q_rope"], st["positions"], st["w_uk"], st["w_uv"], st["cache"])
+    torch.cuda.synchronize()
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)
+    return {"q_lat": f(step.q_lat), "q_pe": f(step.q_pe), "u": f(step.u), "lse": f(step.lse),
+            "o": f(step.out), "u_part": f(step.u_part), "lse_part": f(step.lse_part)}
+
+
+def _oracle(w, st, b, heads=None):
+    rows = W.cache_rows(w, b, 0, int(st["ctx_host"][b]))
+    wt = W.weights(w)
+    q = W.queries(w)
+    return oracle.decode_sequence(q["q_nope"][b], q["q_rope"][b], st["positions_host"][b], rows["c_kv"],
+                                  rows["k_rope_raw"], wt["w_uk"], wt["w_uv"], w.sm_scale, w.rope_base,
+                                  heads=heads)
+
+
+def _check(w, st, got, seqs=None, heads=None):
+    tol = _tol(w)
+    seqs = range(w.batch) if seqs is None else seqs
+    hsel = slice(None) if heads is None else list(heads)
+    for b in seqs:
+        ref = _oracle(w, st, b, heads)
+        errs = {
+            "q_lat": vec_rel_err(got["q_lat"][b][:, hsel], ref["q_lat"]),
+            "q_pe": vec_rel_err(got["q_pe"][b][:, hsel], ref["q_pe"]),
+            "u": vec_rel_err(got["u"][b][:, hsel], ref["u"]),
+            "o": vec_rel_err(got["o"][b][:, hsel], ref["o"]),
+            "lse": scalar_err(got["lse"][b][:, hsel], ref["lse"]),
+        }
+        print(f"  seq {b} ctx {st['ctx_host'][b]}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()),
+              flush=True)
+        for k, v in errs.items():
+            assert v <= tol, (b, k, v)
+
+
+def test_synth_device_rows_match_host():
+    _need_gpu()
+    w = W.get("v3_b64")
+    seq = np.array([0, 5, 63, 17], np.int32)
+    tok = np.array([0, 4097, 8191, 12], np.int32)
+    table = torch.from_numpy(W.normal_table_bf16_bits().view(np.int16)).cuda()
+    out = torch.empty((4, w.row), dtype=torch.bfloat16, device="cuda")
+    sd, td = torch.from_numpy(seq).cuda(), torch.from_numpy(tok).cuda()
+    W.fill_cache_rows_device(w, sd.data_ptr(), td.data_ptr(), 4, table.data_ptr(), out.data_ptr(),
+                             torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    for k in range(4):
+        r = W.cache_rows(w, int(seq[k]), int(tok[k]), int(tok[k]) + 1)
+        host = np.concatenate([r["c_kv"], r["k_rope_raw"]], axis=1)[0]
+        np.testing.assert_array_equal(W.bf16_bits_to_f32(got[k]), host)
+
+
+@pytest.mark.parametrize("num_splits", [1, 3, 7])
+def test_tiny_fp32(num_splits):
+    _need_gpu()
+    from workloads.device import stage
+    w = W.get("tiny_fp32")
+    st = stage(w)
+    got = _run(st, num_splits)
+    _check(w, st, got)
+
+
+@pytest.mark.parametrize("num_splits", [1, 4, 9])
+def test_v3_contiguous_ragged(num_splits):
+    _need_gpu()
+    from workloads.device import stage
+    w = W.custom(name="v3_small", seed=21, batch=3, n_q=1, ctx=None, ctx_range=(1, 1))
+    st = stage(w, ctx=np.array([300, 1, 130], np.int32))
+    got = _run(st, num_splits)
+    _check(w, st, got)
+
+
+@pytest.mark.parametrize("num_splits", [1, 5])
+def test_v3_two_query_tokens(num_splits):
+    _need_gpu()
+    from workloads.device import stage
+    w = W.custom(name="v3_nq2", seed=22, batch=3, n_q=2, ctx=None, ctx_range=(1, 1))
+    st = stage(w, ctx=np.array([257, 2, 66], np.int32))
+    got = _run(st, num_splits)
+    _check(w, st, got)
+
+
+@pytest.mark.parametrize("num_splits", [1, 3, 6])
+def test_v3_paged_nan_poisoned(num_splits):
+    _need_gpu()
+    from workloads.device import stage
+    w = W.custom(name="v3_paged_small", seed=23, batch=4, n_q=1, ctx=None, ctx_range=(1, 1), block_size=64)
+    st = stage(w, ctx=np.array([200, 64, 65, 1], np.int32))
+    # every unused slot of the pool holds NaN
+    assert torch.isnan(st["cache"].data.float()).any()
+    got = _run(st, num_splits)
+    _check(w, st, got)
+
+
+def test_generic_path_bf16_small_dims():
+    _need_gpu()
+    from workloads.device import stage
+    w = W.custom(name="bf16_small", seed=24, batch=2, n_q=2, n_h=4, d_c=64, d_rope=16, d_nope=32, d_v=32,
+                 ctx=None, ctx_range=(1, 1))
+    st = stage(w, ctx=np.array([97, 3], np.int32))
+    for ns in (1, 4):
+        got = _run(st, ns)
+        _check(w, st, got)
+
+
+def test_split_invariance_and_determinism():
+    """Splitting the tokens into more work units changes nothing but rounding.
+    On the fp32 path that is fp32 rounding; on the bf16 MFMA path the softmax
+    weights are rounded to bf16 against each unit's own running maximum, so
+    different splits round differently (bf16 level, ~2^-9).  Reruns with the
+    same split are bit-identical (fixed reduction order)."""
+    _need_gpu()
+    from workloads.device import stage
+    wt = W.get("tiny_fp32")
+    st = stage(wt)
+    one, many = _run(st, 1), _run(st, 13)
+    assert vec_rel_err(many["u"], one["u"]) < 1e-5
+    assert scalar_err(many["lse"], one["lse"]) < 1e-6
+    w = W.custom(name="v3_split_inv", seed=25, batch=2, n_q=1, ctx=None, ctx_range=(1, 1))
+    st = stage(w, ctx=np.array([700, 450], np.int32))
+    one = _run(st, 1)
+    many = _run(st, 11)
+    again = _run(st, 11)
+    assert vec_rel_err(many["u"], one["u"]) < 1e-2
+    assert scalar_err(many["lse"], one["lse"]) < 1e-3
+    for k in ("u", "lse", "o", "u_part", "lse_part"):
+        np.testing.assert_array_equal(many[k], again[k])
+
+
+def test_combine_alone_against_oracle():
+    _need_gpu()
+    import mla_latent_kv_02_amd as mla
+    rng = np.random.default_rng(5)
+    dims = mla.Dims(8, 64, 16, 32, 32)
+    ctx = np.array([10, 1, 35, 7], np.int32)
+    num_splits = 6
+    slots = mla.mla_num_partials(len(ctx), num_splits)
+    u_part = rng.standard_normal((slots, 1, 8, 64)).astype(np.float32)
+    lse_part = (rng.standard_normal((slots, 1, 8)) * 5).astype(np.float32)
+    lse_part[1, 0, 3] = -np.inf
+    u_part[1, 0, 3] = 0
+    u = torch.empty((4, 1, 8, 64), device="cuda")
+    lse = torch.empty((4, 1, 8), device="cuda")
+    mla.mla_combine(dims, torch.from_numpy(ctx).cuda(), num_splits, torch.from_numpy(u_part).cuda(),
+                    torch.from_numpy(lse_part).cuda(), u, lse)
+    torch.cuda.synchronize()
+    # slots of each sequence under the documented plan
+    total = int(ctx.sum())
+    q = -(-total // num_splits)
+    prefix = np.concatenate([[0], np.cumsum(ctx)])
+    base = 0
+    for b in range(4):
+        n = (prefix[b] + ctx[b] - 1) // q - prefix[b] // q + 1
+        ref_u, ref_l = oracle.merge_partials(u_part[base:base + n], lse_part[base:base + n])
+        assert vec_rel_err(u[b].cpu().numpy(), ref_u) < 1e-5
+        assert scalar_err(lse[b].cpu().numpy(), ref_l) < 1e-6
+        base += n
+    assert base <= slots
+
+
+def test_out_proj_alone_against_oracle():
+    _need_gpu()
+    import mla_latent_kv_02_amd as mla
+    rng = np.random.default_rng(6)
+    dims = mla.Dims(16, 512, 64, 128, 128)
+    u = rng.standard_normal((5, 2, 16, 512)).astype(np.float32)
+    wuv = W.round_to_bf16((rng.standard_normal((16, 512, 128)) / np.sqrt(512)).astype(np.float32))
+    out = torch.empty((5, 2, 16, 128), device="cuda")
+    mla.mla_out_proj(dims, torch.from_numpy(u).cuda(), torch.from_numpy(wuv).cuda().bfloat16(), out)
+    torch.cuda.synchronize()
+    ref = oracle.value_up_projection(u, wuv)
+    assert vec_rel_err(out.cpu().numpy(), ref) < 1e-4
+
+
+def test_cache_append_rotates_positional_key():
+    _need_gpu()
+    from workloads.device import stage
+    w = W.custom(name="append", seed=26, batch=2, n_q=1, ctx=None, ctx_range=(1, 1))
+    ctx = np.array([70, 5], np.int32)
+    st = stage(w, ctx=ctx)
+    data = st["cache"].data.float().cpu().numpy()
+    for b in range(2):
+        rows = W.cache_rows(w, b, 0, int(ctx[b]))
+        np.testing.assert_array_equal(data[b, :ctx[b], :512], rows["c_kv"])
+        ref = oracle.rope_rotate(rows["k_rope_raw"], np.arange(ctx[b]), 10000.0)
+        assert np.abs(data[b, :ctx[b], 512:] - ref).max() <= 2 ** -8 * np.abs(ref).max()
+        assert np.isnan(data[b, ctx[b]:]).all()
