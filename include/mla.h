@@ -103,18 +103,22 @@ int64_t mla_num_partials(int32_t B, int32_t num_splits);
  * The tokens of all sequences, taken in order (sequence 0 first), are cut
  * into num_splits consecutive ranges of ceil(sum ctx / num_splits) tokens;
  * each range is one work unit.  Every (sequence, work unit) pair that shares
- * tokens produces one partial: the softmax restricted to those tokens,
- *   u_part[p][j][i][:] = sum_t a_t c_t / sum_t a_t,
- *   lse_part[p][j][i]  = log sum_t exp(s_t)        (natural log),
- * with u = 0, lse = -inf when no token of the range is visible to query j.
- * Partials of sequence b occupy consecutive slots p in order of their token
- * ranges; the slot layout is an implementation detail read by mla_combine.
+ * tokens produces one partial over those tokens T_p: with a reference r_p
+ * (any real number the kernel picks; it keeps the weights in range),
+ *   u_part[p][j][i][:]   = sum_{t in T_p} exp(s_t - r_p) c_t     (not normalised)
+ *   lse_part[p][j][i][0] = r_p
+ *   lse_part[p][j][i][1] = log sum_{t in T_p} exp(s_t)           (natural log)
+ * so that u_part * exp(r_p - lse_part[..][1]) is the softmax-weighted latent
+ * of the range.  A range with no token visible to query j gives u = 0,
+ * r = 0, lse = -inf.  Partials of sequence b occupy consecutive slots p in
+ * order of their token ranges; the slot layout is an implementation detail
+ * read by mla_combine.
  *   q_lat     [B][n_q][n_h][d_c]      cache dtype (from mla_absorb_q)
  *   q_pe      [B][n_q][n_h][d_rope]   cache dtype, rotated
  *   positions [B][n_q]                query j of sequence b attends to tokens
  *                                     t <= positions[b][j]
  *   u_part    [mla_num_partials(B, num_splits)][n_q][n_h][d_c]  fp32, out
- *   lse_part  [mla_num_partials(B, num_splits)][n_q][n_h]       fp32, out
+ *   lse_part  [mla_num_partials(B, num_splits)][n_q][n_h][2]    fp32, out
  * Requires 1 <= num_splits. */
 mla_status_t mla_decode(const mla_dims_t *dims, int32_t B, int32_t n_q, const void *q_lat,
                         const void *q_pe, const mla_cache_t *cache, const int32_t *positions,
@@ -122,9 +126,10 @@ mla_status_t mla_decode(const mla_dims_t *dims, int32_t B, int32_t n_q, const vo
 
 /* Log-sum-exp merge of the partials of each sequence (split-KV combine).
  * With L = log sum_k exp(lse_k) over the partials k of (b, j, i):
- *   u[b][j][i][:] = sum_k exp(lse_k - L) u_k,   lse[b][j][i] = L;
- * u = 0, lse = -inf when every partial is empty.  ctx_lens and num_splits
- * must be those given to mla_decode.
+ *   u[b][j][i][:] = sum_k exp(r_k - L) u_part_k,   lse[b][j][i] = L,
+ * i.e. the softmax over the union of the ranges ([Ikmyung] §1.4) written in
+ * terms of per-range results; u = 0, lse = -inf when every partial is empty.
+ * ctx_lens and num_splits must be those given to mla_decode.
  *   u   [B][n_q][n_h][d_c] fp32, out;  lse [B][n_q][n_h] fp32, out (may be NULL) */
 mla_status_t mla_combine(const mla_dims_t *dims, int32_t B, int32_t n_q, const int32_t *ctx_lens,
                          int32_t num_splits, const float *u_part, const float *lse_part,

@@ -194,7 +194,7 @@ def mla_decode(dims: Dims, q_lat, q_pe, cache: LatentCache, positions, num_split
         raise ValueError("contiguous cache holds fewer sequences than B")
     slots = mla_num_partials(B, num_splits)
     _shape(u_part, "u_part", (slots, n_q, dims.n_h, dims.d_c))
-    _shape(lse_part, "lse_part", (slots, n_q, dims.n_h))
+    _shape(lse_part, "lse_part", (slots, n_q, dims.n_h, 2))
     d, c = dims._c(), cache._c()
     _check("mla_decode", load_library().mla_decode(
         ctypes.byref(d), B, n_q, q_lat.data_ptr(), q_pe.data_ptr(), ctypes.byref(c),
@@ -210,7 +210,7 @@ def mla_combine(dims: Dims, ctx_lens, num_splits: int, u_part, lse_part, u, lse=
     slots = mla_num_partials(B, num_splits)
     _shape(ctx_lens, "ctx_lens", (B,))
     _shape(u_part, "u_part", (slots, n_q, dims.n_h, dims.d_c))
-    _shape(lse_part, "lse_part", (slots, n_q, dims.n_h))
+    _shape(lse_part, "lse_part", (slots, n_q, dims.n_h, 2))
     _shape(u, "u", (B, n_q, dims.n_h, dims.d_c))
     if lse is not None:
         _dev(lse, "lse", torch.float32)

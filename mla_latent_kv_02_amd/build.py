@@ -23,16 +23,18 @@ SYNTH_SRC = os.path.join(ROOT, "workloads", "synth_fill.hip")
 SYNTH_LIB = os.path.join(ROOT, "workloads", "libmla_synth.so")
 
 ARCH = "gfx950"
-# No packed-fp32 instructions anywhere; MFMA accumulators in the VGPR form so
-# that free AGPRs hold MFMA operands instead of spilling to scratch.
+# No packed-fp32 instructions anywhere.
 DEVICE_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
+# Per-source extra flags: MFMA accumulators of built-in MFMAs in the VGPR form
+# (the decode kernel pins its large accumulator to AGPRs itself).
+EXTRA_FLAGS = {"proj_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+               "decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 SOURCES = ["mla_api.cpp", "decode_mfma.hip", "decode_generic.hip", "combine.hip",
-           "absorb.hip", "out_proj.hip", "cache_append.hip"]
+           "absorb.hip", "out_proj.hip", "cache_append.hip", "proj_mfma.hip"]
 
 
 def _hipcc() -> str:
@@ -56,7 +58,8 @@ def build(verbose: bool = False, jobs: int = 4) -> None:
         def compile_one(src):
             obj = os.path.join(tmp, os.path.basename(src) + ".o")
             lang = ["-x", "hip"] if src.endswith(".cpp") else []
-            _run([hipcc, *DEVICE_FLAGS, *lang, "-I", CSRC, "-I", os.path.join(ROOT, "include"),
+            _run([hipcc, *DEVICE_FLAGS, *EXTRA_FLAGS.get(src, []), *lang, "-I", CSRC,
+                  "-I", os.path.join(ROOT, "include"),
                   "-c", os.path.join(CSRC, src), "-o", obj])
             return obj
         with cf.ThreadPoolExecutor(max_workers=jobs) as ex:

@@ -1,8 +1,8 @@
 // Split-KV combine: log-sum-exp merge of the per-work-unit partials of each
-// sequence.  For a query row with partials (u_k, lse_k), L = log sum_k
-// exp(lse_k) and the merged value sum is sum_k exp(lse_k - L) u_k -- the
-// softmax over the union of the token ranges written in terms of per-range
-// results (each u_k is already normalised by its own range's sum).
+// sequence.  Partial k of a query row holds u_k = sum_t exp(s_t - r_k) c_t
+// over its token range, its reference r_k and lse_k = log sum_t exp(s_t).
+// With L = log sum_k exp(lse_k), the merged value sum is
+// sum_k exp(r_k - L) u_k -- the softmax over the union of the ranges.
 //
 // One wave per query row; lanes cover the latent dimension with 16-byte
 // loads, so each partial row (d_c floats) is read once, coalesced.
@@ -26,13 +26,14 @@ __global__ __launch_bounds__(NT) void combine_kernel(CombineParams p) {
   if (r >= rows) return;
   const int64_t stride_rows = rows;   // partial slot stride, in rows
 
+  const float2* lp = reinterpret_cast<const float2*>(p.lse_part);   // (r_k, lse_k)
   float m = -INFINITY;
-  for (int k = lane; k < nparts; k += 64) m = fmaxf(m, p.lse_part[(int64_t)(slot0 + k) * stride_rows + r]);
+  for (int k = lane; k < nparts; k += 64) m = fmaxf(m, lp[(int64_t)(slot0 + k) * stride_rows + r].y);
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
   float s = 0.f;
   if (m != -INFINITY)
-    for (int k = lane; k < nparts; k += 64) s += expf(p.lse_part[(int64_t)(slot0 + k) * stride_rows + r] - m);
+    for (int k = lane; k < nparts; k += 64) s += expf(lp[(int64_t)(slot0 + k) * stride_rows + r].y - m);
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) s += __shfl_xor(s, d, 64);
   const float L = m != -INFINITY ? m + logf(s) : -INFINITY;
@@ -44,9 +45,9 @@ __global__ __launch_bounds__(NT) void combine_kernel(CombineParams p) {
     if (m != -INFINITY) {
       for (int k = 0; k < nparts; ++k) {
         const int64_t prow = (int64_t)(slot0 + k) * stride_rows + r;
-        const float lk = p.lse_part[prow];
-        if (lk == -INFINITY) continue;
-        const float wk = expf(lk - L);
+        const float2 rl = lp[prow];
+        if (rl.y == -INFINITY) continue;
+        const float wk = expf(rl.x - L);
         acc += wk * reinterpret_cast<const f32x4*>(p.u_part + prow * p.d_c)[c4];
       }
     }

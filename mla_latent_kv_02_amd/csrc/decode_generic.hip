@@ -102,7 +102,12 @@ __global__ __launch_bounds__(NT) void decode_generic_kernel(DecodeParams p) {
       const int d = tid + k * NT;
       if (d < p.d_c) p.u_part[prow * p.d_c + d] = acc[k] * inv;
     }
-    if (tid == 0) p.lse_part[prow] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+    if (tid == 0) {
+      // normalised partial: reference r = lse
+      const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+      p.lse_part[2 * prow] = l_run > 0.f ? lse : 0.f;
+      p.lse_part[2 * prow + 1] = lse;
+    }
     __syncthreads();
   });
 }

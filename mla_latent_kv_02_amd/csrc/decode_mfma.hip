@@ -17,14 +17,21 @@
 // loads; the V^T operand of PV is read with ds_read_b64_tr_b16 (transposed
 // 4x16 blocks), so the tile is stored once, token-major.
 //
-// LDS tile layout ("chunk groups"): a tile holds T=64 tokens of 72 16-byte
-// chunks (576 bf16).  Chunk c of tile token t lives at 16-byte slot
-//     (c / 8) * 512 + t * 8 + ((c % 8) ^ s(t)),  s(t) = ((t & 3) << 1) | ((t >> 2) & 1).
+// LDS stage layout ("chunk groups"): a stage holds T=32 tokens of 72 16-byte
+// chunks (576 bf16).  Chunk c of stage token t lives at 16-byte slot
+//     (c / 8) * 256 + t * 8 + ((c % 8) ^ s(t)),  s(t) = ((t & 3) << 1) | ((t >> 2) & 1).
 // A 1 KiB run of slots holds 8 tokens x 8 chunks, which is exactly what one
 // 16-byte-per-lane global->LDS load writes; 8 lanes read 128 contiguous bytes
 // of one token row (coalesced).  The xor keeps both LDS read patterns free of
 // bank conflicts: 8 consecutive tokens of one chunk (QK), and 4 consecutive
 // tokens of 2 neighbouring chunks (the transposed PV read).
+//
+// Pipeline: a ring of NSTAGE stages in LDS; loads run NSTAGE - 1 stages ahead
+// of the stage being used, and each wave waits (vmcnt) only for the oldest
+// stage it needs.  Softmax weights exp2(s - m_ref) use a fixed per-row
+// reference, so the fp32 accumulator is never rescaled; the partial is
+// written unnormalised together with its reference and log-sum-exp, and the
+// combine normalises (exact for any reference).
 //
 // Split-KV: the workgroup walks the segments of its work unit (see
 // for_each_segment) and writes one normalised partial (u, lse) per segment.
@@ -38,12 +45,16 @@ namespace {
 constexpr int DC = 512;
 constexpr int DR = 64;
 constexpr int ROW = DC + DR;          // 576 elements
-constexpr int T = 64;                 // tokens per tile
+constexpr int T = 32;                 // tokens per pipeline stage
+constexpr int NSTAGE = 4;             // LDS ring: NSTAGE - 1 stages in flight while one is used
 constexpr int NT = 256;               // threads per workgroup
 constexpr int KSTEPS = ROW / 32;      // 18 MFMA k-steps for QK^T
 constexpr int CGROUPS = ROW / 64;     // 9 chunk groups of 8 chunks
-constexpr int TILE_BYTES = T * ROW * 2;  // 73728
+constexpr int CG_BYTES = T * 128;     // one chunk group of a stage: 32 tokens x 128 B
+constexpr int STAGE_BYTES = CGROUPS * CG_BYTES;   // 36864
+constexpr int LOADS_PER_STAGE = CGROUPS;          // 16-byte-per-lane loads per wave per stage
 constexpr int MBLK = DC / 16;         // 32 latent blocks of 16
+constexpr float REF_HEADROOM = 64.f;  // log2 units a score may exceed its row's reference
 
 struct DecodeArgs {
   const uint16_t* q_lat;   // [B][n_q][n_h][512]
@@ -60,38 +71,111 @@ struct DecodeArgs {
 __device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
 
 struct __attribute__((aligned(16))) DecodeSmem {
-  unsigned char tile[2][TILE_BYTES];
+  unsigned char stage[NSTAGE][STAGE_BYTES];
+  bf16x8 pbuf[8][64];        // softmax weights of the stage, MFMA B-operand layout, per head block
+  int flag[4];               // per wave: a score ran past its row's reference (redo needed)
   PlanScratch<NT> plan;
 };
 
-// Issue this wave's share of the global->LDS loads of one tile: tile tokens
-// 16*wave + 8*mm + lane/8 (mm = 0, 1), all 9 chunk groups.
-__device__ __forceinline__ void load_tile(const DecodeArgs& a, int b, int tok0, int tok_end,
-                                          unsigned char* buf, int wave, int lane) {
-  const unsigned char* base = static_cast<const unsigned char*>(a.cache.data);
-#pragma unroll
-  for (int mm = 0; mm < 2; ++mm) {
-    const int tt = 16 * wave + 8 * mm + (lane >> 3);
-    int tok = tok0 + tt;
-    tok = tok < tok_end ? tok : tok_end - 1;   // rows past the segment repeat a valid row
-    const unsigned char* rowp = base + cache_row_offset(a.cache, b, tok) * 2;
-    const int cpos = ((lane & 7) ^ swz(tt)) * 16;
-#pragma unroll
-    for (int cg = 0; cg < CGROUPS; ++cg) {
-      unsigned char* dst = buf + cg * 8192 + (2 * wave + mm) * 1024;
-      __builtin_amdgcn_global_load_lds(rowp + cg * 128 + cpos, (lds_void*)dst, 16, 0, 0);
-    }
-  }
+// Block id of the paged cache for token `tok` of sequence b, read with a
+// scalar load (the index is wave-uniform).  Scalar loads are counted by
+// lgkmcnt, so waiting for them does not drain the vector-memory queue that
+// holds the in-flight stage loads.
+__device__ __forceinline__ int block_id_scalar(const CacheView& c, int b, int tok) {
+  const int32_t* p = c.block_table + (int64_t)b * c.max_blocks + tok / c.block_size;
+  // readfirstlane returns a signed int: widen through uint32_t (zero-extend)
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)p);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uintptr_t)p >> 32));
+  const uint64_t addr = (uint64_t)lo | ((uint64_t)hi << 32);
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(addr) : "memory");
+  return v;
 }
 
+// This wave's share of the global->LDS loads of one stage: stage tokens
+// 8*wave + lane/8, all 9 chunk groups (9 loads of 1 KiB per wave).
+__device__ __forceinline__ void load_stage(const DecodeArgs& a, int b, int tok0, int tok_end,
+                                           unsigned char* buf, int wave, int lane) {
+  const unsigned char* base = static_cast<const unsigned char*>(a.cache.data);
+  const int tt = 8 * wave + (lane >> 3);
+  int tok = tok0 + tt;
+  tok = tok < tok_end ? tok : tok_end - 1;   // rows past the segment repeat a valid row
+  int64_t off;
+  const CacheView& c = a.cache;
+  if (c.block_size == 0) {
+    off = (int64_t)b * c.seq_stride + (int64_t)tok * ROW;
+  } else if (c.block_size >= T) {
+    // the stage's tokens lie in at most two blocks: those of its first and last token
+    const int last = tok0 + T - 1 < tok_end - 1 ? tok0 + T - 1 : tok_end - 1;
+    const int blk0 = block_id_scalar(c, b, tok0);
+    const int blk1 = block_id_scalar(c, b, last);
+    const int blk = tok / c.block_size == tok0 / c.block_size ? blk0 : blk1;
+    off = ((int64_t)blk * c.block_size + tok % c.block_size) * ROW;
+  } else {
+    off = cache_row_offset(c, b, tok);
+  }
+  const unsigned char* rowp = base + off * 2 + ((lane & 7) ^ swz(tt)) * 16;
+  unsigned char* dst = buf + wave * 1024;
+#pragma unroll
+  for (int cg = 0; cg < CGROUPS; ++cg)
+    __builtin_amdgcn_global_load_lds(rowp + cg * 128, (lds_void*)(dst + cg * CG_BYTES), 16, 0, 0);
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations (a
+// __syncthreads() would also wait for every outstanding global load and so
+// drain the stage pipeline).  Stage data arriving through global->LDS loads is
+// covered by the explicit vmcnt waits before the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt immediates (GFX9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
+// vmcnt[5:4] << 14) that wait on vector memory only.  Issued through the
+// builtin so that the compiler's own wait insertion sees them.
+constexpr int kWaitVm0 = 0x0F70, kWaitVm9 = 0x0F79, kWaitVm18 = 0x4F72;
+
+// O += A . B for one 16x16 block of the PV product, with the accumulator pinned
+// to AGPRs.  O needs all 256 AGPRs; the QK^T accumulators (built-in MFMAs,
+// compiled in the VGPR form) stay in VGPRs, so the allocator never moves O
+// blocks between register files inside the stage loop.
+__device__ __forceinline__ void pv_mfma(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Wait states between the last PV MFMA and any other read of its accumulator
+// (the compiler cannot see the MFMA inside the asm statements above).
+__device__ __forceinline__ void pv_mfma_drain() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
+// Wait until at most `n` stages of this wave's loads are still in flight.
+__device__ __forceinline__ void wait_stages_in_flight(int n) {
+  if (n >= 2) __builtin_amdgcn_s_waitcnt(kWaitVm18);
+  else if (n == 1) __builtin_amdgcn_s_waitcnt(kWaitVm9);
+  else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+}
+static_assert(LOADS_PER_STAGE == 9 && NSTAGE == 4, "wait counts assume 9 loads per stage, 4 stages");
+
+// Work split inside a workgroup of 4 waves serving 128 query rows:
+//   QK^T and softmax: wave w owns rows 32w .. 32w+31 (its heads' queries stay in
+//     registers as the MFMA B operand);
+//   PV: wave w owns latent columns 128w .. 128w+127 for all 128 rows, so each
+//     V element is read from LDS once per workgroup; the softmax weights of all
+//     rows come through LDS (each wave's weights are already in the B-operand
+//     lane layout, so the exchange is a 16-byte copy per lane and head block).
+// The accumulator O is touched only by MFMAs and by the final store: the
+// weights use a fixed per-row reference (the row's maximum over the first
+// stage), which needs no rescaling of O.  If a later score exceeds the
+// reference by more than REF_HEADROOM (log2 units; weights stay below
+// 2^REF_HEADROOM, far from fp32/bf16 overflow), the segment is computed again
+// with the row's true maximum as the reference.
 __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ DecodeSmem smem;
   DecodeSmem* sm = &smem;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = lane >> 5;          // lane half
-  const int l32 = lane & 31;
+  const int g4 = lane >> 4;         // lane group of 16
+  const int l16 = lane & 15;
 
   // block -> (work unit, row group); the groups of one unit sit 8 blocks apart
   // so that they land on the same XCD and share its L2.
@@ -101,22 +185,20 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
   if (w >= a.num_splits) return;
 
   const int rows = a.n_q * a.n_h;
-  const int row0 = g * 128 + wave * 32;     // first query row of this wave
+  const int grow0 = g * 128;                  // first query row of the workgroup
+  const int row0 = grow0 + wave * 32;         // first QK row of this wave
   const bool active = row0 < rows;
-  const int jq = active ? row0 / a.n_h : 0;   // query token of this wave
-  const int i0 = active ? row0 % a.n_h : 0;   // first head of this wave
+  const int jq = active ? row0 / a.n_h : 0;   // query token of this wave's QK rows
 
   for_each_segment<NT>(a.ctx_lens, a.B, a.num_splits, w, &sm->plan,
                        [&](int b, int t0, int t1, int slot) {
-    const int g4 = lane >> 4;         // lane group of 16
-    const int l16 = lane & 15;
-    // ---- query operand (B of QK^T): head i0 + 16*hb + l16, k = 32*ks + 8*g4 .. +8
+    // ---- query operand (B of QK^T): row row0 + 16*hb + l16, k = 32*ks + 8*g4 .. +8
     bf16x8 qreg[2][KSTEPS];
     int limit = t1;
     if (active) {
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
-        const int64_t qrow = ((int64_t)b * a.n_q + jq) * a.n_h + i0 + 16 * hb + l16;
+        const int64_t qrow = (int64_t)b * rows + row0 + 16 * hb + l16;
         const u16x8* ql = reinterpret_cast<const u16x8*>(a.q_lat + qrow * DC);
         const u16x8* qp = reinterpret_cast<const u16x8*>(a.q_pe + qrow * DR);
 #pragma unroll
@@ -128,142 +210,170 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
       const int qpos = a.positions[(int64_t)b * a.n_q + jq];
       limit = qpos + 1 < t1 ? qpos + 1 : t1;
     }
-    f32x4 o[MBLK][2];
-#pragma unroll
-    for (int m = 0; m < MBLK; ++m) { o[m][0] = f32x4{}; o[m][1] = f32x4{}; }
-    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-
-    // per-lane LDS byte offsets that do not depend on the tile
+    // the query operands must not be waited for inside the stage loop, where the
+    // vector-memory counter also covers the stage loads
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    // per-lane LDS byte offsets that do not depend on the stage
     const int sw_qk = swz(l16 & 7);
     int qk_off[2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) qk_off[r] = l16 * 128 + (((4 * r + g4) ^ sw_qk) << 4);
-    const int tr_tok = 4 * g4 + (l16 >> 2);                // token (mod 32) of this lane's row
+    const int tr_tok = 4 * g4 + (l16 >> 2);                // token (mod 16) of this lane's row
     const int sw_tr = swz(tr_tok & 7);
     const int half8 = (l16 & 1) * 8;
     const int cch = (l16 & 3) >> 1;                        // chunk within a chunk pair
+    const int nst = (t1 - t0 + T - 1) / T;
 
-    const int ntiles = (t1 - t0 + T - 1) / T;
-    load_tile(a, b, t0, t1, sm->tile[0], wave, lane);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    // m_ref: reference (log2 units) of each of the lane's two QK rows;
+    // m_max: running maximum of the row's scores
+    float m_ref[2] = {-INFINITY, -INFINITY}, m_max[2] = {-INFINITY, -INFINITY};
+    float l_run[2];
+    // O^T accumulators of this wave: latent block mb (16 latents at 128*wave + 16*mb)
+    // x head block hb (rows grow0 + 16*hb .. +16)
+    f32x4 o[8][8];
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int hb = 0; hb < 8; ++hb) o[mb][hb] = f32x4{};
+      l_run[0] = l_run[1] = 0.f;
+      bool over = false;
+#pragma unroll
+      for (int s = 0; s < NSTAGE - 1; ++s)
+        if (s < nst) load_stage(a, b, t0 + s * T, t1, sm->stage[s], wave, lane);
 
-    for (int it = 0; it < ntiles; ++it) {
-      const int tile0 = t0 + it * T;
-      unsigned char* cur = sm->tile[it & 1];
-      if (it + 1 < ntiles) load_tile(a, b, tile0 + T, t1, sm->tile[(it + 1) & 1], wave, lane);
-#pragma unroll 1
-      for (int sub = 0; sub < 2; ++sub) {
-        const int tok0 = tile0 + 32 * sub;
-        if (!(active && tok0 < limit)) continue;
-        unsigned char* sbuf = cur + sub * 32 * 128;
-        // ------------ S^T = K . Q^T for 32 tokens: 4 chains (token block tb x head block hb),
-        // K operands read from LDS PF k-steps ahead of their use.
-        auto rd_k = [&](int ks, int tb) -> bf16x8 {
-          const unsigned char* p = sbuf + (ks >> 1) * 8192 + tb * 2048 + qk_off[ks & 1];
-          return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
-              (const __attribute__((address_space(3))) unsigned char*)p);
-        };
-        constexpr int PF = 2;
-        f32x4 sacc[2][2] = {{f32x4{}, f32x4{}}, {f32x4{}, f32x4{}}};
-        bf16x8 kring[PF][2];
+      for (int it = 0; it < nst; ++it) {
+        const int after = nst - 1 - it;     // stages already issued beyond this one (at most 2)
+        wait_stages_in_flight(after < NSTAGE - 2 ? after : NSTAGE - 2);
+        lds_barrier();
+        if (it + NSTAGE - 1 < nst)
+          load_stage(a, b, t0 + (it + NSTAGE - 1) * T, t1, sm->stage[(it + NSTAGE - 1) % NSTAGE], wave, lane);
+        const int tok0 = t0 + it * T;
+        unsigned char* sbuf = sm->stage[it % NSTAGE];
+        bf16x8 pb[2] = {bf16x8{}, bf16x8{}};
+        if (active && tok0 < limit) {
+          // ------------ S^T = K . Q^T for 32 tokens: 4 chains (token block tb x head block hb),
+          // K operands read from LDS PF k-steps ahead of their use.
+          auto rd_k = [&](int ks, int tb) -> bf16x8 {
+            const unsigned char* p = sbuf + (ks >> 1) * CG_BYTES + tb * 2048 + qk_off[ks & 1];
+            return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+                (const __attribute__((address_space(3))) unsigned char*)p);
+          };
+          constexpr int PF = 2;
+          f32x4 sacc[2][2] = {{f32x4{}, f32x4{}}, {f32x4{}, f32x4{}}};
+          bf16x8 kring[PF][2];
 #pragma unroll
-        for (int ks = 0; ks < PF; ++ks) { kring[ks][0] = rd_k(ks, 0); kring[ks][1] = rd_k(ks, 1); }
+          for (int ks = 0; ks < PF; ++ks) { kring[ks][0] = rd_k(ks, 0); kring[ks][1] = rd_k(ks, 1); }
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-          const bf16x8 k0 = kring[ks % PF][0], k1 = kring[ks % PF][1];
-          if (ks + PF < KSTEPS) { kring[ks % PF][0] = rd_k(ks + PF, 0); kring[ks % PF][1] = rd_k(ks + PF, 1); }
-          sacc[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qreg[0][ks], sacc[0][0], 0, 0, 0);
-          sacc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qreg[1][ks], sacc[0][1], 0, 0, 0);
-          sacc[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qreg[0][ks], sacc[1][0], 0, 0, 0);
-          sacc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qreg[1][ks], sacc[1][1], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
+          for (int ks = 0; ks < KSTEPS; ++ks) {
+            const bf16x8 k0 = kring[ks % PF][0], k1 = kring[ks % PF][1];
+            if (ks + PF < KSTEPS) { kring[ks % PF][0] = rd_k(ks + PF, 0); kring[ks % PF][1] = rd_k(ks + PF, 1); }
+            sacc[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qreg[0][ks], sacc[0][0], 0, 0, 0);
+            sacc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qreg[1][ks], sacc[0][1], 0, 0, 0);
+            sacc[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qreg[0][ks], sacc[1][0], 0, 0, 0);
+            sacc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qreg[1][ks], sacc[1][1], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          // ------------ softmax weights; lane holds rows (hb, l16), tokens 16*tb + 4*g4 + i
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            float mt = -INFINITY;
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int tok = tok0 + 16 * tb + 4 * g4 + i;
+                float x = sacc[tb][hb][i] * a.scale_log2;
+                x = tok < limit ? x : -INFINITY;
+                sacc[tb][hb][i] = x;
+                mt = fmaxf(mt, x);
+              }
+            mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+            m_max[hb] = fmaxf(m_max[hb], mt);
+            if (m_ref[hb] == -INFINITY) m_ref[hb] = mt;       // first visible stage of the row
+            over |= mt > m_ref[hb] + REF_HEADROOM;
+            const float m_use = m_ref[hb] == -INFINITY ? 0.f : m_ref[hb];
+            float psum = 0.f;
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float p = __builtin_amdgcn_exp2f(sacc[tb][hb][i] - m_use);
+                psum += p;
+                pb[hb][4 * tb + i] = (__bf16)p;
+              }
+            l_run[hb] += psum;
+          }
         }
-        // ------------ online softmax; lane holds heads (hb, l16), tokens 16*tb + 4*g4 + i
-        bf16x8 pb[2];
-        float alpha[2];
+        // ------------ publish this wave's weights (B-operand layout)
+        sm->pbuf[2 * wave][lane] = pb[0];
+        sm->pbuf[2 * wave + 1][lane] = pb[1];
+        lds_barrier();
+        // ------------ O^T[own 128 latents][128 rows] += V^T . P^T: 8 latent blocks,
+        // each fed by two transposed LDS reads and reused for the 8 head blocks.
+        bf16x8 pall[8];
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          float mt = -INFINITY;
-#pragma unroll
-          for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int tok = tok0 + 16 * tb + 4 * g4 + i;
-              float x = sacc[tb][hb][i] * a.scale_log2;
-              x = tok < limit ? x : -INFINITY;
-              sacc[tb][hb][i] = x;
-              mt = fmaxf(mt, x);
-            }
-          mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-          mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-          const float m_new = fmaxf(m_run[hb], mt);
-          const float m_use = m_new == -INFINITY ? 0.f : m_new;
-          alpha[hb] = __builtin_amdgcn_exp2f(m_run[hb] - m_use);
-          float psum = 0.f;
-#pragma unroll
-          for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float p = __builtin_amdgcn_exp2f(sacc[tb][hb][i] - m_use);
-              psum += p;
-              pb[hb][4 * tb + i] = (__bf16)p;
-            }
-          l_run[hb] = l_run[hb] * alpha[hb] + psum;
-          m_run[hb] = m_new;
-        }
-        if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.f || alpha[1] != 1.f)) {
-#pragma unroll
-          for (int m = 0; m < MBLK; ++m) { o[m][0] *= alpha[0]; o[m][1] *= alpha[1]; }
-        }
-        // ------------ O^T += V^T . P^T: 32 latent blocks of 16, each fed by two
-        // transposed LDS reads (tokens 4*g4 + r and 16 + 4*g4 + r) issued
-        // PV_PF blocks ahead; the A operand serves both head blocks.
+        for (int hb = 0; hb < 8; ++hb) pall[hb] = sm->pbuf[hb][lane];
         auto rd_v = [&](int mb) -> bf16x8 {
-          const int cq = 2 * (mb & 3) + cch;
+          const int mbg = 8 * wave + mb;                   // global latent block (16 latents)
+          const int cq = 2 * (mbg & 3) + cch;
           bf16x4 v[2];
 #pragma unroll
           for (int ins = 0; ins < 2; ++ins) {
             const int t = 16 * ins + tr_tok;
-            const unsigned char* p = sbuf + (mb >> 2) * 8192 + t * 128 + ((cq ^ sw_tr) << 4) + half8;
+            const unsigned char* p = sbuf + (mbg >> 2) * CG_BYTES + t * 128 + ((cq ^ sw_tr) << 4) + half8;
             v[ins] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                 (lds_bf16x4*)((__attribute__((address_space(3))) unsigned char*)p));
           }
           return __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
         };
-        constexpr int PV_PF = 2;
-        bf16x8 vring[PV_PF];
+        bf16x8 va = rd_v(0);
 #pragma unroll
-        for (int mb = 0; mb < PV_PF; ++mb) vring[mb] = rd_v(mb);
+        for (int mb = 0; mb < 8; ++mb) {
+          const bf16x8 cur = va;
+          if (mb + 1 < 8) va = rd_v(mb + 1);
 #pragma unroll
-        for (int mb = 0; mb < MBLK; ++mb) {
-          const bf16x8 va = vring[mb % PV_PF];
-          if (mb + PV_PF < MBLK) vring[mb % PV_PF] = rd_v(mb + PV_PF);
-          o[mb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[0], o[mb][0], 0, 0, 0);
-          o[mb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[1], o[mb][1], 0, 0, 0);
+          for (int hb = 0; hb < 8; ++hb) pv_mfma(o[mb][hb], cur, pall[hb]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // ------------ did any row of the workgroup outgrow its reference?
+      const bool wover = __builtin_amdgcn_ballot_w64(over) != 0;
+      if (lane == 0) sm->flag[wave] = wover;
       __syncthreads();
+      const bool redo = (sm->flag[0] | sm->flag[1] | sm->flag[2] | sm->flag[3]) != 0;
+      __syncthreads();
+      if (!redo) break;
+      m_ref[0] = m_max[0];
+      m_ref[1] = m_max[1];
     }
-
-    // ---------------- write the partial of this segment
+    pv_mfma_drain();
+    // ---------------- write the partial of this segment (unnormalised; see mla.h)
     if (active) {
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
         float l_tot = l_run[hb] + __shfl_xor(l_run[hb], 16, 64);
         l_tot += __shfl_xor(l_tot, 32, 64);
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        const int64_t prow = ((int64_t)slot * a.n_q + jq) * a.n_h + i0 + 16 * hb + l16;
-        float* up = a.u_part + prow * DC + 4 * g4;
-#pragma unroll
-        for (int mb = 0; mb < MBLK; ++mb)
-          *reinterpret_cast<f32x4*>(up + 16 * mb) = o[mb][hb] * inv;
-        if (g4 == 0)
-          a.lse_part[prow] = l_tot > 0.f ? (m_run[hb] + __log2f(l_tot)) * kLn2 : -INFINITY;
+        if (g4 == 0) {
+          const int r = row0 + 16 * hb + l16;
+          float2 rl;
+          rl.x = l_tot > 0.f ? m_ref[hb] * kLn2 : 0.f;
+          rl.y = l_tot > 0.f ? (m_ref[hb] + __log2f(l_tot)) * kLn2 : -INFINITY;
+          reinterpret_cast<float2*>(a.lse_part)[(int64_t)slot * rows + r] = rl;
+        }
       }
     }
+#pragma unroll
+    for (int hb = 0; hb < 8; ++hb) {
+      const int r = grow0 + 16 * hb + l16;
+      if (r < rows) {
+        float* up = a.u_part + ((int64_t)slot * rows + r) * DC + 128 * wave + 4 * g4;
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) *reinterpret_cast<f32x4*>(up + 16 * mb) = o[mb][hb];
+      }
+    }
+    __syncthreads();   // all waves done with the ring and the exchange buffers
   });
 }
 

@@ -50,6 +50,8 @@ struct AbsorbParams {
   float rope_base;
 };
 hipError_t launch_absorb(const AbsorbParams& p, hipStream_t stream);
+bool absorb_mfma_ok(const AbsorbParams& p);
+hipError_t launch_absorb_mfma(const AbsorbParams& p, hipStream_t stream);
 
 struct OutProjParams {
   const float* u;
@@ -59,6 +61,8 @@ struct OutProjParams {
   bool bf16;
 };
 hipError_t launch_out_proj(const OutProjParams& p, hipStream_t stream);
+bool out_proj_mfma_ok(const OutProjParams& p);
+hipError_t launch_out_proj_mfma(const OutProjParams& p, hipStream_t stream);
 
 struct AppendParams {
   CacheView cache;

@@ -78,6 +78,7 @@ mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t B, int32_t n_q, mla_dt
   p.B = B; p.n_q = n_q; p.n_h = dims->n_h; p.d_c = dims->d_c; p.d_rope = dims->d_rope;
   p.d_nope = dims->d_nope; p.bf16 = dt == MLA_BF16; p.rope_base = base_of(dims);
   if ((size_t)16 * p.d_nope * sizeof(float) > 64 * 1024) return MLA_ERR_UNSUPPORTED;
+  if (mla::absorb_mfma_ok(p)) return from_hip(mla::launch_absorb_mfma(p, (hipStream_t)stream));
   return from_hip(mla::launch_absorb(p, (hipStream_t)stream));
 }
 
@@ -125,6 +126,7 @@ mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t B, int32_t n_q, const 
   p.u = u; p.w_uv = w_uv; p.out = out;
   p.B = B; p.n_q = n_q; p.n_h = dims->n_h; p.d_c = dims->d_c; p.d_v = dims->d_v;
   p.bf16 = w_dt == MLA_BF16;
+  if (mla::out_proj_mfma_ok(p)) return from_hip(mla::launch_out_proj_mfma(p, (hipStream_t)stream));
   return from_hip(mla::launch_out_proj(p, (hipStream_t)stream));
 }
 

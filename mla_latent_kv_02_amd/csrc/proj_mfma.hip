@@ -1,0 +1,222 @@
+// MFMA (gfx950) kernels for the two per-head projections around the decode,
+// bf16 weights, fp32 accumulation.  Both are weight-bandwidth-bound skinny
+// GEMMs (M = B * n_q rows, one head's weight matrix per workgroup).
+//
+// Key absorption q_lat = q^C_i (W_i^UK)^T ([Huny] = "Multi-Head Latent
+// Attention(MLA) 아키텍처 해부", Huny's Dev Blog, §3.1).  Computed transposed,
+// q_lat^T[c][m] = W_i^UK[c][:] . q^C[m][:], so that both MFMA operands are
+// rows that are contiguous in memory along the contraction (d_nope): W_UK row c
+// is the A operand and the query row m the B operand, 16 bytes per lane, no
+// transpose.  One wave = 16 latent columns x all query rows.
+//
+// Value up-projection o_i = u_i W_i^UV ([Huny] §3.2).  W_i^UV is [d_c][d_v]
+// with d_v contiguous, but the MFMA B operand wants d_c (the contraction)
+// contiguous per lane, so 64-row chunks of W_i^UV are staged in LDS and read
+// with ds_read_b64_tr_b16 (transposed 4x16 blocks).  u is fp32; it is split
+// into a bf16 high part and a bf16 residual (u = hi + lo to ~2^-16) and both
+// are multiplied, so the projection keeps fp32-level accuracy.
+
+#include "mla_device.h"
+#include "launch.h"
+
+namespace mla {
+namespace {
+
+// ------------------------------------------------------------- absorption
+// grid (n_h, d_c / 64); 4 waves, wave w -> latent columns c0 = 64*blockIdx.y + 16*w.
+// Requires d_nope % 32 == 0, d_nope <= 128, d_c % 64 == 0.
+constexpr int AB_MAXK = 4;            // d_nope / 32 held in registers
+__global__ __launch_bounds__(256) void absorb_mfma_kernel(AbsorbParams p) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = blockIdx.x;
+  const int c0 = blockIdx.y * 64 + wave * 16;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int M = p.B * p.n_q;
+  const int ksteps = p.d_nope / 32;
+  const uint16_t* w = static_cast<const uint16_t*>(p.w_uk) + ((int64_t)i * p.d_c + c0 + l16) * p.d_nope + 8 * g;
+  const uint16_t* q = static_cast<const uint16_t*>(p.q_nope);
+  uint16_t* out = static_cast<uint16_t*>(p.q_lat);
+  bf16x8 a[AB_MAXK];
+#pragma unroll
+  for (int ks = 0; ks < AB_MAXK; ++ks)
+    if (ks < ksteps) a[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(w + 32 * ks));
+  for (int m0 = 0; m0 < M; m0 += 64) {
+    u16x8 bq[4][AB_MAXK];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int m = m0 + 16 * mb + l16;
+      const uint16_t* qr = q + ((int64_t)m * p.n_h + i) * p.d_nope + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < AB_MAXK; ++ks) {
+        bq[mb][ks] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        if (ks < ksteps && m < M) bq[mb][ks] = *reinterpret_cast<const u16x8*>(qr + 32 * ks);
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int m = m0 + 16 * mb + l16;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < AB_MAXK; ++ks)
+        if (ks < ksteps)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], __builtin_bit_cast(bf16x8, bq[mb][ks]), acc, 0, 0, 0);
+      // acc[r] = q_lat[m][i][c0 + 4g + r]
+      if (m < M) {
+        u16x4 o4 = {f32_to_bf16(acc[0]), f32_to_bf16(acc[1]), f32_to_bf16(acc[2]), f32_to_bf16(acc[3])};
+        *reinterpret_cast<u16x4*>(out + ((int64_t)m * p.n_h + i) * p.d_c + c0 + 4 * g) = o4;
+      }
+    }
+  }
+}
+
+// Query RoPE: one thread per (query row m, rotation plane k, group of 4
+// heads); the fp64 angle depends on (m, k) only.
+template <typename T>
+__global__ __launch_bounds__(256) void rope_q_rows_kernel(AbsorbParams p) {
+  const int half = p.d_rope / 2;
+  const int hgroups = (p.n_h + 3) / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t n = (int64_t)p.B * p.n_q * half * hgroups;
+  if (idx >= n) return;
+  const int hg = (int)(idx % hgroups);
+  const int k = (int)((idx / hgroups) % half);
+  const int64_t m = idx / ((int64_t)hgroups * half);
+  const T* src = static_cast<const T*>(p.q_rope);
+  T* dst = static_cast<T*>(p.q_pe);
+  double sd, cd;
+  sincos((double)p.positions[m] * pow((double)p.rope_base, -2.0 * k / p.d_rope), &sd, &cd);
+  const float c = (float)cd, s = (float)sd;
+  for (int i = 4 * hg; i < 4 * hg + 4 && i < p.n_h; ++i) {
+    const int64_t off = ((int64_t)m * p.n_h + i) * p.d_rope + 2 * k;
+    const float x0 = Elem<T>::load(src, off), x1 = Elem<T>::load(src, off + 1);
+    Elem<T>::store(dst, off, x0 * c - x1 * s);
+    Elem<T>::store(dst, off + 1, x0 * s + x1 * c);
+  }
+}
+
+// --------------------------------------------------------- up-projection
+constexpr int OP_MROWS = 64;          // query rows per workgroup (4 waves x 16)
+constexpr int OP_KCHUNK = 64;         // rows of W_UV staged per LDS chunk
+constexpr int OP_VCOLS = 32;          // value columns per workgroup
+constexpr int OP_MAXV = OP_VCOLS;
+constexpr int OP_PITCH = OP_MAXV * 2 + 32;  // bytes per staged row (pad against bank conflicts)
+
+// grid (n_h, ceil(M / 64), d_v / 32); wave w -> rows m0 + 16w .. +16 and the
+// workgroup's 32 value columns.  Requires d_c % 64 == 0, d_v % 32 == 0.
+__global__ __launch_bounds__(256) void out_proj_mfma_kernel(OutProjParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char wsm[OP_KCHUNK * OP_PITCH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int i = blockIdx.x;
+  const int M = p.B * p.n_q;
+  const int m = blockIdx.y * OP_MROWS + wave * 16 + l16;     // A-operand row of this lane
+  const int vblocks = OP_VCOLS / 16;
+  const int v0 = blockIdx.z * OP_VCOLS;
+  const uint16_t* w = static_cast<const uint16_t*>(p.w_uv) + (int64_t)i * p.d_c * p.d_v + v0;
+  const float* ur = p.u + ((int64_t)(m < M ? m : 0) * p.n_h + i) * p.d_c + 8 * g;
+  f32x4 acc[OP_MAXV / 16];
+#pragma unroll
+  for (int v = 0; v < OP_MAXV / 16; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int row_bytes = OP_VCOLS * 2;
+  const int pieces = OP_KCHUNK * (row_bytes / 16);               // 16-byte pieces per chunk
+  constexpr int PER_T = (OP_KCHUNK * OP_MAXV * 2 / 16 + 255) / 256;  // pieces per thread
+  u16x8 stage[PER_T];
+#define OP_FETCH(C0)                                                                       \
+  _Pragma("unroll") for (int k = 0; k < PER_T; ++k) {                                     \
+    const int e = tid + 256 * k;                                                           \
+    if (e < pieces) {                                                                      \
+      const int r = e / (row_bytes / 16), cc = e % (row_bytes / 16);                       \
+      stage[k] = *reinterpret_cast<const u16x8*>(w + (int64_t)((C0) + r) * p.d_v + cc * 8); \
+    }                                                                                      \
+  }
+  OP_FETCH(0)
+  for (int c0 = 0; c0 < p.d_c; c0 += OP_KCHUNK) {
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < PER_T; ++k) {
+      const int e = tid + 256 * k;
+      if (e < pieces) {
+        const int r = e / (row_bytes / 16), cc = e % (row_bytes / 16);
+        *reinterpret_cast<u16x8*>(wsm + r * OP_PITCH + cc * 16) = stage[k];
+      }
+    }
+    __syncthreads();
+    if (c0 + OP_KCHUNK < p.d_c) { OP_FETCH(c0 + OP_KCHUNK) }
+#pragma unroll
+    for (int ks = 0; ks < OP_KCHUNK / 32; ++ks) {
+      // A: u[m][c0 + 32ks + 8g .. +8], split into bf16 hi + lo
+      f32x4 u0 = {0.f, 0.f, 0.f, 0.f}, u1 = u0;
+      if (m < M) {
+        u0 = *reinterpret_cast<const f32x4*>(ur + c0 + 32 * ks);
+        u1 = *reinterpret_cast<const f32x4*>(ur + c0 + 32 * ks + 4);
+      }
+      u16x8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = e < 4 ? u0[e] : u1[e - 4];
+        const uint16_t h = f32_to_bf16(x);
+        hi[e] = h;
+        lo[e] = f32_to_bf16(x - bf16_to_f32(h));
+      }
+      const bf16x8 ahi = __builtin_bit_cast(bf16x8, hi), alo = __builtin_bit_cast(bf16x8, lo);
+      // B: W[c0 + 32ks + 8g + 4ins + (l16 >> 2)][16vb + 4(l16 & 3) .. +4], transposed read
+#pragma unroll
+      for (int vb = 0; vb < OP_MAXV / 16; ++vb) {
+        if (vb < vblocks) {
+        bf16x4 bv[2];
+#pragma unroll
+        for (int ins = 0; ins < 2; ++ins) {
+          const int r = 32 * ks + 8 * g + 4 * ins + (l16 >> 2);
+          const unsigned char* ptr = wsm + r * OP_PITCH + (16 * vb + 4 * (l16 & 3)) * 2;
+          bv[ins] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (lds_bf16x4*)((__attribute__((address_space(3))) unsigned char*)ptr));
+        }
+        const bf16x8 b = __builtin_shufflevector(bv[0], bv[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b, acc[vb], 0, 0, 0);
+        acc[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b, acc[vb], 0, 0, 0);
+        }
+      }
+    }
+  }
+#undef OP_FETCH
+  // acc[vb][r] = o[m' = rowblock + 4g + r][16 vb + l16]
+  const int mrow0 = blockIdx.y * OP_MROWS + wave * 16 + 4 * g;
+#pragma unroll
+  for (int vb = 0; vb < OP_MAXV / 16; ++vb) {
+    if (vb < vblocks) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int mm = mrow0 + r;
+        if (mm < M) p.out[((int64_t)mm * p.n_h + i) * p.d_v + v0 + 16 * vb + l16] = acc[vb][r];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool absorb_mfma_ok(const AbsorbParams& p) {
+  return p.bf16 && p.d_nope % 32 == 0 && p.d_nope <= 32 * AB_MAXK && p.d_c % 64 == 0;
+}
+
+hipError_t launch_absorb_mfma(const AbsorbParams& p, hipStream_t stream) {
+  const int M = p.B * p.n_q;
+  hipLaunchKernelGGL(absorb_mfma_kernel, dim3(p.n_h, p.d_c / 64), dim3(256), 0, stream, p);
+  const int64_t nthreads = (int64_t)M * (p.d_rope / 2) * ((p.n_h + 3) / 4);
+  hipLaunchKernelGGL(rope_q_rows_kernel<uint16_t>, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+bool out_proj_mfma_ok(const OutProjParams& p) {
+  return p.bf16 && p.d_c % OP_KCHUNK == 0 && p.d_v % OP_VCOLS == 0;
+}
+
+hipError_t launch_out_proj_mfma(const OutProjParams& p, hipStream_t stream) {
+  const int M = p.B * p.n_q;
+  dim3 grid(p.n_h, (M + OP_MROWS - 1) / OP_MROWS, p.d_v / OP_VCOLS);
+  hipLaunchKernelGGL(out_proj_mfma_kernel, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -21,7 +21,7 @@ class DecodeStep:
         self.q_lat = torch.empty((B, n_q, dims.n_h, dims.d_c), dtype=dtype, device=device)
         self.q_pe = torch.empty((B, n_q, dims.n_h, dims.d_rope), dtype=dtype, device=device)
         self.u_part = torch.empty((slots, n_q, dims.n_h, dims.d_c), dtype=f32, device=device)
-        self.lse_part = torch.empty((slots, n_q, dims.n_h), dtype=f32, device=device)
+        self.lse_part = torch.empty((slots, n_q, dims.n_h, 2), dtype=f32, device=device)
         self.u = torch.empty((B, n_q, dims.n_h, dims.d_c), dtype=f32, device=device)
         self.lse = torch.empty((B, n_q, dims.n_h), dtype=f32, device=device)
         self.out = torch.empty((B, n_q, dims.n_h, dims.d_v), dtype=f32, device=device)

@@ -1,0 +1,39 @@
+"""GPU parity at the full sizes of the DeepSeek-V3-shaped workloads, in the
+launch configuration bench.py times (default split count), on outputs the
+oracle computes one by one: sampled sequences (shortest and longest of the
+ragged batch included) and sampled heads of each.  Tolerance 1e-2 (bf16)."""
+import numpy as np
+import pytest
+
+import workloads as W
+from tests.test_gpu_parity import _check, _need_gpu, torch
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "v3_b1": (lambda ctx: [0], list(range(128))),
+    "v3_b64": (lambda ctx: [0, 37, 63], [0, 1, 31, 32, 64, 95, 100, 127]),
+    "v3_paged": (lambda ctx: sorted({int(np.argmin(ctx)), int(np.argmax(ctx)), 77}), [0, 45, 90, 127]),
+    "v3_split": (lambda ctx: [0, 3], [0, 63, 64, 127]),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_full_size_sampled(name):
+    _need_gpu()
+    from mla_latent_kv_02_amd.plan import default_num_splits
+    from mla_latent_kv_02_amd.step import DecodeStep
+    from workloads.device import stage
+    w = W.get(name)
+    st = stage(w)
+    ctx = st["ctx_host"]
+    ns = default_num_splits(int(ctx.sum()), w.n_q, w.n_h)
+    step = DecodeStep(st["dims"], w.batch, w.n_q, ns, torch.bfloat16)
+    step.run(st["q_nope"], st["q_rope"], st["positions"], st["w_uk"], st["w_uv"], st["cache"])
+    torch.cuda.synchronize()
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)
+    got = {"q_lat": f(step.q_lat), "q_pe": f(step.q_pe), "u": f(step.u), "lse": f(step.lse), "o": f(step.out)}
+    assert np.isfinite(got["o"]).all() and np.isfinite(got["lse"]).all()
+    seqs, heads = CASES[name]
+    print(f"{name}: num_splits={ns}, total tokens {int(ctx.sum())}", flush=True)
+    _check(w, st, got, seqs=seqs(ctx), heads=heads)

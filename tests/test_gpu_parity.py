@@ -166,6 +166,9 @@ def test_split_invariance_and_determinism():
 
 
 def test_combine_alone_against_oracle():
+    """Partials in the documented format (unnormalised value sum with its
+    reference r, and lse) merged by mla_combine vs the oracle's merge of the
+    normalised partials u_k = u_part_k * exp(r_k - lse_k)."""
     _need_gpu()
     import mla_latent_kv_02_amd as mla
     rng = np.random.default_rng(5)
@@ -173,14 +176,18 @@ def test_combine_alone_against_oracle():
     ctx = np.array([10, 1, 35, 7], np.int32)
     num_splits = 6
     slots = mla.mla_num_partials(len(ctx), num_splits)
-    u_part = rng.standard_normal((slots, 1, 8, 64)).astype(np.float32)
-    lse_part = (rng.standard_normal((slots, 1, 8)) * 5).astype(np.float32)
-    lse_part[1, 0, 3] = -np.inf
+    u_norm = rng.standard_normal((slots, 1, 8, 64))
+    lse = rng.standard_normal((slots, 1, 8)) * 5
+    ref_shift = rng.standard_normal((slots, 1, 8)) * 3          # arbitrary references r_k
+    lse[1, 0, 3] = -np.inf
+    u_part = (u_norm * np.exp(lse - ref_shift)[..., None]).astype(np.float32)
     u_part[1, 0, 3] = 0
+    rl = np.stack([ref_shift, lse], axis=-1).astype(np.float32)
+    rl[1, 0, 3] = (0.0, -np.inf)
     u = torch.empty((4, 1, 8, 64), device="cuda")
-    lse = torch.empty((4, 1, 8), device="cuda")
+    lse_out = torch.empty((4, 1, 8), device="cuda")
     mla.mla_combine(dims, torch.from_numpy(ctx).cuda(), num_splits, torch.from_numpy(u_part).cuda(),
-                    torch.from_numpy(lse_part).cuda(), u, lse)
+                    torch.from_numpy(rl).cuda(), u, lse_out)
     torch.cuda.synchronize()
     # slots of each sequence under the documented plan
     total = int(ctx.sum())
@@ -189,9 +196,9 @@ def test_combine_alone_against_oracle():
     base = 0
     for b in range(4):
         n = (prefix[b] + ctx[b] - 1) // q - prefix[b] // q + 1
-        ref_u, ref_l = oracle.merge_partials(u_part[base:base + n], lse_part[base:base + n])
+        ref_u, ref_l = oracle.merge_partials(u_norm[base:base + n], lse[base:base + n])
         assert vec_rel_err(u[b].cpu().numpy(), ref_u) < 1e-5
-        assert scalar_err(lse[b].cpu().numpy(), ref_l) < 1e-6
+        assert scalar_err(lse_out[b].cpu().numpy(), ref_l) < 1e-6
         base += n
     assert base <= slots
 
