@@ -8,9 +8,11 @@
 // query rows (heads x query tokens) of one sequence and streams each cache
 // tile through LDS once:
 //
-//   S^T[tok][row]  = K_tile[tok][0:576] . [q_lat | q_pe]^T      (MFMA 16x16x32)
-//   online softmax over tokens, in registers (a lane holds 2 rows x 8 tokens)
-//   O^T[lat][row] += V_tile^T[lat][tok] . P^T[tok][row]          (MFMA 16x16x32)
+//   S^T[tok][row]  = K_tile[tok][0:576] . [q_lat | q_pe]^T      (MFMA 32x32x16)
+//   softmax over tokens, in registers (a lane holds 1 row x 16 tokens)
+//   O^T[lat][row] += V_tile^T[lat][tok] . P^T[tok][row]          (MFMA 32x32x16)
+// (32x32x16 is the full-rate bf16 MFMA shape on gfx950; 16x16x32 issues at
+// half the rate.)
 //
 // Workgroup = 4 waves; wave w owns 32 query rows (one query token, 32 heads)
 // for both products.  The K operand of QK^T is read from LDS with 16-byte
@@ -48,12 +50,11 @@ constexpr int ROW = DC + DR;          // 576 elements
 constexpr int T = 32;                 // tokens per pipeline stage
 constexpr int NSTAGE = 4;             // LDS ring: NSTAGE - 1 stages in flight while one is used
 constexpr int NT = 256;               // threads per workgroup
-constexpr int KSTEPS = ROW / 32;      // 18 MFMA k-steps for QK^T
+constexpr int KSTEPS = ROW / 16;      // 36 MFMA k-steps (32x32x16) for QK^T
 constexpr int CGROUPS = ROW / 64;     // 9 chunk groups of 8 chunks
 constexpr int CG_BYTES = T * 128;     // one chunk group of a stage: 32 tokens x 128 B
 constexpr int STAGE_BYTES = CGROUPS * CG_BYTES;   // 36864
 constexpr int LOADS_PER_STAGE = CGROUPS;          // 16-byte-per-lane loads per wave per stage
-constexpr int MBLK = DC / 16;         // 32 latent blocks of 16
 constexpr float REF_HEADROOM = 64.f;  // log2 units a score may exceed its row's reference
 
 struct DecodeArgs {
@@ -72,7 +73,7 @@ __device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 
 
 struct __attribute__((aligned(16))) DecodeSmem {
   unsigned char stage[NSTAGE][STAGE_BYTES];
-  bf16x8 pbuf[8][64];        // softmax weights of the stage, MFMA B-operand layout, per head block
+  bf16x8 pbuf[4][2][64];     // softmax weights of the stage: [head block][k-step][lane], B-operand layout
   int flag[4];               // per wave: a score ran past its row's reference (redo needed)
   PlanScratch<NT> plan;
 };
@@ -134,12 +135,12 @@ __device__ __forceinline__ void lds_barrier() {
 // builtin so that the compiler's own wait insertion sees them.
 constexpr int kWaitVm0 = 0x0F70, kWaitVm9 = 0x0F79, kWaitVm18 = 0x4F72;
 
-// O += A . B for one 16x16 block of the PV product, with the accumulator pinned
+// O += A . B for one 32x32 block of the PV product, with the accumulator pinned
 // to AGPRs.  O needs all 256 AGPRs; the QK^T accumulators (built-in MFMAs,
 // compiled in the VGPR form) stay in VGPRs, so the allocator never moves O
 // blocks between register files inside the stage loop.
-__device__ __forceinline__ void pv_mfma(f32x4& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+__device__ __forceinline__ void pv_mfma(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 // Wait states between the last PV MFMA and any other read of its accumulator
 // (the compiler cannot see the MFMA inside the asm statements above).
@@ -157,11 +158,17 @@ static_assert(LOADS_PER_STAGE == 9 && NSTAGE == 4, "wait counts assume 9 loads p
 
 // Work split inside a workgroup of 4 waves serving 128 query rows:
 //   QK^T and softmax: wave w owns rows 32w .. 32w+31 (its heads' queries stay in
-//     registers as the MFMA B operand);
-//   PV: wave w owns latent columns 128w .. 128w+127 for all 128 rows, so each
-//     V element is read from LDS once per workgroup; the softmax weights of all
-//     rows come through LDS (each wave's weights are already in the B-operand
-//     lane layout, so the exchange is a 16-byte copy per lane and head block).
+//     registers as the MFMA B operand); per stage it computes one 32-token x
+//     32-row block S^T with 32x32x16 MFMAs (two accumulation chains over
+//     alternate k-steps).  Lane l holds row l%32 and tokens
+//     8*(i/4) + 4*(l/32) + i%4 (i < 16) of the block.
+//   PV: wave w owns latent columns 128w .. 128w+127 for all 128 rows (4 x 4
+//     blocks of 32x32), so each V element is read from LDS once per workgroup.
+//     The k index of the PV MFMA is mapped to tokens so that a lane's own
+//     softmax weights are its B operand (k = 8*(l/32) + e <-> token
+//     16q + 8*(e/4) + 4*(l/32) + e%4 for k-step q), and V^T is read with the
+//     same token order by transposed 4x16 LDS reads.  The weights of all rows
+//     pass through LDS as 16-byte copies.
 // The accumulator O is touched only by MFMAs and by the final store: the
 // weights use a fixed per-row reference (the row's maximum over the first
 // stage), which needs no rescaling of O.  If a later score exceeds the
@@ -174,7 +181,9 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g4 = lane >> 4;         // lane group of 16
+  const int h = lane >> 5;          // lane half
+  const int l32 = lane & 31;
+  const int g4 = lane >> 4;         // lane group of 16 (transposed reads)
   const int l16 = lane & 15;
 
   // block -> (work unit, row group); the groups of one unit sit 8 blocks apart
@@ -192,21 +201,17 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
 
   for_each_segment<NT>(a.ctx_lens, a.B, a.num_splits, w, &sm->plan,
                        [&](int b, int t0, int t1, int slot) {
-    // ---- query operand (B of QK^T): row row0 + 16*hb + l16, k = 32*ks + 8*g4 .. +8
-    bf16x8 qreg[2][KSTEPS];
+    // ---- query operand (B of QK^T): row row0 + l32, k = 16*ks + 8*h .. +8
+    bf16x8 qreg[KSTEPS];
     int limit = t1;
     if (active) {
+      const int64_t qrow = (int64_t)b * rows + row0 + l32;
+      const u16x8* ql = reinterpret_cast<const u16x8*>(a.q_lat + qrow * DC);
+      const u16x8* qp = reinterpret_cast<const u16x8*>(a.q_pe + qrow * DR);
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const int64_t qrow = (int64_t)b * rows + row0 + 16 * hb + l16;
-        const u16x8* ql = reinterpret_cast<const u16x8*>(a.q_lat + qrow * DC);
-        const u16x8* qp = reinterpret_cast<const u16x8*>(a.q_pe + qrow * DR);
+      for (int ks = 0; ks < DC / 16; ++ks) qreg[ks] = __builtin_bit_cast(bf16x8, ql[2 * ks + h]);
 #pragma unroll
-        for (int ks = 0; ks < DC / 32; ++ks) qreg[hb][ks] = __builtin_bit_cast(bf16x8, ql[4 * ks + g4]);
-#pragma unroll
-        for (int ks = DC / 32; ks < KSTEPS; ++ks)
-          qreg[hb][ks] = __builtin_bit_cast(bf16x8, qp[4 * (ks - DC / 32) + g4]);
-      }
+      for (int ks = DC / 16; ks < KSTEPS; ++ks) qreg[ks] = __builtin_bit_cast(bf16x8, qp[2 * (ks - DC / 16) + h]);
       const int qpos = a.positions[(int64_t)b * a.n_q + jq];
       limit = qpos + 1 < t1 ? qpos + 1 : t1;
     }
@@ -214,128 +219,170 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
     // vector-memory counter also covers the stage loads
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     // per-lane LDS byte offsets that do not depend on the stage
-    const int sw_qk = swz(l16 & 7);
-    int qk_off[2];
+    const int sw_qk = swz(l32 & 7);
+    int qk_off[4];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) qk_off[r] = l16 * 128 + (((4 * r + g4) ^ sw_qk) << 4);
-    const int tr_tok = 4 * g4 + (l16 >> 2);                // token (mod 16) of this lane's row
-    const int sw_tr = swz(tr_tok & 7);
+    for (int r = 0; r < 4; ++r) qk_off[r] = l32 * 128 + (((2 * r + h) ^ sw_qk) << 4);
+    const int hq = g4 >> 1;                              // k half of this lane's transposed read
+    const int tr_tok = 4 * hq + (l16 >> 2);              // token (mod 8) of this lane's row
+    const int sw_tr = swz(tr_tok);
     const int half8 = (l16 & 1) * 8;
-    const int cch = (l16 & 3) >> 1;                        // chunk within a chunk pair
+    const int cch = 2 * (g4 & 1) + ((l16 & 3) >> 1);     // chunk within a group of 4
     const int nst = (t1 - t0 + T - 1) / T;
 
-    // m_ref: reference (log2 units) of each of the lane's two QK rows;
-    // m_max: running maximum of the row's scores
-    float m_ref[2] = {-INFINITY, -INFINITY}, m_max[2] = {-INFINITY, -INFINITY};
-    float l_run[2];
-    // O^T accumulators of this wave: latent block mb (16 latents at 128*wave + 16*mb)
-    // x head block hb (rows grow0 + 16*hb .. +16)
-    f32x4 o[8][8];
+    // m_ref: reference (log2 units) of the lane's QK row; m_max: running maximum
+    float m_ref = -INFINITY, m_max = -INFINITY;
+    float l_run;
+    // O^T accumulators of this wave: latent block mb (32 latents at 128*wave + 32*mb)
+    // x head block hb (rows grow0 + 32*hb .. +32)
+    f32x16 o[4][4];
+    // K operand of QK^T for k-step ks from a stage buffer
+    auto rd_k = [&](const unsigned char* sb, int ks) -> bf16x8 {
+      const unsigned char* p = sb + (ks >> 2) * CG_BYTES + qk_off[ks & 3];
+      return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+          (const __attribute__((address_space(3))) unsigned char*)p);
+    };
+    // V^T operand of PV for k-step q and latent block mb (32 latents of this wave)
+    auto rd_v = [&](const unsigned char* sb, int q, int mb) -> bf16x8 {
+      const int mbg = 4 * wave + mb;                   // global latent block (32 latents)
+      const int cq = 4 * (mbg & 1) + cch;
+      bf16x4 v[2];
+#pragma unroll
+      for (int ins = 0; ins < 2; ++ins) {
+        const int t = 16 * q + 8 * ins + tr_tok;
+        const unsigned char* p = sb + (mbg >> 1) * CG_BYTES + t * 128 + ((cq ^ sw_tr) << 4) + half8;
+        v[ins] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4*)((__attribute__((address_space(3))) unsigned char*)p));
+      }
+      return __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    constexpr int PF = 2;
+
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int hb = 0; hb < 8; ++hb) o[mb][hb] = f32x4{};
-      l_run[0] = l_run[1] = 0.f;
+        for (int hb = 0; hb < 4; ++hb) o[mb][hb] = f32x16{};
+      l_run = 0.f;
       bool over = false;
 #pragma unroll
       for (int s = 0; s < NSTAGE - 1; ++s)
         if (s < nst) load_stage(a, b, t0 + s * T, t1, sm->stage[s], wave, lane);
 
+      // Software pipeline: iteration it computes S^T of stage it+1 (MFMA) while
+      // it turns the scores of stage it into weights (VALU), then accumulates
+      // PV of stage it.  Stage it+3 is loaded into the slot stage it-1 freed.
+      // s_cur: scores of the stage whose weights come next (two MFMA chains summed).
+      f32x16 s_cur = f32x16{};
+      // S^T of one stage into s_cur (no overlap; pipeline fill and edges)
+      auto qk_plain = [&](const unsigned char* sb) {
+        f32x16 c0 = f32x16{}, c1 = f32x16{};
+        bf16x8 kring[PF];
+#pragma unroll
+        for (int ks = 0; ks < PF; ++ks) kring[ks] = rd_k(sb, ks);
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          const bf16x8 kk = kring[ks % PF];
+          if (ks + PF < KSTEPS) kring[ks % PF] = rd_k(sb, ks + PF);
+          if (ks & 1) c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qreg[ks], c1, 0, 0, 0);
+          else c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qreg[ks], c0, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        s_cur = c0 + c1;
+      };
+      // softmax pieces on s_cur for stage tokens tok0..: scale + mask, row max, weights
+      auto sm_scale_mask = [&](int tok0, float* x, float& mt) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int tok = tok0 + 8 * (i >> 2) + 4 * h + (i & 3);
+          const float v = s_cur[i] * a.scale_log2;
+          x[i] = tok < limit ? v : -INFINITY;
+          mt = fmaxf(mt, x[i]);
+        }
+      };
+      auto sm_rowmax = [&](float& mt, bool& ov) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+        mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        m_max = fmaxf(m_max, mt);
+        if (m_ref == -INFINITY) m_ref = mt;       // first visible stage of the row
+        ov |= mt > m_ref + REF_HEADROOM;
+      };
+      auto sm_weights = [&](const float* x, int q, bf16x8* pb, float& psum) {
+        const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = __builtin_amdgcn_exp2f(x[8 * q + e] - m_use);
+          psum += p;
+          pb[q][e] = (__bf16)p;
+        }
+      };
+
+      wait_stages_in_flight(nst - 1 < NSTAGE - 2 ? nst - 1 : NSTAGE - 2);
+      lds_barrier();
+      if (active && t0 < limit) qk_plain(sm->stage[0]);
+
       for (int it = 0; it < nst; ++it) {
-        const int after = nst - 1 - it;     // stages already issued beyond this one (at most 2)
-        wait_stages_in_flight(after < NSTAGE - 2 ? after : NSTAGE - 2);
+        const bool has_next = it + 1 < nst;
+        if (has_next) wait_stages_in_flight(it + 2 < nst ? 1 : 0);   // stage it+1 resident
         lds_barrier();
         if (it + NSTAGE - 1 < nst)
           load_stage(a, b, t0 + (it + NSTAGE - 1) * T, t1, sm->stage[(it + NSTAGE - 1) % NSTAGE], wave, lane);
         const int tok0 = t0 + it * T;
-        unsigned char* sbuf = sm->stage[it % NSTAGE];
+        const bool qk_now = active && tok0 < limit;                     // weights of stage it
+        const bool qk_next = active && has_next && tok0 + T < limit;    // scores of stage it+1
+        const unsigned char* sb_next = sm->stage[(it + 1) % NSTAGE];
         bf16x8 pb[2] = {bf16x8{}, bf16x8{}};
-        if (active && tok0 < limit) {
-          // ------------ S^T = K . Q^T for 32 tokens: 4 chains (token block tb x head block hb),
-          // K operands read from LDS PF k-steps ahead of their use.
-          auto rd_k = [&](int ks, int tb) -> bf16x8 {
-            const unsigned char* p = sbuf + (ks >> 1) * CG_BYTES + tb * 2048 + qk_off[ks & 1];
-            return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
-                (const __attribute__((address_space(3))) unsigned char*)p);
-          };
-          constexpr int PF = 2;
-          f32x4 sacc[2][2] = {{f32x4{}, f32x4{}}, {f32x4{}, f32x4{}}};
-          bf16x8 kring[PF][2];
+        float x[16];
+        float psum = 0.f, mt = -INFINITY;
+        if (qk_now && qk_next) {
+          // ------------ S^T(it+1) by MFMA, interleaved with the softmax of stage it
+          f32x16 c0 = f32x16{}, c1 = f32x16{};
+          bf16x8 kring[PF];
 #pragma unroll
-          for (int ks = 0; ks < PF; ++ks) { kring[ks][0] = rd_k(ks, 0); kring[ks][1] = rd_k(ks, 1); }
+          for (int ks = 0; ks < PF; ++ks) kring[ks] = rd_k(sb_next, ks);
 #pragma unroll
           for (int ks = 0; ks < KSTEPS; ++ks) {
-            const bf16x8 k0 = kring[ks % PF][0], k1 = kring[ks % PF][1];
-            if (ks + PF < KSTEPS) { kring[ks % PF][0] = rd_k(ks + PF, 0); kring[ks % PF][1] = rd_k(ks + PF, 1); }
-            sacc[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qreg[0][ks], sacc[0][0], 0, 0, 0);
-            sacc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qreg[1][ks], sacc[0][1], 0, 0, 0);
-            sacc[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qreg[0][ks], sacc[1][0], 0, 0, 0);
-            sacc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qreg[1][ks], sacc[1][1], 0, 0, 0);
+            const bf16x8 kk = kring[ks % PF];
+            if (ks + PF < KSTEPS) kring[ks % PF] = rd_k(sb_next, ks + PF);
+            if (ks & 1) c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qreg[ks], c1, 0, 0, 0);
+            else c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qreg[ks], c0, 0, 0, 0);
+            if (ks == 1) sm_scale_mask(tok0, x, mt);
+            if (ks == 4) sm_rowmax(mt, over);
+            if (ks == 7) sm_weights(x, 0, pb, psum);
+            if (ks == 10) sm_weights(x, 1, pb, psum);
             __builtin_amdgcn_sched_barrier(0);
           }
-          // ------------ softmax weights; lane holds rows (hb, l16), tokens 16*tb + 4*g4 + i
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb) {
-            float mt = -INFINITY;
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int tok = tok0 + 16 * tb + 4 * g4 + i;
-                float x = sacc[tb][hb][i] * a.scale_log2;
-                x = tok < limit ? x : -INFINITY;
-                sacc[tb][hb][i] = x;
-                mt = fmaxf(mt, x);
-              }
-            mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-            m_max[hb] = fmaxf(m_max[hb], mt);
-            if (m_ref[hb] == -INFINITY) m_ref[hb] = mt;       // first visible stage of the row
-            over |= mt > m_ref[hb] + REF_HEADROOM;
-            const float m_use = m_ref[hb] == -INFINITY ? 0.f : m_ref[hb];
-            float psum = 0.f;
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const float p = __builtin_amdgcn_exp2f(sacc[tb][hb][i] - m_use);
-                psum += p;
-                pb[hb][4 * tb + i] = (__bf16)p;
-              }
-            l_run[hb] += psum;
+          s_cur = c0 + c1;
+        } else {
+          if (qk_now) {
+            sm_scale_mask(tok0, x, mt);
+            sm_rowmax(mt, over);
+            sm_weights(x, 0, pb, psum);
+            sm_weights(x, 1, pb, psum);
           }
+          if (qk_next) qk_plain(sb_next);
         }
-        // ------------ publish this wave's weights (B-operand layout)
-        sm->pbuf[2 * wave][lane] = pb[0];
-        sm->pbuf[2 * wave + 1][lane] = pb[1];
+        l_run += psum;
+        // ------------ publish this wave's weights (B-operand layout, per k-step)
+        sm->pbuf[wave][0][lane] = pb[0];
+        sm->pbuf[wave][1][lane] = pb[1];
         lds_barrier();
-        // ------------ O^T[own 128 latents][128 rows] += V^T . P^T: 8 latent blocks,
-        // each fed by two transposed LDS reads and reused for the 8 head blocks.
-        bf16x8 pall[8];
+        // ------------ O^T[own 128 latents][128 rows] += V^T . P^T for stage it
+        const unsigned char* sb = sm->stage[it % NSTAGE];
 #pragma unroll
-        for (int hb = 0; hb < 8; ++hb) pall[hb] = sm->pbuf[hb][lane];
-        auto rd_v = [&](int mb) -> bf16x8 {
-          const int mbg = 8 * wave + mb;                   // global latent block (16 latents)
-          const int cq = 2 * (mbg & 3) + cch;
-          bf16x4 v[2];
+        for (int q = 0; q < 2; ++q) {
+          bf16x8 pq[4];
 #pragma unroll
-          for (int ins = 0; ins < 2; ++ins) {
-            const int t = 16 * ins + tr_tok;
-            const unsigned char* p = sbuf + (mbg >> 2) * CG_BYTES + t * 128 + ((cq ^ sw_tr) << 4) + half8;
-            v[ins] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (lds_bf16x4*)((__attribute__((address_space(3))) unsigned char*)p));
+          for (int hb = 0; hb < 4; ++hb) pq[hb] = sm->pbuf[hb][q][lane];
+          bf16x8 va = rd_v(sb, q, 0);
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb) {
+            const bf16x8 cur = va;
+            if (mb + 1 < 4) va = rd_v(sb, q, mb + 1);
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb) pv_mfma(o[mb][hb], cur, pq[hb]);
+            __builtin_amdgcn_sched_barrier(0);
           }
-          return __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
-        };
-        bf16x8 va = rd_v(0);
-#pragma unroll
-        for (int mb = 0; mb < 8; ++mb) {
-          const bf16x8 cur = va;
-          if (mb + 1 < 8) va = rd_v(mb + 1);
-#pragma unroll
-          for (int hb = 0; hb < 8; ++hb) pv_mfma(o[mb][hb], cur, pall[hb]);
-          __builtin_amdgcn_sched_barrier(0);
         }
       }
       // ------------ did any row of the workgroup outgrow its reference?
@@ -345,32 +392,32 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
       const bool redo = (sm->flag[0] | sm->flag[1] | sm->flag[2] | sm->flag[3]) != 0;
       __syncthreads();
       if (!redo) break;
-      m_ref[0] = m_max[0];
-      m_ref[1] = m_max[1];
+      m_ref = m_max;
     }
     pv_mfma_drain();
     // ---------------- write the partial of this segment (unnormalised; see mla.h)
     if (active) {
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        float l_tot = l_run[hb] + __shfl_xor(l_run[hb], 16, 64);
-        l_tot += __shfl_xor(l_tot, 32, 64);
-        if (g4 == 0) {
-          const int r = row0 + 16 * hb + l16;
-          float2 rl;
-          rl.x = l_tot > 0.f ? m_ref[hb] * kLn2 : 0.f;
-          rl.y = l_tot > 0.f ? (m_ref[hb] + __log2f(l_tot)) * kLn2 : -INFINITY;
-          reinterpret_cast<float2*>(a.lse_part)[(int64_t)slot * rows + r] = rl;
-        }
+      const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+      if (h == 0) {
+        const int r = row0 + l32;
+        float2 rl;
+        rl.x = l_tot > 0.f ? m_ref * kLn2 : 0.f;
+        rl.y = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
+        reinterpret_cast<float2*>(a.lse_part)[(int64_t)slot * rows + r] = rl;
       }
     }
+    // o[mb][hb][i] = u[row grow0 + 32 hb + l32][latent 128 wave + 32 mb + 8 (i/4) + 4 h + i%4]
 #pragma unroll
-    for (int hb = 0; hb < 8; ++hb) {
-      const int r = grow0 + 16 * hb + l16;
+    for (int hb = 0; hb < 4; ++hb) {
+      const int r = grow0 + 32 * hb + l32;
       if (r < rows) {
-        float* up = a.u_part + ((int64_t)slot * rows + r) * DC + 128 * wave + 4 * g4;
+        float* up = a.u_part + ((int64_t)slot * rows + r) * DC + 128 * wave + 4 * h;
 #pragma unroll
-        for (int mb = 0; mb < 8; ++mb) *reinterpret_cast<f32x4*>(up + 16 * mb) = o[mb][hb];
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4)
+            *reinterpret_cast<f32x4*>(up + 32 * mb + 8 * i4) =
+                f32x4{o[mb][hb][4 * i4], o[mb][hb][4 * i4 + 1], o[mb][hb][4 * i4 + 2], o[mb][hb][4 * i4 + 3]};
       }
     }
     __syncthreads();   // all waves done with the ring and the exchange buffers
