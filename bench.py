@@ -37,7 +37,10 @@ def parse():
     ap.add_argument("--workload", default="v3_b64")
     ap.add_argument("--num-splits", type=int, default=0, help="0 = library default for the batch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=16, help="heads of one sequence in the CPU sample")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain fp32 copy kernel (dst = -src) over this many MiB, 5 times: the "
+                         "calibration run for the HBM byte counters")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time in the CPU sample")
     return ap.parse_args()
 
 
@@ -62,8 +65,16 @@ def decode_flops(w, ctx, pos):
     return int(visible) * w.n_h * 2 * (2 * w.d_c + w.d_rope)
 
 
-def cpu_baseline(w, heads_n):
-    """fp64 oracle on one sequence and a subset of its heads."""
+def cpu_baseline(w, min_seconds=10.0, head_group=16):
+    """The fp64 oracle timed on a bounded sample of the same workload.
+
+    Sequences are taken shortest and longest first, then in index order; each
+    sequence is decoded for all its query tokens, one group of heads at a time,
+    until the oracle has run for at least ``min_seconds`` (one group of 16
+    heads is a few seconds at most).  Only the oracle calls are timed, not
+    the generation of the synthetic rows.  GB/s = cache bytes the sample
+    attended (each sequence's rows times the fraction of heads done) / time.
+    """
     import numpy as np
     import oracle
     import workloads as W
@@ -71,24 +82,82 @@ def cpu_baseline(w, heads_n):
         from threadpoolctl import threadpool_info
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
-        cores = len(os.sched_getaffinity(0))
+        cores = 1
     ctx = W.context_lengths(w)
-    b = int(np.argmin(ctx)) if w.ctx is None else 0
-    heads = list(range(min(heads_n, w.n_h)))
-    rows = W.cache_rows(w, b, 0, int(ctx[b]))
+    order = [int(np.argmin(ctx)), int(np.argmax(ctx))] + list(range(w.batch))
+    order = list(dict.fromkeys(order))
     wt, q = W.weights(w), W.queries(w)
     pos = W.positions(w, ctx)
-    t0 = time.perf_counter()
-    oracle.decode_sequence(q["q_nope"][b], q["q_rope"][b], pos[b], rows["c_kv"], rows["k_rope_raw"],
-                           wt["w_uk"], wt["w_uv"], w.sm_scale, w.rope_base, heads=heads)
-    dt = time.perf_counter() - t0
     eb = 2 if w.dtype == "bf16" else 4
-    # cache bytes the sample consumed, counted per head (the oracle's cost scales with heads)
-    sample_bytes = int(ctx[b]) * w.row * eb * len(heads) / w.n_h
-    return {"value": round(sample_bytes / dt / 1e9, 6), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"sequence {b} (ctx {int(ctx[b])}), {len(heads)} of {w.n_h} heads, fp64 reconstruct-then-"
-                      f"attend; GB/s = cache bytes x heads/{w.n_h} / {dt:.2f} s",
-            "seconds": round(dt, 3)}
+    spent, sample_bytes, head_rows, done = 0.0, 0.0, 0, []
+    for b in order:
+        rows = W.cache_rows(w, b, 0, int(ctx[b]))
+        heads_done = 0
+        for h0 in range(0, w.n_h, head_group):
+            heads = list(range(h0, min(h0 + head_group, w.n_h)))
+            t0 = time.perf_counter()
+            oracle.decode_sequence(q["q_nope"][b], q["q_rope"][b], pos[b], rows["c_kv"], rows["k_rope_raw"],
+                                   wt["w_uk"], wt["w_uv"], w.sm_scale, w.rope_base, heads=heads)
+            spent += time.perf_counter() - t0
+            heads_done += len(heads)
+            if spent >= min_seconds:
+                break
+        sample_bytes += int(ctx[b]) * w.row * eb * heads_done / w.n_h
+        head_rows += heads_done * w.n_q
+        done.append(f"{b}(ctx {int(ctx[b])}, {heads_done} heads)")
+        if spent >= min_seconds:
+            break
+    return {"value": round(sample_bytes / spent / 1e9, 6), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"sequences {', '.join(done)} of {w.name}, all {w.n_q} query token(s), heads in groups of "
+                      f"{head_group}; fp64 reconstruct-then-attend; GB/s = attended cache bytes x heads done/"
+                      f"{w.n_h} / oracle time",
+            "seconds": round(spent, 3),
+            "head_rows_per_s": round(head_rows / spent, 3)}
+
+
+DECODE_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "mla_latent_kv_02_amd", "csrc",
+                             "decode_mfma.hip")
+PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+
+
+def measured_traffic(workload):
+    """HBM bytes per decode launch from the committed counter summaries.
+
+    A summary under profiles/ carries a line ``traffic-record: {json}`` with the
+    workload, the sha256 of the decode kernel's source when the counters were
+    taken, and the calibrated FETCH_SIZE + WRITE_SIZE bytes per launch.  The
+    figure is returned only while the source is unchanged; otherwise None.
+    """
+    import hashlib
+    try:
+        with open(DECODE_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        names = sorted(os.listdir(PROFILES))
+    except OSError:
+        return None
+    for name in names:
+        if not name.endswith((".md", ".txt")):
+            continue
+        with open(os.path.join(PROFILES, name)) as f:
+            for line in f:
+                if not line.startswith("traffic-record:"):
+                    continue
+                rec = json.loads(line.split(":", 1)[1])
+                if rec.get("workload") == workload and rec.get("source_sha256") == sha:
+                    return int(rec["fetch_bytes"] + rec["write_bytes"])
+    return None
+
+
+def copy_probe(mib):
+    """A plain elementwise copy of known size, for scaling the byte counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"copy probe: 5 x {mib} MiB read + {mib} MiB written")
 
 
 def main():
@@ -97,6 +166,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); multi-GPU sharding of this "
               f"path is a design note, not a measured configuration.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
     import numpy as np
     import torch
     import mla_latent_kv_02_amd as mla
@@ -184,14 +256,14 @@ def main():
         "step_bytes": nbytes["step"],
         "roofline": {"kernel": "mla_decode (decode_mfma_kernel)", "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": nbytes["decode"], "avg_launch_us": round(dec_avg * 1e3, 3),
+                     "traffic": measured_traffic(w.name), "bytes_per_launch": nbytes["decode"], "avg_launch_us": round(dec_avg * 1e3, 3),
                      "mfma_tflops": round(flops / (dec_avg * 1e-3) / 1e12, 2),
                      "mfma_frac": round(flops / (dec_avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a CPU sample")
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

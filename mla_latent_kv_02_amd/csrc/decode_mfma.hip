@@ -38,6 +38,9 @@
 // Split-KV: the workgroup walks the segments of its work unit (see
 // for_each_segment) and writes one normalised partial (u, lse) per segment.
 
+#include <climits>
+#include <type_traits>
+
 #include "mla_device.h"
 #include "launch.h"
 
@@ -56,6 +59,9 @@ constexpr int CG_BYTES = T * 128;     // one chunk group of a stage: 32 tokens x
 constexpr int STAGE_BYTES = CGROUPS * CG_BYTES;   // 36864
 constexpr int LOADS_PER_STAGE = CGROUPS;          // 16-byte-per-lane loads per wave per stage
 constexpr float REF_HEADROOM = 64.f;  // log2 units a score may exceed its row's reference
+// Word 3 of a raw buffer resource on gfx9-class chips (32-bit data format, no
+// swizzle, offsets in bytes); words 0-2 carry the base and the byte range.
+constexpr int kBufferWord3 = 0x00020000;
 
 struct DecodeArgs {
   const uint16_t* q_lat;   // [B][n_q][n_h][512]
@@ -93,34 +99,87 @@ __device__ __forceinline__ int block_id_scalar(const CacheView& c, int b, int to
   return v;
 }
 
-// This wave's share of the global->LDS loads of one stage: stage tokens
-// 8*wave + lane/8, all 9 chunk groups (9 loads of 1 KiB per wave).
-__device__ __forceinline__ void load_stage(const DecodeArgs& a, int b, int tok0, int tok_end,
-                                           unsigned char* buf, int wave, int lane) {
-  const unsigned char* base = static_cast<const unsigned char*>(a.cache.data);
-  const int tt = 8 * wave + (lane >> 3);
-  int tok = tok0 + tt;
-  tok = tok < tok_end ? tok : tok_end - 1;   // rows past the segment repeat a valid row
-  int64_t off;
-  const CacheView& c = a.cache;
-  if (c.block_size == 0) {
-    off = (int64_t)b * c.seq_stride + (int64_t)tok * ROW;
-  } else if (c.block_size >= T) {
-    // the stage's tokens lie in at most two blocks: those of its first and last token
-    const int last = tok0 + T - 1 < tok_end - 1 ? tok0 + T - 1 : tok_end - 1;
-    const int blk0 = block_id_scalar(c, b, tok0);
-    const int blk1 = block_id_scalar(c, b, last);
-    const int blk = tok / c.block_size == tok0 / c.block_size ? blk0 : blk1;
-    off = ((int64_t)blk * c.block_size + tok % c.block_size) * ROW;
-  } else {
-    off = cache_row_offset(c, b, tok);
+// Cache layouts the kernel is compiled for.
+enum Layout : int {
+  kContiguous = 0,   // [B][seq_stride] rows; a sequence's rows (plus one stage) span < 4 GiB
+  kPaged = 1,        // block table, block_size >= T (a stage meets at most two blocks)
+  kAnyLayout = 2,    // any block size: per-token row lookup
+};
+
+// Issues this wave's share of the global->LDS loads of one stage: stage
+// tokens 8*wave + lane/8, all 9 chunk groups (9 loads of 1 KiB per wave).
+// Lane (token tt, chunk c%8) reads 16 bytes at chunk (c%8) ^ s(tt) of its
+// row, so the LDS slot it fills is the swizzled one (see the layout above).
+//
+// Contiguous caches use buffer loads: the resource (SGPRs) spans the
+// segment's rows of one sequence, so tokens past the segment end fall out of
+// range and read as zeros (never the cache's padding); each lane keeps one
+// 32-bit offset.  Paged and generic caches clamp such tokens to the last row
+// of the segment and use 64-bit per-lane addresses.
+template <int LAYOUT>
+struct StageLoader {
+  const unsigned char* base;   // contiguous: first row of the sequence; else cache base
+  __amdgpu_buffer_rsrc_t rsrc;
+  const CacheView* c;
+  int b, tok_end;
+  int lane_off;                // contiguous: byte offset of the lane within a stage
+  int tt, chunk_off;
+
+  __device__ __forceinline__ void init(const CacheView& cache, int b_, int tok_end_, int wave, int lane) {
+    c = &cache;
+    b = b_;
+    tok_end = tok_end_;
+    tt = 8 * wave + (lane >> 3);
+    chunk_off = ((lane & 7) ^ swz(tt)) * 16;
+    base = static_cast<const unsigned char*>(cache.data);
+    if (LAYOUT == kContiguous) {
+      base += (int64_t)b * cache.seq_stride * 2;
+      rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(base), (short)0,
+                                               tok_end * (ROW * 2), kBufferWord3);
+      lane_off = tt * (ROW * 2) + chunk_off;
+    }
   }
-  const unsigned char* rowp = base + off * 2 + ((lane & 7) ^ swz(tt)) * 16;
-  unsigned char* dst = buf + wave * 1024;
+
+  // per-stage addressing (scalar block lookups for paged caches), then one
+  // chunk group per issue_cg call, so the 9 loads can be spread out
+  uint32_t voff;
+  const unsigned char* rowp;
+  __device__ __forceinline__ void prepare(int tok0) {
+    if (LAYOUT == kContiguous) {
+      voff = (uint32_t)lane_off + (uint32_t)tok0 * (uint32_t)(ROW * 2);
+      return;
+    }
+    int tok = tok0 + tt;
+    tok = tok < tok_end ? tok : tok_end - 1;   // rows past the segment repeat a valid row
+    int64_t off;   // elements
+    if (LAYOUT == kPaged) {
+      // the stage's tokens lie in at most two blocks: those of its first and last token
+      const int bs = c->block_size;
+      const int last = tok0 + T - 1 < tok_end - 1 ? tok0 + T - 1 : tok_end - 1;
+      const int blk0 = block_id_scalar(*c, b, tok0);
+      const int blk1 = block_id_scalar(*c, b, last);
+      const int r0 = tok0 % bs;
+      const int rel = r0 + (tok - tok0);
+      const bool in0 = rel < bs;
+      off = ((int64_t)(in0 ? blk0 : blk1) * bs + (in0 ? rel : rel - bs)) * ROW;
+    } else {
+      off = cache_row_offset(*c, b, tok);
+    }
+    rowp = base + off * 2 + chunk_off;
+  }
+  __device__ __forceinline__ void issue_cg(int cg, unsigned char* buf, int wave) {
+    unsigned char* dst = buf + wave * 1024 + cg * CG_BYTES;
+    if (LAYOUT == kContiguous)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, (int)voff, cg * 128, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(rowp + cg * 128, (lds_void*)dst, 16, 0, 0);
+  }
+  __device__ __forceinline__ void issue(int tok0, unsigned char* buf, int wave) {
+    prepare(tok0);
 #pragma unroll
-  for (int cg = 0; cg < CGROUPS; ++cg)
-    __builtin_amdgcn_global_load_lds(rowp + cg * 128, (lds_void*)(dst + cg * CG_BYTES), 16, 0, 0);
-}
+    for (int cg = 0; cg < CGROUPS; ++cg) issue_cg(cg, buf, wave);
+  }
+};
 
 // Workgroup barrier that waits only for this wave's LDS operations (a
 // __syncthreads() would also wait for every outstanding global load and so
@@ -175,6 +234,7 @@ static_assert(LOADS_PER_STAGE == 9 && NSTAGE == 4, "wait counts assume 9 loads p
 // reference by more than REF_HEADROOM (log2 units; weights stay below
 // 2^REF_HEADROOM, far from fp32/bf16 overflow), the segment is computed again
 // with the row's true maximum as the reference.
+template <int LAYOUT>
 __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ DecodeSmem smem;
   DecodeSmem* sm = &smem;
@@ -215,9 +275,11 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
       const int qpos = a.positions[(int64_t)b * a.n_q + jq];
       limit = qpos + 1 < t1 ? qpos + 1 : t1;
     }
-    // the query operands must not be waited for inside the stage loop, where the
-    // vector-memory counter also covers the stage loads
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    // The query loads are not waited for here: the first stages' loads are
+    // issued behind them, and the wait for stage 0 (vector-memory counter,
+    // completed in order) covers them too.
+    StageLoader<LAYOUT> ld;
+    ld.init(a.cache, b, t1, wave, lane);
     // per-lane LDS byte offsets that do not depend on the stage
     const int sw_qk = swz(l32 & 7);
     int qk_off[4];
@@ -267,15 +329,20 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
       bool over = false;
 #pragma unroll
       for (int s = 0; s < NSTAGE - 1; ++s)
-        if (s < nst) load_stage(a, b, t0 + s * T, t1, sm->stage[s], wave, lane);
+        if (s < nst) ld.issue(t0 + s * T, sm->stage[s], wave);
 
-      // Software pipeline: iteration it computes S^T of stage it+1 (MFMA) while
-      // it turns the scores of stage it into weights (VALU), then accumulates
-      // PV of stage it.  Stage it+3 is loaded into the slot stage it-1 freed.
-      // s_cur: scores of the stage whose weights come next (two MFMA chains summed).
-      f32x16 s_cur = f32x16{};
-      // S^T of one stage into s_cur (no overlap; pipeline fill and edges)
-      auto qk_plain = [&](const unsigned char* sb) {
+      // Pipeline, iteration it: publish the weights of stage it (computed in
+      // the previous iteration), S^T of stage it+1 (MFMA only), then PV of
+      // stage it with the softmax of stage it+1 spread between its MFMAs, one
+      // small piece after each (the VALU work then runs while the matrix core
+      // is busy).  Stage it+3 is loaded into the slot stage it-1 freed.
+      f32x16 s_nx = f32x16{};            // scores of the stage whose weights come next
+      bf16x8 pb[2] = {bf16x8{}, bf16x8{}};   // weights of the stage about to be published
+      // S^T of one stage into s_nx: two MFMA accumulation chains over alternate k-steps
+      // With LOADS, the 9 loads of a later stage (prepared in ld) are issued
+      // one per 4 k-steps, so their issue overlaps the MFMAs.
+      auto qk = [&](const unsigned char* sb, auto loads_tag, unsigned char* ldst) {
+        constexpr bool LOADS = decltype(loads_tag)::value;
         f32x16 c0 = f32x16{}, c1 = f32x16{};
         bf16x8 kring[PF];
 #pragma unroll
@@ -286,89 +353,64 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
           if (ks + PF < KSTEPS) kring[ks % PF] = rd_k(sb, ks + PF);
           if (ks & 1) c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qreg[ks], c1, 0, 0, 0);
           else c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qreg[ks], c0, 0, 0, 0);
+          if (LOADS && (ks & 3) == 1) ld.issue_cg(ks >> 2, ldst, wave);
           __builtin_amdgcn_sched_barrier(0);
         }
-        s_cur = c0 + c1;
+        s_nx = c0 + c1;
       };
-      // softmax pieces on s_cur for stage tokens tok0..: scale + mask, row max, weights
-      auto sm_scale_mask = [&](int tok0, float* x, float& mt) {
+      using NoLoads = std::integral_constant<bool, false>;
+      using WithLoads = std::integral_constant<bool, true>;
+      // Softmax of the raw scores in s_nx in 30 small pieces (a few VALU ops
+      // each), so that one piece fits in the shadow of one PV MFMA: 0-7 mask
+      // scores of tokens at or past the row's limit (lim = limit minus the
+      // lane's base token; INT_MIN masks all, and leaves the weights zero);
+      // 8-11 lane maximum over the raw scores; 12 row maximum (the two lanes
+      // holding a row exchange theirs); 13 reference update; 14-29 one weight
+      // exp2(s * scale - m_ref) each, into pb.
+      constexpr int PIECES = 30;
+      float mt = -INFINITY, psum = 0.f, neg_m = 0.f;
+      auto sm_piece = [&](int k, int lim) {
+        if (k < 8) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int tok = tok0 + 8 * (i >> 2) + 4 * h + (i & 3);
-          const float v = s_cur[i] * a.scale_log2;
-          x[i] = tok < limit ? v : -INFINITY;
-          mt = fmaxf(mt, x[i]);
+          for (int e = 2 * k; e < 2 * k + 2; ++e) {
+            const int rel = 8 * (e >> 2) + (e & 3);      // token of s_nx[e] minus the lane's base token
+            s_nx[e] = rel < lim ? s_nx[e] : -INFINITY;
+          }
+        } else if (k < 12) {
+          const int j = k - 8;
+          mt = fmaxf(mt, fmaxf(fmaxf(s_nx[4 * j], s_nx[4 * j + 1]), fmaxf(s_nx[4 * j + 2], s_nx[4 * j + 3])));
+        } else if (k == 12) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+          mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.scale_log2;
+        } else if (k == 13) {
+          m_max = fmaxf(m_max, mt);
+          if (m_ref == -INFINITY) m_ref = mt;       // first visible stage of the row
+          over |= mt > m_ref + REF_HEADROOM;
+          neg_m = m_ref == -INFINITY ? 0.f : -m_ref;
+        } else if (k < PIECES) {
+          const int e = k - 14;
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s_nx[e], a.scale_log2, neg_m));
+          psum += pv;
+          pb[e >> 3][e & 7] = (__bf16)pv;
         }
       };
-      auto sm_rowmax = [&](float& mt, bool& ov) {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
-        mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        m_max = fmaxf(m_max, mt);
-        if (m_ref == -INFINITY) m_ref = mt;       // first visible stage of the row
-        ov |= mt > m_ref + REF_HEADROOM;
-      };
-      auto sm_weights = [&](const float* x, int q, bf16x8* pb, float& psum) {
-        const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(x[8 * q + e] - m_use);
-          psum += p;
-          pb[q][e] = (__bf16)p;
-        }
-      };
+      // base token of this lane's scores within a stage: 8*(i/4) + 4*h + i%4 for score i
+      auto lane_lim = [&](int tok0) { return limit - tok0 - 4 * h; };
 
+      // ---- prologue: scores and weights of stage 0
       wait_stages_in_flight(nst - 1 < NSTAGE - 2 ? nst - 1 : NSTAGE - 2);
       lds_barrier();
-      if (active && t0 < limit) qk_plain(sm->stage[0]);
-
-      for (int it = 0; it < nst; ++it) {
-        const bool has_next = it + 1 < nst;
-        if (has_next) wait_stages_in_flight(it + 2 < nst ? 1 : 0);   // stage it+1 resident
-        lds_barrier();
-        if (it + NSTAGE - 1 < nst)
-          load_stage(a, b, t0 + (it + NSTAGE - 1) * T, t1, sm->stage[(it + NSTAGE - 1) % NSTAGE], wave, lane);
-        const int tok0 = t0 + it * T;
-        const bool qk_now = active && tok0 < limit;                     // weights of stage it
-        const bool qk_next = active && has_next && tok0 + T < limit;    // scores of stage it+1
-        const unsigned char* sb_next = sm->stage[(it + 1) % NSTAGE];
-        bf16x8 pb[2] = {bf16x8{}, bf16x8{}};
-        float x[16];
-        float psum = 0.f, mt = -INFINITY;
-        if (qk_now && qk_next) {
-          // ------------ S^T(it+1) by MFMA, interleaved with the softmax of stage it
-          f32x16 c0 = f32x16{}, c1 = f32x16{};
-          bf16x8 kring[PF];
+      if (active && t0 < limit) {
+        qk(sm->stage[0], NoLoads{}, nullptr);
+        const int lim = lane_lim(t0);
 #pragma unroll
-          for (int ks = 0; ks < PF; ++ks) kring[ks] = rd_k(sb_next, ks);
-#pragma unroll
-          for (int ks = 0; ks < KSTEPS; ++ks) {
-            const bf16x8 kk = kring[ks % PF];
-            if (ks + PF < KSTEPS) kring[ks % PF] = rd_k(sb_next, ks + PF);
-            if (ks & 1) c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qreg[ks], c1, 0, 0, 0);
-            else c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qreg[ks], c0, 0, 0, 0);
-            if (ks == 1) sm_scale_mask(tok0, x, mt);
-            if (ks == 4) sm_rowmax(mt, over);
-            if (ks == 7) sm_weights(x, 0, pb, psum);
-            if (ks == 10) sm_weights(x, 1, pb, psum);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-          s_cur = c0 + c1;
-        } else {
-          if (qk_now) {
-            sm_scale_mask(tok0, x, mt);
-            sm_rowmax(mt, over);
-            sm_weights(x, 0, pb, psum);
-            sm_weights(x, 1, pb, psum);
-          }
-          if (qk_next) qk_plain(sb_next);
-        }
+        for (int k = 0; k < PIECES; ++k) sm_piece(k, lim);
         l_run += psum;
-        // ------------ publish this wave's weights (B-operand layout, per k-step)
-        sm->pbuf[wave][0][lane] = pb[0];
-        sm->pbuf[wave][1][lane] = pb[1];
-        lds_barrier();
-        // ------------ O^T[own 128 latents][128 rows] += V^T . P^T for stage it
-        const unsigned char* sb = sm->stage[it % NSTAGE];
+      }
+
+      // O^T[own 128 latents][128 rows] += V^T . P^T for one stage, with the
+      // softmax pieces of the next stage after the MFMAs
+      auto pv_stage = [&](const unsigned char* sb, int lim) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           bf16x8 pq[4];
@@ -380,10 +422,44 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
             const bf16x8 cur = va;
             if (mb + 1 < 4) va = rd_v(sb, q, mb + 1);
 #pragma unroll
-            for (int hb = 0; hb < 4; ++hb) pv_mfma(o[mb][hb], cur, pq[hb]);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int hb = 0; hb < 4; ++hb) {
+              pv_mfma(o[mb][hb], cur, pq[hb]);
+              sm_piece(16 * q + 4 * mb + hb, lim);
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
         }
+      };
+
+      for (int it = 0; it < nst; ++it) {
+        const bool has_next = it + 1 < nst;
+        if (has_next) wait_stages_in_flight(it + 2 < nst ? 1 : 0);   // stage it+1 resident
+        lds_barrier();   // every wave is done with the weights of stage it-1
+        // ------------ publish the weights of stage it (B-operand layout, per k-step)
+        sm->pbuf[wave][0][lane] = pb[0];
+        sm->pbuf[wave][1][lane] = pb[1];
+        pb[0] = bf16x8{};
+        pb[1] = bf16x8{};
+        // stage it+3 goes into the slot stage it-1 freed; its loads ride along
+        // with the MFMAs of S^T(it+1) when there are any
+        const bool do_load = it + NSTAGE - 1 < nst;
+        unsigned char* ldst = sm->stage[(it + NSTAGE - 1) % NSTAGE];
+        if (do_load) ld.prepare(t0 + (it + NSTAGE - 1) * T);
+        const int tok_nx = t0 + (it + 1) * T;
+        const bool qk_next = active && has_next && tok_nx < limit;    // scores of stage it+1
+        if (qk_next) {
+          if (do_load) qk(sm->stage[(it + 1) % NSTAGE], WithLoads{}, ldst);
+          else qk(sm->stage[(it + 1) % NSTAGE], NoLoads{}, nullptr);
+        } else if (do_load) {
+#pragma unroll
+          for (int cg = 0; cg < CGROUPS; ++cg) ld.issue_cg(cg, ldst, wave);
+        }
+        lds_barrier();   // weights of stage it visible to all waves
+        const unsigned char* sb = sm->stage[it % NSTAGE];
+        mt = -INFINITY;
+        psum = 0.f;
+        pv_stage(sb, qk_next ? lane_lim(tok_nx) : INT_MIN);
+        l_run += psum;
       }
       // ------------ did any row of the workgroup outgrow its reference?
       const bool wover = __builtin_amdgcn_ballot_w64(over) != 0;
@@ -420,7 +496,8 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
                 f32x4{o[mb][hb][4 * i4], o[mb][hb][4 * i4 + 1], o[mb][hb][4 * i4 + 2], o[mb][hb][4 * i4 + 3]};
       }
     }
-    __syncthreads();   // all waves done with the ring and the exchange buffers
+    // (the segment walker's barrier after this call keeps the ring and the
+    // exchange buffers until every wave is done with them)
   });
 }
 
@@ -445,7 +522,13 @@ hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
   a.n_work_pad = (p.num_splits + 7) / 8 * 8;
   a.scale_log2 = p.sm_scale * kLog2e;
   const int grid = a.n_work_pad * a.n_groups;
-  hipLaunchKernelGGL(decode_mfma_kernel, dim3(grid), dim3(NT), 0, stream, a);
+  // buffer offsets are 32-bit: a sequence plus one stage of overrun must fit
+  if (p.cache.block_size == 0 && (p.cache.seq_stride + (int64_t)T * ROW) * 2 <= (int64_t)0xFFFFFFFF)
+    hipLaunchKernelGGL(decode_mfma_kernel<kContiguous>, dim3(grid), dim3(NT), 0, stream, a);
+  else if (p.cache.block_size >= T)
+    hipLaunchKernelGGL(decode_mfma_kernel<kPaged>, dim3(grid), dim3(NT), 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_mfma_kernel<kAnyLayout>, dim3(grid), dim3(NT), 0, stream, a);
   return hipGetLastError();
 }
 

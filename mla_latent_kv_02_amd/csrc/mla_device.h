@@ -142,15 +142,22 @@ __device__ void for_each_segment(const int32_t* __restrict__ ctx_lens, int B, in
     sc->slot[tid] = (int32_t)(sb + (w - p / q));
     if (hit) { atomicMin(&sc->first, tid); atomicMax(&sc->last, tid); }
     __syncthreads();
-    const int first = sc->first, last = sc->last;
+    // the segment values are the same in every lane: keep them in scalar
+    // registers so that everything derived from them stays scalar too
+    const int first = __builtin_amdgcn_readfirstlane(sc->first);
+    const int last = __builtin_amdgcn_readfirstlane(sc->last);
     for (int k = first; k <= last; ++k) {
       const int64_t pk = sc->prefix[k];
       const int64_t lo = a > pk ? a : pk;
       const int64_t hi = e < pk + sc->len[k] ? e : pk + sc->len[k];
-      const int slot = sc->slot[k];
-      __syncthreads();
-      f(c0 + k, (int)(lo - pk), (int)(hi - pk), slot);
-      __syncthreads();
+      const int t0 = __builtin_amdgcn_readfirstlane((int)(lo - pk));
+      const int t1 = __builtin_amdgcn_readfirstlane((int)(hi - pk));
+      const int slot = __builtin_amdgcn_readfirstlane(sc->slot[k]);
+      // LDS-only barrier: the plan scratch is read; global stores of the
+      // previous segment may still be in flight
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      f(c0 + k, t0, t1, slot);
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
     run += tot_len;
     slot_run += tot_np;
