@@ -32,8 +32,9 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=40,
+                    help="untimed steps first; the clock settles within ~10 ms of load")
     ap.add_argument("--workload", default="v3_b64")
     ap.add_argument("--num-splits", type=int, default=0, help="0 = library default for the batch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -221,19 +222,36 @@ def main():
     for _ in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # (1) the step itself: K steps back to back, no event inside the steps
     log(f"timing {args.steps} steps")
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
-    for k in range(args.steps):
-        run_step(evs[k])
+    for _ in range(args.steps):
+        run_step()
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_step = start.elapsed_time(end) / args.steps
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    # (2) the dominant kernel: the same K steps again, with HIP events recorded on
+    # the launch stream right before and after mla_decode in every 5th step.  An
+    # event pair adds a few microseconds of idle time to its step; on every step
+    # that idle time would let the clock rise and flatter the kernel, so only a
+    # sample of the steps carries one.
+    every = 5
+    evs = {}
+    for k in range(args.steps):
+        ev = None
+        if k % every == every - 1:
+            ev = evs[k] = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        run_step(ev)
+    torch.cuda.synchronize()
+    if not evs:   # fewer steps than the sampling period: time the last one
+        ev = evs[0] = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        run_step(ev)
+        torch.cuda.synchronize()
+    dec_ms = [a.elapsed_time(b) for a, b in evs.values()]
     dec_avg = sum(dec_ms) / len(dec_ms)
     log(f"step {ms_step * 1e3:.1f} us (wall {wall / args.steps * 1e6:.1f} us); decode kernel avg "
         f"{dec_avg * 1e3:.1f} us (min {min(dec_ms) * 1e3:.1f})")
@@ -257,6 +275,7 @@ def main():
         "roofline": {"kernel": "mla_decode (decode_mfma_kernel)", "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(w.name), "bytes_per_launch": nbytes["decode"], "avg_launch_us": round(dec_avg * 1e3, 3),
+                     "launches_timed": len(dec_ms),
                      "mfma_tflops": round(flops / (dec_avg * 1e-3) / 1e12, 2),
                      "mfma_frac": round(flops / (dec_avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4)},
         "cpu_baseline": None,
