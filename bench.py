@@ -5,7 +5,8 @@
 A step is the whole hot path over one batch: append the step's own latents to
 the cache, absorb the query through W_UK (+ query RoPE), decode attention over
 the latent cache split into token-balanced work units, log-sum-exp combine of
-the partials, and the W_UV up-projection.  Inputs are seeded synthetic
+the partials, and the W_UV up-projection (the last two as one pass over the
+partials, mla_combine_out_proj, unless --separate-tail).  Inputs are seeded synthetic
 DeepSeek-V3-shaped tensors already resident in HBM when timing starts.
 
 Prints one JSON line: algorithmic GB/s of the step (value), decode tokens/s,
@@ -38,6 +39,8 @@ def parse():
     ap.add_argument("--workload", default="v3_b64")
     ap.add_argument("--num-splits", type=int, default=0, help="0 = library default for the batch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-tail", action="store_true",
+                    help="mla_combine then mla_out_proj instead of mla_combine_out_proj")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain fp32 copy kernel (dst = -src) over this many MiB, 5 times: the "
                          "calibration run for the HBM byte counters")
@@ -205,6 +208,8 @@ def main():
 
     stream = torch.cuda.current_stream()
     d = st["dims"]
+    # combine + up-projection as one pass over the partials where it is compiled
+    fused_tail = w.dtype == "bf16" and w.d_c == 512 and w.d_v == 128 and not args.separate_tail
 
     def run_step(ev=None):
         mla.mla_cache_append(d, st["cache"], *new_tokens)
@@ -215,8 +220,12 @@ def main():
                        step.lse_part)
         if ev is not None:
             ev[1].record(stream)
-        mla.mla_combine(d, st["cache"].ctx_lens, num_splits, step.u_part, step.lse_part, step.u, step.lse)
-        mla.mla_out_proj(d, step.u, st["w_uv"], step.out)
+        if fused_tail:
+            mla.mla_combine_out_proj(d, st["cache"].ctx_lens, num_splits, step.u_part, step.lse_part, st["w_uv"],
+                                     step.out, step.lse)
+        else:
+            mla.mla_combine(d, st["cache"].ctx_lens, num_splits, step.u_part, step.lse_part, step.u, step.lse)
+            mla.mla_out_proj(d, step.u, st["w_uv"], step.out)
 
     log(f"num_splits={num_splits}; warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -266,7 +275,7 @@ def main():
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic (seeded Philox N(0,1) latents/queries, "
         "N(0,1/d_c) weights)",
-        "config": {"workload": w.name, "description": w.description, "batch": w.batch, "n_q": w.n_q,
+        "config": {"workload": w.name, "description": w.description, "fused_tail": fused_tail, "batch": w.batch, "n_q": w.n_q,
                    "n_h": w.n_h, "d_c": w.d_c, "d_rope": w.d_rope, "d_nope": w.d_nope, "d_v": w.d_v,
                    "context_tokens": int(ctx.sum()), "block_size": w.block_size, "num_splits": num_splits},
         "tokens_per_s": round(w.batch * w.n_q / (ms_step * 1e-3), 1),

@@ -144,6 +144,18 @@ mla_status_t mla_combine(const mla_dims_t *dims, int32_t B, int32_t n_q, const i
 mla_status_t mla_out_proj(const mla_dims_t *dims, int32_t B, int32_t n_q, const float *u,
                           mla_dtype_t w_dt, const void *w_uv, float *out, void *stream);
 
+/* The merge of mla_combine followed by the value up-projection of
+ * mla_out_proj, in one pass over the partials ([Huny] §3.2, [Ikmyung] §1.4):
+ *   out[b][j][i][:] = (sum_k exp(r_k - L) u_part_k) W_i^UV,   lse[b][j][i] = L,
+ * L = log sum_k exp(lse_k) over the partials k of (b, j, i).  The merged u is
+ * not stored.  Arguments as for mla_combine and mla_out_proj; lse may be
+ * NULL.  Compiled for bf16 weights with d_c = 512 and d_v = 128; other shapes
+ * return MLA_ERR_UNSUPPORTED (use mla_combine, then mla_out_proj). */
+mla_status_t mla_combine_out_proj(const mla_dims_t *dims, int32_t B, int32_t n_q, const int32_t *ctx_lens,
+                                  int32_t num_splits, const float *u_part, const float *lse_part,
+                                  mla_dtype_t w_dt, const void *w_uv, float *out, float *lse,
+                                  void *stream);
+
 /* Write n new tokens into the cache: token k belongs to sequence seq_ids[k]
  * at position positions[k]; its row becomes [c_kv_new[k] | RoPE(k_rope_new[k],
  * positions[k])] ([Huny] §2.2: the positional key is cached rotated).  Inputs

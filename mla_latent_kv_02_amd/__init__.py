@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     mla_decode,
     mla_num_partials,
     mla_out_proj,
+    mla_combine_out_proj,
 )
 
 __version__ = "0.1.0"

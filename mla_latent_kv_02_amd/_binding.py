@@ -17,8 +17,8 @@ LIB_PATH = os.path.join(HERE, "libmla.so")
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP = 0, 1, 2, 3
 F32, BF16 = 0, 1
 
-EXPORTED = ("mla_absorb_q", "mla_decode", "mla_combine", "mla_out_proj", "mla_cache_append",
-            "mla_num_partials", "mla_status_string", "mla_version")
+EXPORTED = ("mla_absorb_q", "mla_decode", "mla_combine", "mla_out_proj", "mla_combine_out_proj",
+            "mla_cache_append", "mla_num_partials", "mla_status_string", "mla_version")
 
 
 class MlaError(RuntimeError):
@@ -58,6 +58,7 @@ def load_library(path: str = LIB_PATH):
         "mla_decode": [DP, I32, I32, P, P, CP, P, I32, P, P, V],
         "mla_combine": [DP, I32, I32, P, I32, P, P, P, P, V],
         "mla_out_proj": [DP, I32, I32, P, ctypes.c_int, P, P, V],
+        "mla_combine_out_proj": [DP, I32, I32, P, I32, P, P, ctypes.c_int, P, P, P, V],
         "mla_cache_append": [DP, CP, I32, P, P, P, I64, P, I64, V],
     }
     for name, args in sig.items():
@@ -233,6 +234,29 @@ def mla_out_proj(dims: Dims, u, w_uv, out, stream=None) -> None:
     d = dims._c()
     _check("mla_out_proj", load_library().mla_out_proj(
         ctypes.byref(d), B, n_q, u.data_ptr(), _dtype(w_uv), w_uv.data_ptr(), out.data_ptr(), _stream(stream)))
+
+
+def mla_combine_out_proj(dims: Dims, ctx_lens, num_splits: int, u_part, lse_part, w_uv, out, lse=None,
+                         stream=None) -> None:
+    torch = _torch()
+    B, n_q = out.shape[0], out.shape[1]
+    _dev(ctx_lens, "ctx_lens", torch.int32)
+    for t, n in ((u_part, "u_part"), (lse_part, "lse_part"), (out, "out")):
+        _dev(t, n, torch.float32)
+    _dev(w_uv, "w_uv")
+    slots = mla_num_partials(B, num_splits)
+    _shape(ctx_lens, "ctx_lens", (B,))
+    _shape(u_part, "u_part", (slots, n_q, dims.n_h, dims.d_c))
+    _shape(lse_part, "lse_part", (slots, n_q, dims.n_h, 2))
+    _shape(w_uv, "w_uv", (dims.n_h, dims.d_c, dims.d_v))
+    _shape(out, "out", (B, n_q, dims.n_h, dims.d_v))
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+        _shape(lse, "lse", (B, n_q, dims.n_h))
+    d = dims._c()
+    _check("mla_combine_out_proj", load_library().mla_combine_out_proj(
+        ctypes.byref(d), B, n_q, ctx_lens.data_ptr(), num_splits, u_part.data_ptr(), lse_part.data_ptr(),
+        _dtype(w_uv), w_uv.data_ptr(), out.data_ptr(), None if lse is None else lse.data_ptr(), _stream(stream)))
 
 
 def mla_cache_append(dims: Dims, cache: LatentCache, seq_ids, positions, c_kv_new, k_rope_new,

@@ -246,11 +246,17 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
   const int g4 = lane >> 4;         // lane group of 16 (transposed reads)
   const int l16 = lane & 15;
 
-  // block -> (work unit, row group); the groups of one unit sit 8 blocks apart
-  // so that they land on the same XCD and share its L2.
+  // block -> (work unit, row group).  Workgroups are dealt to the 8 XCDs in
+  // turn (block b runs on XCD b % 8), so XCD x gets blocks x, x+8, ...; they
+  // take the consecutive work units x*U .. x*U+U-1 (U = units per XCD), all
+  // row groups of a unit together.  The units of one sequence then share an
+  // L2: its query rows are fetched from memory once per XCD, and the row
+  // groups of a unit read the same cache tiles.
   const int bid = blockIdx.x;
-  const int w = (bid / (8 * a.n_groups)) * 8 + (bid & 7);
-  const int g = (bid >> 3) % a.n_groups;
+  const int units_per_xcd = a.n_work_pad / 8;
+  const int j = bid >> 3;
+  const int w = (bid & 7) * units_per_xcd + j / a.n_groups;
+  const int g = j % a.n_groups;
   if (w >= a.num_splits) return;
 
   const int rows = a.n_q * a.n_h;

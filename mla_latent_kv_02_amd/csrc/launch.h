@@ -64,6 +64,21 @@ hipError_t launch_out_proj(const OutProjParams& p, hipStream_t stream);
 bool out_proj_mfma_ok(const OutProjParams& p);
 hipError_t launch_out_proj_mfma(const OutProjParams& p, hipStream_t stream);
 
+// Value up-projection o = u W_i^UV, u either given or merged on the fly from
+// the split-KV partials (the merge of mla_combine; u is then never stored).
+struct TailParams {
+  const float* u;              // [M][n_h][d_c] (no partials)
+  const int32_t* ctx_lens;     // partials: plan of mla_decode
+  const float* u_part;
+  const float* lse_part;
+  const void* w_uv;            // bf16 [n_h][d_c][d_v]
+  float* out;                  // [M][n_h][d_v]
+  float* lse;                  // [M][n_h] or null (partials only)
+  int B, n_q, n_h, d_c, d_v, num_splits;
+};
+bool tail_mfma_ok(int d_c, int d_v, bool bf16_weights);
+hipError_t launch_tail_mfma(const TailParams& p, bool from_partials, hipStream_t stream);
+
 struct AppendParams {
   CacheView cache;
   void* cache_data;

@@ -126,8 +126,28 @@ mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t B, int32_t n_q, const 
   p.u = u; p.w_uv = w_uv; p.out = out;
   p.B = B; p.n_q = n_q; p.n_h = dims->n_h; p.d_c = dims->d_c; p.d_v = dims->d_v;
   p.bf16 = w_dt == MLA_BF16;
+  if (mla::tail_mfma_ok(p.d_c, p.d_v, p.bf16)) {
+    mla::TailParams t{};
+    t.u = u; t.w_uv = w_uv; t.out = out;
+    t.B = B; t.n_q = n_q; t.n_h = p.n_h; t.d_c = p.d_c; t.d_v = p.d_v;
+    return from_hip(mla::launch_tail_mfma(t, false, (hipStream_t)stream));
+  }
   if (mla::out_proj_mfma_ok(p)) return from_hip(mla::launch_out_proj_mfma(p, (hipStream_t)stream));
   return from_hip(mla::launch_out_proj(p, (hipStream_t)stream));
+}
+
+mla_status_t mla_combine_out_proj(const mla_dims_t* dims, int32_t B, int32_t n_q, const int32_t* ctx_lens,
+                                  int32_t num_splits, const float* u_part, const float* lse_part,
+                                  mla_dtype_t w_dt, const void* w_uv, float* out, float* lse, void* stream) {
+  if (!dims_ok(dims) || B < 0 || n_q < 1 || num_splits < 1 || num_splits > kMaxSplits || !dtype_ok(w_dt))
+    return MLA_ERR_INVALID_ARG;
+  if (B == 0) return MLA_OK;
+  if (!ctx_lens || !u_part || !lse_part || !w_uv || !out) return MLA_ERR_INVALID_ARG;
+  if (!mla::tail_mfma_ok(dims->d_c, dims->d_v, w_dt == MLA_BF16)) return MLA_ERR_UNSUPPORTED;
+  mla::TailParams p{};
+  p.ctx_lens = ctx_lens; p.u_part = u_part; p.lse_part = lse_part; p.w_uv = w_uv; p.out = out; p.lse = lse;
+  p.B = B; p.n_q = n_q; p.n_h = dims->n_h; p.d_c = dims->d_c; p.d_v = dims->d_v; p.num_splits = num_splits;
+  return from_hip(mla::launch_tail_mfma(p, true, (hipStream_t)stream));
 }
 
 mla_status_t mla_cache_append(const mla_dims_t* dims, const mla_cache_t* cache, int32_t n,

@@ -165,6 +165,33 @@ __device__ void for_each_segment(const int32_t* __restrict__ ctx_lens, int B, in
   }
 }
 
+// For the n (<= NT) sequences b_lo .. b_lo + n - 1: first partial slot and
+// number of partials, written to slot0[] and nparts[] (n entries each, LDS).
+// All NT threads of the workgroup must call this together.
+template <int NT>
+__device__ void plan_slot_range(const int32_t* __restrict__ ctx_lens, int B, int num_splits, int b_lo, int n,
+                                PlanScratch<NT>* sc, int* slot0, int* nparts) {
+  const int tid = threadIdx.x;
+  int64_t part = 0;
+  for (int k = tid; k < B; k += NT) part += ctx_lens[k];
+  int64_t total;
+  block_scan_incl<NT>(part, sc->scan, &total);
+  const int64_t q = plan_chunk(total, num_splits);
+  int64_t run = 0, slot_run = 0;
+  for (int c0 = 0; c0 < b_lo + n; c0 += NT) {
+    const int k = c0 + tid;
+    const int64_t len = k < B ? ctx_lens[k] : 0;
+    int64_t tot_len, tot_np;
+    const int64_t p = run + block_scan_incl<NT>(len, sc->scan, &tot_len) - len;
+    const int64_t np = plan_parts(p, len, q);
+    const int64_t sb = slot_run + block_scan_incl<NT>(np, sc->scan, &tot_np) - np;
+    if (k >= b_lo && k < b_lo + n) { slot0[k - b_lo] = (int32_t)sb; nparts[k - b_lo] = (int32_t)np; }
+    run += tot_len;
+    slot_run += tot_np;
+  }
+  __syncthreads();
+}
+
 // For sequence b: first partial slot and number of partials (0 if empty).
 template <int NT>
 __device__ void plan_lookup(const int32_t* __restrict__ ctx_lens, int B, int num_splits, int b,

@@ -2,14 +2,16 @@
 
     [cache_append of the new tokens] -> absorb_q -> decode -> combine -> out_proj
 
-``DecodeStep`` owns the intermediate buffers (q_lat, q_pe, the split-KV
-partials, u, lse) and the output, sized once for a batch shape, so that a
-step allocates nothing.  Every call goes through the C ABI.
+or, with ``fused_tail``, the last two as the single mla_combine_out_proj call
+(the merged u is then not stored).  ``DecodeStep`` owns the intermediate
+buffers (q_lat, q_pe, the split-KV partials, u, lse) and the output, sized once
+for a batch shape, so that a step allocates nothing.  Every call goes through
+the C ABI.
 """
 from __future__ import annotations
 
-from ._binding import (Dims, LatentCache, mla_absorb_q, mla_cache_append, mla_combine, mla_decode,
-                       mla_num_partials, mla_out_proj)
+from ._binding import (Dims, LatentCache, mla_absorb_q, mla_cache_append, mla_combine, mla_combine_out_proj,
+                       mla_decode, mla_num_partials, mla_out_proj)
 
 
 class DecodeStep:
@@ -26,7 +28,8 @@ class DecodeStep:
         self.lse = torch.empty((B, n_q, dims.n_h), dtype=f32, device=device)
         self.out = torch.empty((B, n_q, dims.n_h, dims.d_v), dtype=f32, device=device)
 
-    def run(self, q_nope, q_rope, positions, w_uk, w_uv, cache: LatentCache, new_tokens=None, stream=None):
+    def run(self, q_nope, q_rope, positions, w_uk, w_uv, cache: LatentCache, new_tokens=None, stream=None,
+            fused_tail: bool = False):
         """``new_tokens`` = (seq_ids, positions, c_kv_new, k_rope_new) appends the
         step's own latents to the cache first."""
         d = self.dims
@@ -35,7 +38,11 @@ class DecodeStep:
         mla_absorb_q(d, q_nope, q_rope, positions, w_uk, self.q_lat, self.q_pe, stream=stream)
         mla_decode(d, self.q_lat, self.q_pe, cache, positions, self.num_splits, self.u_part,
                    self.lse_part, stream=stream)
-        mla_combine(d, cache.ctx_lens, self.num_splits, self.u_part, self.lse_part, self.u, self.lse,
-                    stream=stream)
-        mla_out_proj(d, self.u, w_uv, self.out, stream=stream)
+        if fused_tail:
+            mla_combine_out_proj(d, cache.ctx_lens, self.num_splits, self.u_part, self.lse_part, w_uv, self.out,
+                                 self.lse, stream=stream)
+        else:
+            mla_combine(d, cache.ctx_lens, self.num_splits, self.u_part, self.lse_part, self.u, self.lse,
+                        stream=stream)
+            mla_out_proj(d, self.u, w_uv, self.out, stream=stream)
         return self.out

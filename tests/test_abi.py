@@ -118,6 +118,14 @@ def test_other_entry_points_reject_bad_arguments(lib):
     assert lib.mla_combine(d, 2, 1, FAKE, 4, FAKE, FAKE, None, FAKE, None) == bd.MLA_ERR_INVALID_ARG
     assert lib.mla_out_proj(d, 2, 1, FAKE, 3, FAKE, FAKE, None) == bd.MLA_ERR_INVALID_ARG
     assert lib.mla_out_proj(d, 2, 1, None, 1, FAKE, FAKE, None) == bd.MLA_ERR_INVALID_ARG
+    cop = lib.mla_combine_out_proj
+    assert cop(d, 2, 1, FAKE, 0, FAKE, FAKE, 1, FAKE, FAKE, None, None) == bd.MLA_ERR_INVALID_ARG
+    assert cop(d, 2, 1, FAKE, 4, FAKE, FAKE, 7, FAKE, FAKE, None, None) == bd.MLA_ERR_INVALID_ARG
+    assert cop(d, 2, 1, FAKE, 4, FAKE, FAKE, 1, None, FAKE, None, None) == bd.MLA_ERR_INVALID_ARG
+    assert cop(d, 2, 1, FAKE, 4, FAKE, FAKE, 1, FAKE, None, None, None) == bd.MLA_ERR_INVALID_ARG
+    # fp32 weights are not compiled for the fused pass: refused before any launch
+    assert cop(d, 2, 1, FAKE, 4, FAKE, FAKE, 0, FAKE, FAKE, None, None) == bd.MLA_ERR_UNSUPPORTED
+    assert cop(d, 0, 1, None, 4, None, None, 1, None, None, None, None) == 0
     c = _cache()
     cr = ctypes.byref(c)
     assert lib.mla_cache_append(d, cr, -1, FAKE, FAKE, FAKE, 512, FAKE, 64, None) == bd.MLA_ERR_INVALID_ARG

@@ -38,8 +38,17 @@ def _run(st, num_splits):
     step.run(st["q_nope"], st["q_rope"], st["positions"], st["w_uk"], st["w_uv"], st["cache"])
     torch.cuda.synchronize()
     f = lambda t: t.float().cpu().numpy().astype(np.float64)
-    return {"q_lat": f(step.q_lat), "q_pe": f(step.q_pe), "u": f(step.u), "lse": f(step.lse),
-            "o": f(step.out), "u_part": f(step.u_part), "lse_part": f(step.lse_part)}
+    got = {"q_lat": f(step.q_lat), "q_pe": f(step.q_pe), "u": f(step.u), "lse": f(step.lse),
+           "o": f(step.out), "u_part": f(step.u_part), "lse_part": f(step.lse_part)}
+    if w.dtype == "bf16" and w.d_c == 512 and w.d_v == 128:
+        # the same partials through the fused merge + up-projection
+        out2 = torch.full_like(step.out, float("nan"))
+        lse2 = torch.full_like(step.lse, float("nan"))
+        mla.mla_combine_out_proj(st["dims"], st["cache"].ctx_lens, num_splits, step.u_part, step.lse_part,
+                                 st["w_uv"], out2, lse2)
+        torch.cuda.synchronize()
+        got["o_fused"], got["lse_fused"] = f(out2), f(lse2)
+    return got
 
 
 def _oracle(w, st, b, heads=None):
@@ -64,6 +73,9 @@ def _check(w, st, got, seqs=None, heads=None):
             "o": vec_rel_err(got["o"][b][:, hsel], ref["o"]),
             "lse": scalar_err(got["lse"][b][:, hsel], ref["lse"]),
         }
+        if "o_fused" in got:
+            errs["o_fused"] = vec_rel_err(got["o_fused"][b][:, hsel], ref["o"])
+            errs["lse_fused"] = scalar_err(got["lse_fused"][b][:, hsel], ref["lse"])
         print(f"  seq {b} ctx {st['ctx_host'][b]}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()),
               flush=True)
         for k, v in errs.items():
@@ -199,6 +211,49 @@ def test_combine_alone_against_oracle():
         ref_u, ref_l = oracle.merge_partials(u_norm[base:base + n], lse[base:base + n])
         assert vec_rel_err(u[b].cpu().numpy(), ref_u) < 1e-5
         assert scalar_err(lse_out[b].cpu().numpy(), ref_l) < 1e-6
+        base += n
+    assert base <= slots
+
+
+@pytest.mark.parametrize("num_splits", [1, 7, 50])
+def test_combine_out_proj_against_oracle(num_splits):
+    """mla_combine_out_proj on partials in the documented format, 80 query rows
+    (three 32-row blocks, the last one ragged), one empty partial: against the
+    oracle's merge of the normalised partials followed by its W_UV product."""
+    _need_gpu()
+    import mla_latent_kv_02_amd as mla
+    rng = np.random.default_rng(31 + num_splits)
+    n_h, d_c, d_v, n_q = 16, 512, 128, 2
+    dims = mla.Dims(n_h, d_c, 64, 128, d_v)
+    ctx = rng.integers(1, 400, size=40).astype(np.int32)
+    ctx[3] = 1
+    B = len(ctx)
+    slots = mla.mla_num_partials(B, num_splits)
+    u_norm = rng.standard_normal((slots, n_q, n_h, d_c))
+    lse = rng.standard_normal((slots, n_q, n_h)) * 4
+    ref_shift = lse + rng.standard_normal((slots, n_q, n_h))      # references near lse
+    lse[0, 1, 5] = -np.inf
+    u_part = (u_norm * np.exp(lse - ref_shift)[..., None]).astype(np.float32)
+    u_part[0, 1, 5] = 0
+    rl = np.stack([ref_shift, lse], axis=-1).astype(np.float32)
+    rl[0, 1, 5] = (0.0, -np.inf)
+    wuv = W.round_to_bf16((rng.standard_normal((n_h, d_c, d_v)) / np.sqrt(d_c)).astype(np.float32))
+    out = torch.full((B, n_q, n_h, d_v), float("nan"), device="cuda")
+    lse_out = torch.full((B, n_q, n_h), float("nan"), device="cuda")
+    mla.mla_combine_out_proj(dims, torch.from_numpy(ctx).cuda(), num_splits, torch.from_numpy(u_part).cuda(),
+                             torch.from_numpy(rl).cuda(), torch.from_numpy(wuv).cuda().bfloat16(), out, lse_out)
+    torch.cuda.synchronize()
+    out, lse_out = out.cpu().numpy(), lse_out.cpu().numpy()
+    total = int(ctx.sum())
+    q = -(-total // num_splits)
+    prefix = np.concatenate([[0], np.cumsum(ctx)])
+    base = 0
+    for b in range(B):
+        n = (prefix[b] + ctx[b] - 1) // q - prefix[b] // q + 1
+        ref_u, ref_l = oracle.merge_partials(u_norm[base:base + n], lse[base:base + n])
+        ref_o = oracle.value_up_projection(ref_u, wuv)
+        assert vec_rel_err(out[b], ref_o) < 1e-4, b
+        assert scalar_err(lse_out[b], ref_l) < 1e-5, b
         base += n
     assert base <= slots
 
