@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--workload", default="v3_b64")
     ap.add_argument("--num-splits", type=int, default=0, help="0 = library default for the batch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the timed steps from a HIP graph captured once (eager launches are as fast "
+                         "or faster on these kernels, so they are the default)")
     ap.add_argument("--separate-tail", action="store_true",
                     help="mla_combine then mla_out_proj instead of mla_combine_out_proj")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -232,13 +235,26 @@ def main():
         run_step()
     torch.cuda.synchronize()
     # (1) the step itself: K steps back to back, no event inside the steps
-    log(f"timing {args.steps} steps")
+    # (optionally replayed from a HIP graph captured once)
+    graph = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run_step()
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+    log(f"timing {args.steps} steps" + (" (graph replays)" if graph is not None else ""))
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     start.record(stream)
     for _ in range(args.steps):
-        run_step()
+        if graph is not None:
+            graph.replay()
+        else:
+            run_step()
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
@@ -275,7 +291,8 @@ def main():
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic (seeded Philox N(0,1) latents/queries, "
         "N(0,1/d_c) weights)",
-        "config": {"workload": w.name, "description": w.description, "fused_tail": fused_tail, "batch": w.batch, "n_q": w.n_q,
+        "config": {"workload": w.name, "description": w.description, "fused_tail": fused_tail,
+                   "step_launch": "graph" if graph is not None else "eager", "batch": w.batch, "n_q": w.n_q,
                    "n_h": w.n_h, "d_c": w.d_c, "d_rope": w.d_rope, "d_nope": w.d_nope, "d_v": w.d_v,
                    "context_tokens": int(ctx.sum()), "block_size": w.block_size, "num_splits": num_splits},
         "tokens_per_s": round(w.batch * w.n_q / (ms_step * 1e-3), 1),

@@ -1,8 +1,8 @@
 // Latent-cache append: the row of a new token is [c_kv | RoPE(k_rope, pos)]
 // ([Huny] = "Multi-Head Latent Attention(MLA) 아키텍처 해부", Huny's Dev Blog,
 // §2.2: the positional key k^R_t = RoPE(h_t W_kR) is what is cached, shared
-// by all heads).  The rotation pairs adjacent elements and uses an fp64
-// angle, as on the query side.
+// by all heads).  The rotation pairs adjacent elements; the angle is formed
+// and reduced in fp64, as on the query side.
 
 #include "mla_device.h"
 #include "launch.h"
@@ -31,10 +31,16 @@ __global__ __launch_bounds__(NT) void cache_append_kernel(AppendParams p) {
     const int r = e - p.d_c;
     const T* src = static_cast<const T*>(p.k_rope) + (int64_t)k * p.k_rope_stride + r;
     const double theta = pow((double)p.rope_base, -(double)r / p.d_rope);   // r = 2k
-    double sd, cd;
-    sincos((double)pos * theta, &sd, &cd);
+    float c, s;
+    if (sizeof(T) == 2) {
+      sincos_turns(pos, theta * kInv2Pi, &s, &c);   // bf16 rows: fp32 sin/cos of the fp64-reduced angle
+    } else {
+      double sd, cd;
+      sincos((double)pos * theta, &sd, &cd);
+      c = (float)cd;
+      s = (float)sd;
+    }
     const float x0 = Elem<T>::load(src, 0), x1 = Elem<T>::load(src, 1);
-    const float c = (float)cd, s = (float)sd;
     Elem<T>::store(dst, e, x0 * c - x1 * s);
     Elem<T>::store(dst, e + 1, x0 * s + x1 * c);
   }

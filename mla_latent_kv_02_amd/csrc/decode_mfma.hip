@@ -21,12 +21,18 @@
 //
 // LDS stage layout ("chunk groups"): a stage holds T=32 tokens of 72 16-byte
 // chunks (576 bf16).  Chunk c of stage token t lives at 16-byte slot
-//     (c / 8) * 256 + t * 8 + ((c % 8) ^ s(t)),  s(t) = ((t & 3) << 1) | ((t >> 2) & 1).
+//     (c / 8) * 256 + t * 8 + ((c % 8) ^ s(t)),  s(t) = P[(t / 2) % 8],
+//     P = (0, 4, 1, 5, 2, 6, 3, 7).
 // A 1 KiB run of slots holds 8 tokens x 8 chunks, which is exactly what one
 // 16-byte-per-lane global->LDS load writes; 8 lanes read 128 contiguous bytes
 // of one token row (coalesced).  The xor keeps both LDS read patterns free of
-// bank conflicts: 8 consecutive tokens of one chunk (QK), and 4 consecutive
-// tokens of 2 neighbouring chunks (the transposed PV read).
+// bank conflicts on gfx950's 64 four-byte banks: a 16-byte read serves 16
+// lanes per cycle, here 16 consecutive tokens of one chunk (QK), whose two
+// parity classes (rows 128 B apart share a 256-byte bank period) each see all
+// 8 values of s; the transposed PV read serves 32 lanes, 4 consecutive tokens
+// of 4 chunks, and s(t), s(t+2) differ in bit 2 so the two tokens of a parity
+// class use disjoint aligned groups of 4 chunks.  (Measured: 0 bank conflicts
+// for both patterns.)
 //
 // Pipeline: a ring of NSTAGE stages in LDS; loads run NSTAGE - 1 stages ahead
 // of the stage being used, and each wave waits (vmcnt) only for the oldest
@@ -75,7 +81,8 @@ struct DecodeArgs {
   float scale_log2;        // sm_scale * log2(e)
 };
 
-__device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+// s(t) of the stage layout: P[(t >> 1) & 7] with P packed in nibbles
+__device__ __forceinline__ int swz(int t) { return (0x73625140 >> (4 * ((t >> 1) & 7))) & 7; }
 
 struct __attribute__((aligned(16))) DecodeSmem {
   unsigned char stage[NSTAGE][STAGE_BYTES];
@@ -287,13 +294,13 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
     StageLoader<LAYOUT> ld;
     ld.init(a.cache, b, t1, wave, lane);
     // per-lane LDS byte offsets that do not depend on the stage
-    const int sw_qk = swz(l32 & 7);
+    const int sw_qk = swz(l32);
     int qk_off[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) qk_off[r] = l32 * 128 + (((2 * r + h) ^ sw_qk) << 4);
     const int hq = g4 >> 1;                              // k half of this lane's transposed read
     const int tr_tok = 4 * hq + (l16 >> 2);              // token (mod 8) of this lane's row
-    const int sw_tr = swz(tr_tok);
+    const int sw_tr0 = swz(tr_tok), sw_tr1 = swz(8 + tr_tok);   // s(t) of t = 16q + 8ins + tr_tok
     const int half8 = (l16 & 1) * 8;
     const int cch = 2 * (g4 & 1) + ((l16 & 3) >> 1);     // chunk within a group of 4
     const int nst = (t1 - t0 + T - 1) / T;
@@ -318,13 +325,20 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int ins = 0; ins < 2; ++ins) {
         const int t = 16 * q + 8 * ins + tr_tok;
-        const unsigned char* p = sb + (mbg >> 1) * CG_BYTES + t * 128 + ((cq ^ sw_tr) << 4) + half8;
+        const unsigned char* p = sb + (mbg >> 1) * CG_BYTES + t * 128 + ((cq ^ (ins ? sw_tr1 : sw_tr0)) << 4) + half8;
         v[ins] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
             (lds_bf16x4*)((__attribute__((address_space(3))) unsigned char*)p));
       }
       return __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
     };
-    constexpr int PF = 2;
+#ifndef DECODE_QK_PF
+#define DECODE_QK_PF 2
+#endif
+#ifndef DECODE_QK_CHAINS
+#define DECODE_QK_CHAINS 2
+#endif
+    constexpr int PF = DECODE_QK_PF;          // K operands read ahead
+    constexpr int QKC = DECODE_QK_CHAINS;     // MFMA accumulation chains
 
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -349,7 +363,9 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
       // one per 4 k-steps, so their issue overlaps the MFMAs.
       auto qk = [&](const unsigned char* sb, auto loads_tag, unsigned char* ldst) {
         constexpr bool LOADS = decltype(loads_tag)::value;
-        f32x16 c0 = f32x16{}, c1 = f32x16{};
+        f32x16 cc[QKC];
+#pragma unroll
+        for (int c = 0; c < QKC; ++c) cc[c] = f32x16{};
         bf16x8 kring[PF];
 #pragma unroll
         for (int ks = 0; ks < PF; ++ks) kring[ks] = rd_k(sb, ks);
@@ -357,12 +373,13 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
         for (int ks = 0; ks < KSTEPS; ++ks) {
           const bf16x8 kk = kring[ks % PF];
           if (ks + PF < KSTEPS) kring[ks % PF] = rd_k(sb, ks + PF);
-          if (ks & 1) c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qreg[ks], c1, 0, 0, 0);
-          else c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qreg[ks], c0, 0, 0, 0);
+          cc[ks % QKC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qreg[ks], cc[ks % QKC], 0, 0, 0);
           if (LOADS && (ks & 3) == 1) ld.issue_cg(ks >> 2, ldst, wave);
           __builtin_amdgcn_sched_barrier(0);
         }
-        s_nx = c0 + c1;
+        s_nx = cc[0];
+#pragma unroll
+        for (int c = 1; c < QKC; ++c) s_nx += cc[c];
       };
       using NoLoads = std::integral_constant<bool, false>;
       using WithLoads = std::integral_constant<bool, true>;

@@ -40,6 +40,20 @@ template <> struct Elem<uint16_t> {
   __device__ __forceinline__ static void store(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
 };
 
+// ------------------------------------------------------------------- RoPE
+// sin and cos of the angle pos * theta, given turns = theta / (2 pi): the angle
+// in turns and its reduction to [-1/2, 1/2] are fp64; the sine and cosine of
+// the reduced angle use the fp32 hardware instructions, which take turns.
+// Accurate to ~1e-6 absolute, far below the bf16 resolution of the outputs
+// that use it.
+__device__ __forceinline__ void sincos_turns(int pos, double turns, float* s, float* c) {
+  const double v = (double)pos * turns;
+  const float f = (float)(v - rint(v));
+  *s = __builtin_amdgcn_sinf(f);
+  *c = __builtin_amdgcn_cosf(f);
+}
+constexpr double kInv2Pi = 0.15915494309189535;
+
 // --------------------------------------------------------- cache addressing
 struct CacheView {
   const void* data;

@@ -94,6 +94,128 @@ __global__ __launch_bounds__(256) void rope_q_rows_kernel(AbsorbParams p) {
   }
 }
 
+// ------------------------------------------- absorption + query RoPE, one pass
+// grid: n_h * (d_c / 256) workgroups; workgroup (head i, slice h2) computes
+// q_lat[:, i, 256 h2 .. +256] and the query RoPE of head i for the rows m with
+// m % (d_c / 256) == h2.  Wave w owns latents c0 = 256 h2 + 64 w .. +64 (four
+// 16-latent MFMA tiles, W_UK rows as the A operand held in registers) and walks
+// the query rows 64 at a time (four 16-row tiles, the B operand).  Every load
+// of a 64-row block is issued before any MFMA; the RoPE of the workgroup's rows
+// runs while the first block is in flight.  C tile (latent tile t, row tile
+// mt): lane l holds latents 16t + 4(l/16) + 0..3 of row 16mt + l%16, stored as
+// 8 bytes (a wave writes 128 contiguous bytes of each row).
+// Requires d_nope == 128, d_c % 256 == 0, bf16.
+constexpr int AR_LAT = 256;           // latents per workgroup
+constexpr int AR_ROPE = 8;            // RoPE items per thread whose loads go first
+__global__ __launch_bounds__(256) void absorb_rope_kernel(AbsorbParams p) {
+  __shared__ double theta[64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nslices = p.d_c / AR_LAT;
+  const int i = blockIdx.x / nslices, h2 = blockIdx.x % nslices;
+  const int c0 = h2 * AR_LAT + wave * 64;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int M = p.B * p.n_q;
+  const int half = p.d_rope / 2;
+  // turns per position of plane k: base^(-2k/d_rope) / (2 pi)
+  if (threadIdx.x < half) theta[threadIdx.x] = pow((double)p.rope_base, -2.0 * threadIdx.x / p.d_rope) * kInv2Pi;
+  __syncthreads();
+  // ---- query RoPE of head i, rows m = h2, h2 + nslices, ...: the loads of
+  // the first AR_ROPE items of this thread are issued before the GEMM loads,
+  // so the rotation only waits for them
+  const uint16_t* rsrc = static_cast<const uint16_t*>(p.q_rope);
+  uint16_t* rdst = static_cast<uint16_t*>(p.q_pe);
+  const int rrows = (M - h2 + nslices - 1) / nslices;
+  const int ritems = rrows * half;
+  auto rope_off = [&](int idx, int& m, int& k) -> int64_t {
+    m = h2 + nslices * (idx / half);
+    k = idx % half;
+    return ((int64_t)m * p.n_h + i) * p.d_rope + 2 * k;
+  };
+  uint32_t rx[AR_ROPE];
+  int rpos[AR_ROPE];
+#pragma unroll
+  for (int e = 0; e < AR_ROPE; ++e) {
+    const int idx = threadIdx.x + 256 * e;
+    rx[e] = 0;
+    rpos[e] = 0;
+    if (idx < ritems) {
+      int m, k;
+      const int64_t off = rope_off(idx, m, k);
+      rx[e] = *reinterpret_cast<const uint32_t*>(rsrc + off);
+      rpos[e] = p.positions[m];
+    }
+  }
+  // A: W_UK[i][c0 + 16t + l16][32ks + 8g .. +8]
+  const uint16_t* w = static_cast<const uint16_t*>(p.w_uk) + ((int64_t)i * p.d_c + c0 + l16) * 128 + 8 * g;
+  u16x8 a[4][4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) a[t][ks] = *reinterpret_cast<const u16x8*>(w + t * 16 * 128 + 32 * ks);
+  const uint16_t* q = static_cast<const uint16_t*>(p.q_nope);
+  uint16_t* out = static_cast<uint16_t*>(p.q_lat);
+  auto load_b = [&](int m0, u16x8 (&bq)[4][4]) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int m = m0 + 16 * mt + l16;
+      const uint16_t* qr = q + ((int64_t)(m < M ? m : 0) * p.n_h + i) * 128 + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) bq[mt][ks] = *reinterpret_cast<const u16x8*>(qr + 32 * ks);
+    }
+  };
+  u16x8 bq[4][4];
+  load_b(0, bq);
+  auto rotate = [&](int idx, uint32_t x, int pos) {
+    int m, k;
+    const int64_t off = rope_off(idx, m, k);
+    float sn, cs;
+    sincos_turns(pos, theta[k], &sn, &cs);
+    const float x0 = bf16_to_f32((uint16_t)(x & 0xFFFF)), x1 = bf16_to_f32((uint16_t)(x >> 16));
+    *reinterpret_cast<uint32_t*>(rdst + off) =
+        (uint32_t)f32_to_bf16(x0 * cs - x1 * sn) | ((uint32_t)f32_to_bf16(x0 * sn + x1 * cs) << 16);
+  };
+#pragma unroll
+  for (int e = 0; e < AR_ROPE; ++e) {
+    const int idx = threadIdx.x + 256 * e;
+    if (idx < ritems) rotate(idx, rx[e], rpos[e]);
+  }
+  for (int idx = threadIdx.x + 256 * AR_ROPE; idx < ritems; idx += 256) {   // rows beyond the first 8*256 items
+    int m, k;
+    const int64_t off = rope_off(idx, m, k);
+    rotate(idx, *reinterpret_cast<const uint32_t*>(rsrc + off), p.positions[m]);
+  }
+  for (int m0 = 0; m0 < M; m0 += 64) {
+    // the next block's query rows are in flight while this block is computed
+    u16x8 bn[4][4];
+    if (m0 + 64 < M) load_b(m0 + 64, bn);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int m = m0 + 16 * mt + l16;
+      f32x4 acc[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[t][ks]),
+                                                           __builtin_bit_cast(bf16x8, bq[mt][ks]), acc[t], 0, 0, 0);
+      }
+      if (m < M) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const u16x4 o4 = {f32_to_bf16(acc[t][0]), f32_to_bf16(acc[t][1]), f32_to_bf16(acc[t][2]),
+                            f32_to_bf16(acc[t][3])};
+          *reinterpret_cast<u16x4*>(out + ((int64_t)m * p.n_h + i) * p.d_c + c0 + 16 * t + 4 * g) = o4;
+        }
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) bq[mt][ks] = bn[mt][ks];
+  }
+}
+
 // --------------------------------------------------------- up-projection
 constexpr int OP_MROWS = 64;          // query rows per workgroup (4 waves x 16)
 constexpr int OP_KCHUNK = 64;         // rows of W_UV staged per LDS chunk
@@ -201,6 +323,10 @@ bool absorb_mfma_ok(const AbsorbParams& p) {
 
 hipError_t launch_absorb_mfma(const AbsorbParams& p, hipStream_t stream) {
   const int M = p.B * p.n_q;
+  if (p.d_nope == 128 && p.d_c % AR_LAT == 0) {
+    hipLaunchKernelGGL(absorb_rope_kernel, dim3(p.n_h * (p.d_c / AR_LAT)), dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(absorb_mfma_kernel, dim3(p.n_h, p.d_c / 64), dim3(256), 0, stream, p);
   const int64_t nthreads = (int64_t)M * (p.d_rope / 2) * ((p.n_h + 3) / 4);
   hipLaunchKernelGGL(rope_q_rows_kernel<uint16_t>, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0,

@@ -40,7 +40,9 @@ struct __attribute__((aligned(16))) TailSmem {
   PlanScratch<NT> plan;
 };
 
-__device__ __forceinline__ int wswz(int r) { return 2 * (r & 3); }   // chunk xor of W^UV row r
+// chunk xor of W^UV row r: a transposed read covers 4 consecutive rows x 4
+// chunks (one aligned group of 4); the xor by 4(r%4) gives each row its own group
+__device__ __forceinline__ int wswz(int r) { return 4 * (r & 3); }
 
 template <bool PARTIALS>
 __global__ __launch_bounds__(NT, 1) void tail_kernel(TailParams p, int items_pad) {

@@ -46,3 +46,18 @@ class DecodeStep:
                         stream=stream)
             mla_out_proj(d, self.u, w_uv, self.out, stream=stream)
         return self.out
+
+    def capture(self, q_nope, q_rope, positions, w_uk, w_uv, cache: LatentCache, new_tokens=None,
+                fused_tail: bool = False):
+        """Record one step into a HIP graph (torch.cuda.CUDAGraph) and return it;
+        ``graph.replay()`` then launches the same kernels on the same buffers
+        without the per-call host work.  The library's kernels enqueue no
+        memset or allocation, so the step is capturable as it stands."""
+        import torch
+        self.run(q_nope, q_rope, positions, w_uk, w_uv, cache, new_tokens, fused_tail=fused_tail)   # warm-up
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.run(q_nope, q_rope, positions, w_uk, w_uv, cache, new_tokens, fused_tail=fused_tail)
+        torch.cuda.synchronize()
+        return graph

@@ -285,3 +285,30 @@ def test_cache_append_rotates_positional_key():
         ref = oracle.rope_rotate(rows["k_rope_raw"], np.arange(ctx[b]), 10000.0)
         assert np.abs(data[b, :ctx[b], 512:] - ref).max() <= 2 ** -8 * np.abs(ref).max()
         assert np.isnan(data[b, ctx[b]:]).all()
+
+
+def test_graph_replay_matches_eager():
+    """The step captured once in a HIP graph and replayed: every replay writes
+    the same outputs as the eager step (outputs poisoned with NaN by eager work
+    before each replay), for both the fused and the separate merge."""
+    _need_gpu()
+    from workloads.device import stage
+    from mla_latent_kv_02_amd.step import DecodeStep
+    w = W.custom(name="v3_graph", seed=27, batch=3, n_q=2, ctx=None, ctx_range=(1, 1))
+    st = stage(w, ctx=np.array([300, 2, 97], np.int32))
+    for fused in (True, False):
+        step = DecodeStep(st["dims"], w.batch, w.n_q, 5, torch.bfloat16)
+        args = (st["q_nope"], st["q_rope"], st["positions"], st["w_uk"], st["w_uv"], st["cache"])
+        step.run(*args, fused_tail=fused)
+        torch.cuda.synchronize()
+        ref_o, ref_l = step.out.clone(), step.lse.clone()
+        graph = step.capture(*args, fused_tail=fused)
+        for rep in range(3):
+            step.out.fill_(float("nan"))
+            step.lse.fill_(float("nan"))
+            step.u_part.fill_(float("nan"))
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(step.out, ref_o), (fused, rep)
+            assert torch.equal(step.lse, ref_l), (fused, rep)
