@@ -331,14 +331,7 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
       }
       return __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
     };
-#ifndef DECODE_QK_PF
-#define DECODE_QK_PF 2
-#endif
-#ifndef DECODE_QK_CHAINS
-#define DECODE_QK_CHAINS 2
-#endif
-    constexpr int PF = DECODE_QK_PF;          // K operands read ahead
-    constexpr int QKC = DECODE_QK_CHAINS;     // MFMA accumulation chains
+    constexpr int PF = 2;          // K operands read ahead of their MFMA
 
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -358,14 +351,14 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
       // is busy).  Stage it+3 is loaded into the slot stage it-1 freed.
       f32x16 s_nx = f32x16{};            // scores of the stage whose weights come next
       bf16x8 pb[2] = {bf16x8{}, bf16x8{}};   // weights of the stage about to be published
-      // S^T of one stage into s_nx: two MFMA accumulation chains over alternate k-steps
+      // S^T of one stage into s_nx: one MFMA accumulation chain (dependent
+      // 32x32x16 MFMAs issue back to back; a single chain also spares the sum
+      // of several partial accumulators)
       // With LOADS, the 9 loads of a later stage (prepared in ld) are issued
       // one per 4 k-steps, so their issue overlaps the MFMAs.
       auto qk = [&](const unsigned char* sb, auto loads_tag, unsigned char* ldst) {
         constexpr bool LOADS = decltype(loads_tag)::value;
-        f32x16 cc[QKC];
-#pragma unroll
-        for (int c = 0; c < QKC; ++c) cc[c] = f32x16{};
+        f32x16 acc = f32x16{};
         bf16x8 kring[PF];
 #pragma unroll
         for (int ks = 0; ks < PF; ++ks) kring[ks] = rd_k(sb, ks);
@@ -373,13 +366,11 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
         for (int ks = 0; ks < KSTEPS; ++ks) {
           const bf16x8 kk = kring[ks % PF];
           if (ks + PF < KSTEPS) kring[ks % PF] = rd_k(sb, ks + PF);
-          cc[ks % QKC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qreg[ks], cc[ks % QKC], 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qreg[ks], acc, 0, 0, 0);
           if (LOADS && (ks & 3) == 1) ld.issue_cg(ks >> 2, ldst, wave);
           __builtin_amdgcn_sched_barrier(0);
         }
-        s_nx = cc[0];
-#pragma unroll
-        for (int c = 1; c < QKC; ++c) s_nx += cc[c];
+        s_nx = acc;
       };
       using NoLoads = std::integral_constant<bool, false>;
       using WithLoads = std::integral_constant<bool, true>;

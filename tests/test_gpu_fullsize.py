@@ -1,7 +1,8 @@
 """GPU parity at the full sizes of the DeepSeek-V3-shaped workloads, in the
 launch configuration bench.py times (default split count), on outputs the
 oracle computes one by one: sampled sequences (shortest and longest of the
-ragged batch included) and sampled heads of each.  Tolerance 1e-2 (bf16)."""
+ragged batch included) and sampled heads of each, through both the separate
+merge + up-projection and the fused one.  Tolerance 1e-2 (bf16)."""
 import numpy as np
 import pytest
 
@@ -33,7 +34,15 @@ def test_full_size_sampled(name):
     torch.cuda.synchronize()
     f = lambda t: t.float().cpu().numpy().astype(np.float64)
     got = {"q_lat": f(step.q_lat), "q_pe": f(step.q_pe), "u": f(step.u), "lse": f(step.lse), "o": f(step.out)}
-    assert np.isfinite(got["o"]).all() and np.isfinite(got["lse"]).all()
+    # the fused merge + up-projection that bench.py times, on the same partials
+    import mla_latent_kv_02_amd as mla
+    out2, lse2 = torch.full_like(step.out, float("nan")), torch.full_like(step.lse, float("nan"))
+    mla.mla_combine_out_proj(st["dims"], st["cache"].ctx_lens, ns, step.u_part, step.lse_part, st["w_uv"],
+                             out2, lse2)
+    torch.cuda.synchronize()
+    got["o_fused"], got["lse_fused"] = f(out2), f(lse2)
+    for k in ("o", "lse", "o_fused", "lse_fused"):
+        assert np.isfinite(got[k]).all(), k
     seqs, heads = CASES[name]
     print(f"{name}: num_splits={ns}, total tokens {int(ctx.sum())}", flush=True)
     _check(w, st, got, seqs=seqs(ctx), heads=heads)
