@@ -374,15 +374,24 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
       };
       using NoLoads = std::integral_constant<bool, false>;
       using WithLoads = std::integral_constant<bool, true>;
-      // Softmax of the raw scores in s_nx in 30 small pieces (a few VALU ops
-      // each), so that one piece fits in the shadow of one PV MFMA: 0-7 mask
-      // scores of tokens at or past the row's limit (lim = limit minus the
-      // lane's base token; INT_MIN masks all, and leaves the weights zero);
-      // 8-11 lane maximum over the raw scores; 12 row maximum (the two lanes
-      // holding a row exchange theirs); 13 reference update; 14-29 one weight
-      // exp2(s * scale - m_ref) each, into pb.
-      constexpr int PIECES = 30;
-      float mt = -INFINITY, psum = 0.f, neg_m = 0.f;
+      // Softmax of the raw scores in s_nx in small pieces of a few VALU ops,
+      // one after each PV MFMA of the previous stage, so that the VALU work
+      // runs while the matrix core is busy.  Two schedules:
+      //  - masked (stages that reach the row's limit; 30 pieces): 0-7 mask
+      //    scores of tokens at or past the limit (lim = limit minus the lane's
+      //    base token; INT_MIN masks all, leaving the weights zero), 8-11 lane
+      //    maximum, 12 row maximum (the two lanes holding a row exchange
+      //    theirs), 13 reference update, 14-29 one weight exp2(s*scale - m_ref);
+      //  - visible (every token of the stage visible; 27 pieces), staggered so
+      //    that no piece waits on its own results: 0-3 maxima of 4 scores, 4
+      //    lane maximum, 5 exchange, 6 row maximum, 7-8 reference update, then
+      //    piece 9+i forms the exponent of score i, takes exp2 of score i-1
+      //    and accumulates score i-2 (into one of two sums) and its bf16 weight.
+      constexpr int PIECES_MASKED = 30, PIECES_VISIBLE = 27;
+      float mt = -INFINITY, neg_m = 0.f;
+      float psum[2] = {0.f, 0.f};
+      float t4[4];
+      unsigned sw_mt[2];
       auto sm_piece = [&](int k, int lim) {
         if (k < 8) {
 #pragma unroll
@@ -401,11 +410,39 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
           if (m_ref == -INFINITY) m_ref = mt;       // first visible stage of the row
           over |= mt > m_ref + REF_HEADROOM;
           neg_m = m_ref == -INFINITY ? 0.f : -m_ref;
-        } else if (k < PIECES) {
+        } else if (k < PIECES_MASKED) {
           const int e = k - 14;
           const float pv = __builtin_amdgcn_exp2f(fmaf(s_nx[e], a.scale_log2, neg_m));
-          psum += pv;
+          psum[e & 1] += pv;
           pb[e >> 3][e & 7] = (__bf16)pv;
+        }
+      };
+      auto sm_piece_visible = [&](int k) {
+        if (k < 4) {
+          t4[k] = fmaxf(fmaxf(s_nx[4 * k], s_nx[4 * k + 1]), fmaxf(s_nx[4 * k + 2], s_nx[4 * k + 3]));
+        } else if (k == 4) {
+          mt = fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3]));
+        } else if (k == 5) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+          sw_mt[0] = sw[0];
+          sw_mt[1] = sw[1];
+        } else if (k == 6) {
+          mt = fmaxf(__uint_as_float(sw_mt[0]), __uint_as_float(sw_mt[1])) * a.scale_log2;
+        } else if (k == 7) {
+          m_max = fmaxf(m_max, mt);
+          if (m_ref == -INFINITY) m_ref = mt;       // first visible stage of the row
+        } else if (k == 8) {
+          over |= mt > m_ref + REF_HEADROOM;
+          neg_m = -m_ref;                            // finite: this stage has visible tokens
+        } else if (k < PIECES_VISIBLE) {
+          const int i = k - 9;
+          if (i < 16) s_nx[i] = fmaf(s_nx[i], a.scale_log2, neg_m);
+          if (i >= 1 && i <= 16) s_nx[i - 1] = __builtin_amdgcn_exp2f(s_nx[i - 1]);
+          if (i >= 2) {
+            const int e = i - 2;
+            psum[e & 1] += s_nx[e];
+            pb[e >> 3][e & 7] = (__bf16)s_nx[e];
+          }
         }
       };
       // base token of this lane's scores within a stage: 8*(i/4) + 4*h + i%4 for score i
@@ -418,13 +455,14 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
         qk(sm->stage[0], NoLoads{}, nullptr);
         const int lim = lane_lim(t0);
 #pragma unroll
-        for (int k = 0; k < PIECES; ++k) sm_piece(k, lim);
-        l_run += psum;
+        for (int k = 0; k < PIECES_MASKED; ++k) sm_piece(k, lim);
+        l_run += psum[0] + psum[1];
       }
 
       // O^T[own 128 latents][128 rows] += V^T . P^T for one stage, with the
       // softmax pieces of the next stage after the MFMAs
-      auto pv_stage = [&](const unsigned char* sb, int lim) {
+      auto pv_stage = [&](const unsigned char* sb, auto visible_tag, int lim) {
+        constexpr bool VISIBLE = decltype(visible_tag)::value;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           bf16x8 pq[4];
@@ -438,15 +476,25 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
             for (int hb = 0; hb < 4; ++hb) {
               pv_mfma(o[mb][hb], cur, pq[hb]);
-              sm_piece(16 * q + 4 * mb + hb, lim);
+              if (VISIBLE) sm_piece_visible(16 * q + 4 * mb + hb);
+              else sm_piece(16 * q + 4 * mb + hb, lim);
               __builtin_amdgcn_sched_barrier(0);
             }
           }
         }
       };
+      using Visible = std::integral_constant<bool, true>;
+      using Masked = std::integral_constant<bool, false>;
 
-      for (int it = 0; it < nst; ++it) {
+      // one iteration of the stage loop; VISIBLE: the next stage's tokens are
+      // all visible to this wave's rows (its softmax needs no mask)
+      auto iteration = [&](int it, auto visible_tag) {
+        constexpr bool VISIBLE = decltype(visible_tag)::value;
         const bool has_next = it + 1 < nst;
+        // addresses of stage it+3 first: a paged cache looks its block ids up
+        // with scalar loads, whose wait then merges with the barrier's
+        const bool do_load = it + NSTAGE - 1 < nst;
+        if (do_load) ld.prepare(t0 + (it + NSTAGE - 1) * T);
         if (has_next) wait_stages_in_flight(it + 2 < nst ? 1 : 0);   // stage it+1 resident
         lds_barrier();   // every wave is done with the weights of stage it-1
         // ------------ publish the weights of stage it (B-operand layout, per k-step)
@@ -456,11 +504,9 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
         pb[1] = bf16x8{};
         // stage it+3 goes into the slot stage it-1 freed; its loads ride along
         // with the MFMAs of S^T(it+1) when there are any
-        const bool do_load = it + NSTAGE - 1 < nst;
         unsigned char* ldst = sm->stage[(it + NSTAGE - 1) % NSTAGE];
-        if (do_load) ld.prepare(t0 + (it + NSTAGE - 1) * T);
         const int tok_nx = t0 + (it + 1) * T;
-        const bool qk_next = active && has_next && tok_nx < limit;    // scores of stage it+1
+        const bool qk_next = VISIBLE || (active && has_next && tok_nx < limit);    // scores of stage it+1
         if (qk_next) {
           if (do_load) qk(sm->stage[(it + 1) % NSTAGE], WithLoads{}, ldst);
           else qk(sm->stage[(it + 1) % NSTAGE], NoLoads{}, nullptr);
@@ -471,10 +517,18 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
         lds_barrier();   // weights of stage it visible to all waves
         const unsigned char* sb = sm->stage[it % NSTAGE];
         mt = -INFINITY;
-        psum = 0.f;
-        pv_stage(sb, qk_next ? lane_lim(tok_nx) : INT_MIN);
-        l_run += psum;
-      }
+        psum[0] = psum[1] = 0.f;
+        pv_stage(sb, visible_tag, qk_next ? lane_lim(tok_nx) : INT_MIN);
+        l_run += psum[0] + psum[1];
+      };
+      // Iterations whose next stage is entirely visible (stage it+1 ends at or
+      // before the limit) take the unmasked schedule; every wave runs the same
+      // number of iterations, so the barriers inside stay matched.
+      int it_vis = active ? (limit - t0) / T - 1 : 0;   // iterations it < it_vis are visible
+      it_vis = it_vis < 0 ? 0 : (it_vis > nst ? nst : it_vis);
+      int it = 0;
+      for (; it < it_vis; ++it) iteration(it, Visible{});
+      for (; it < nst; ++it) iteration(it, Masked{});
       // ------------ did any row of the workgroup outgrow its reference?
       const bool wover = __builtin_amdgcn_ballot_w64(over) != 0;
       if (lane == 0) sm->flag[wave] = wover;
