@@ -85,6 +85,13 @@ __device__ __forceinline__ int plan_parts(int64_t prefix, int64_t len, int64_t q
   return len > 0 ? (int)((prefix + len - 1) / q - prefix / q + 1) : 0;
 }
 
+// Workgroup barrier for data exchanged through LDS only: waits for this
+// wave's LDS operations, not for its outstanding global loads (which
+// __syncthreads() also waits for, draining whatever is in flight).
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Inclusive scan of one int64 per thread over a workgroup of NT threads
 // (NT a multiple of 64).  `scratch` holds NT/64 + 1 int64 values.  Returns the
 // inclusive prefix; *total receives the workgroup sum.
@@ -97,16 +104,16 @@ __device__ __forceinline__ int64_t block_scan_incl(int64_t v, int64_t* scratch, 
     if (lane >= d) v += o;
   }
   if (lane == 63) scratch[wave] = v;
-  __syncthreads();
+  lds_sync();
   if (threadIdx.x == 0) {
     int64_t run = 0;
     for (int w = 0; w < NT / 64; ++w) { int64_t s = scratch[w]; scratch[w] = run; run += s; }
     scratch[NT / 64] = run;
   }
-  __syncthreads();
+  lds_sync();
   v += scratch[wave];
   *total = scratch[NT / 64];
-  __syncthreads();
+  lds_sync();
   return v;
 }
 
@@ -181,20 +188,22 @@ __device__ void for_each_segment(const int32_t* __restrict__ ctx_lens, int B, in
 
 // For the n (<= NT) sequences b_lo .. b_lo + n - 1: first partial slot and
 // number of partials, written to slot0[] and nparts[] (n entries each, LDS).
-// All NT threads of the workgroup must call this together.
+// len_tid = ctx_lens[threadIdx.x] (0 for threadIdx.x >= B), loaded by the
+// caller: issued before the caller's other global loads, the wait for it does
+// not wait for them.  All NT threads of the workgroup must call this together.
 template <int NT>
 __device__ void plan_slot_range(const int32_t* __restrict__ ctx_lens, int B, int num_splits, int b_lo, int n,
-                                PlanScratch<NT>* sc, int* slot0, int* nparts) {
+                                int len_tid, PlanScratch<NT>* sc, int* slot0, int* nparts) {
   const int tid = threadIdx.x;
-  int64_t part = 0;
-  for (int k = tid; k < B; k += NT) part += ctx_lens[k];
+  int64_t part = len_tid;
+  for (int k = tid + NT; k < B; k += NT) part += ctx_lens[k];
   int64_t total;
   block_scan_incl<NT>(part, sc->scan, &total);
   const int64_t q = plan_chunk(total, num_splits);
   int64_t run = 0, slot_run = 0;
   for (int c0 = 0; c0 < b_lo + n; c0 += NT) {
     const int k = c0 + tid;
-    const int64_t len = k < B ? ctx_lens[k] : 0;
+    const int64_t len = c0 == 0 ? len_tid : (k < B ? ctx_lens[k] : 0);
     int64_t tot_len, tot_np;
     const int64_t p = run + block_scan_incl<NT>(len, sc->scan, &tot_len) - len;
     const int64_t np = plan_parts(p, len, q);
@@ -203,7 +212,7 @@ __device__ void plan_slot_range(const int32_t* __restrict__ ctx_lens, int B, int
     run += tot_len;
     slot_run += tot_np;
   }
-  __syncthreads();
+  lds_sync();
 }
 
 // For sequence b: first partial slot and number of partials (0 if empty).

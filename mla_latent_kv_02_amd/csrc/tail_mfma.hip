@@ -58,6 +58,8 @@ __global__ __launch_bounds__(NT, 1) void tail_kernel(TailParams p, int items_pad
   const int ih = item / rblocks;
   const int m0 = (item % rblocks) * TR;
   const int k0 = wave * TKW;                 // first latent of this wave's slice
+  // the sequence lengths for the plan, loaded ahead of the weights
+  const int len_tid = PARTIALS && (int)threadIdx.x < p.B ? p.ctx_lens[threadIdx.x] : 0;
 
   // ---- 1. this wave's W^UV rows into LDS (4 rows of 256 B per instruction)
   {
@@ -91,7 +93,8 @@ __global__ __launch_bounds__(NT, 1) void tail_kernel(TailParams p, int items_pad
   const int b_lo = m0 / p.n_q;
   if (PARTIALS) {
     const int b_hi = ((M < m0 + TR ? M : m0 + TR) - 1) / p.n_q;
-    plan_slot_range<NT>(p.ctx_lens, p.B, p.num_splits, b_lo, b_hi - b_lo + 1, &sm.plan, sm.slot0, sm.nparts);
+    plan_slot_range<NT>(p.ctx_lens, p.B, p.num_splits, b_lo, b_hi - b_lo + 1, len_tid, &sm.plan, sm.slot0,
+                        sm.nparts);
   }
   const int b = mvalid ? m / p.n_q : b_lo;
   const int jq = mvalid ? m % p.n_q : 0;
@@ -110,9 +113,14 @@ __global__ __launch_bounds__(NT, 1) void tail_kernel(TailParams p, int items_pad
     // rescaled whenever mx grows; then L = mx + log s and u = acc / s.  Every
     // r_k <= lse_k, so no weight exceeds 1.
     const float2* lp = reinterpret_cast<const float2*>(p.lse_part);
-    // this lane's 16 loads of partial k (latents k0 + 16ks + 8hk .. +8 of the row)
-    auto fetch = [&](int k, f32x4* v, float2& rl) {
-      const int64_t prow = (slot0 + k) * rows_per_slot + rowid;
+    // this lane's partials: k = replica + j*rep, j = 0 .. nj-1.  Partial j is
+    // fetched into buffer j%2 while partial j-1 is merged, so two partials are
+    // in flight.  The loads of a fetch are unconditional (a lane past its last
+    // partial re-reads row 0 and ignores it), so every wait is for exactly the
+    // older buffer.
+    const int nj = replica < np ? (np - replica + rep - 1) / rep : 0;
+    auto fetch = [&](int j, f32x4* v, float2& rl) {
+      const int64_t prow = j < nj ? (int64_t)(slot0 + replica + j * rep) * rows_per_slot + rowid : 0;
       rl = lp[prow];
       const f32x4* src = reinterpret_cast<const f32x4*>(p.u_part + prow * p.d_c + k0 + 8 * hk);
 #pragma unroll
@@ -122,18 +130,8 @@ __global__ __launch_bounds__(NT, 1) void tail_kernel(TailParams p, int items_pad
       }
     };
     float mx = -INFINITY, sum = 0.f;
-    // double-buffered: the loads of the next partial are in flight while the
-    // current one is accumulated
-    f32x4 nxt[2 * TKS];
-    float2 rl_nxt = {0.f, -INFINITY};
-    if (replica < np) fetch(replica, nxt, rl_nxt);
-    for (int k = replica; k < np; k += rep) {
-      f32x4 cur[2 * TKS];
-#pragma unroll
-      for (int e = 0; e < 2 * TKS; ++e) cur[e] = nxt[e];
-      const float2 rl = rl_nxt;
-      if (k + rep < np) fetch(k + rep, nxt, rl_nxt);
-      if (rl.y == -INFINITY) continue;             // no visible token in this partial
+    auto merge = [&](int j, const f32x4* v, float2 rl) {
+      if (j >= nj || rl.y == -INFINITY) return;    // past the lane's partials, or no visible token
       if (rl.y > mx) {
         const float sc = __expf(mx - rl.y);        // 0 while mx is -inf
         sum *= sc;
@@ -144,8 +142,21 @@ __global__ __launch_bounds__(NT, 1) void tail_kernel(TailParams p, int items_pad
       sum += __expf(rl.y - mx);
       const float wk = __expf(rl.x - mx);
 #pragma unroll
-      for (int e = 0; e < 2 * TKS; ++e) u[e] += wk * cur[e];
+      for (int e = 0; e < 2 * TKS; ++e) u[e] += wk * v[e];
+    };
+    f32x4 va[2 * TKS], vb[2 * TKS];
+    float2 ra, rb;
+    fetch(0, va, ra);
+    fetch(1, vb, rb);
+    int j = 0;
+    for (; j + 2 < nj; j += 2) {
+      merge(j, va, ra);
+      fetch(j + 2, va, ra);
+      merge(j + 1, vb, rb);
+      fetch(j + 3, vb, rb);
     }
+    merge(j, va, ra);
+    merge(j + 1, vb, rb);
     // merge the replicas of the row (lanes xor prow2, 2*prow2, ... within the half)
     for (int sh = prow2; sh < TR; sh <<= 1) {
       const float mo = __shfl_xor(mx, sh, 64);
