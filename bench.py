@@ -3,7 +3,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3_b64]
 
 A step is the whole hot path over one batch: append the step's own latents to
-the cache, absorb the query through W_UK (+ query RoPE), decode attention over
+the cache and absorb the query through W_UK (+ query RoPE) in one launch
+(mla_append_absorb_q, unless --separate-append), decode attention over
 the latent cache split into token-balanced work units, log-sum-exp combine of
 the partials, and the W_UV up-projection (the last two as one pass over the
 partials, mla_combine_out_proj, unless --separate-tail).  Inputs are seeded synthetic
@@ -42,6 +43,8 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="replay the timed steps from a HIP graph captured once (eager launches are as fast "
                          "or faster on these kernels, so they are the default)")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="append the step's rows with mla_cache_append, then mla_absorb_q (two launches)")
     ap.add_argument("--separate-tail", action="store_true",
                     help="mla_combine then mla_out_proj instead of mla_combine_out_proj")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -215,8 +218,12 @@ def main():
     fused_tail = w.dtype == "bf16" and w.d_c == 512 and w.d_v == 128 and not args.separate_tail
 
     def run_step(ev=None):
-        mla.mla_cache_append(d, st["cache"], *new_tokens)
-        mla.mla_absorb_q(d, st["q_nope"], st["q_rope"], st["positions"], st["w_uk"], step.q_lat, step.q_pe)
+        if args.separate_append:
+            mla.mla_cache_append(d, st["cache"], *new_tokens)
+            mla.mla_absorb_q(d, st["q_nope"], st["q_rope"], st["positions"], st["w_uk"], step.q_lat, step.q_pe)
+        else:
+            mla.mla_append_absorb_q(d, st["cache"], *new_tokens, st["q_nope"], st["q_rope"], st["positions"],
+                                    st["w_uk"], step.q_lat, step.q_pe)
         if ev is not None:
             ev[0].record(stream)
         mla.mla_decode(d, step.q_lat, step.q_pe, st["cache"], st["positions"], num_splits, step.u_part,
@@ -292,6 +299,7 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic (seeded Philox N(0,1) latents/queries, "
         "N(0,1/d_c) weights)",
         "config": {"workload": w.name, "description": w.description, "fused_tail": fused_tail,
+                   "fused_append": not args.separate_append,
                    "step_launch": "graph" if graph is not None else "eager", "batch": w.batch, "n_q": w.n_q,
                    "n_h": w.n_h, "d_c": w.d_c, "d_rope": w.d_rope, "d_nope": w.d_nope, "d_v": w.d_v,
                    "context_tokens": int(ctx.sum()), "block_size": w.block_size, "num_splits": num_splits},

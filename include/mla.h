@@ -168,6 +168,21 @@ mla_status_t mla_cache_append(const mla_dims_t *dims, const mla_cache_t *cache, 
                               const void *c_kv_new, int64_t c_kv_stride,
                               const void *k_rope_new, int64_t k_rope_stride, void *stream);
 
+/* mla_cache_append (n new tokens, positions new_positions) followed by
+ * mla_absorb_q (B sequences, n_q query tokens, positions), with the same
+ * results as the two calls made in that order on one stream.  For the V3
+ * shapes (bf16, d_nope = 128, d_c a multiple of 256) with a bf16 cache both
+ * run in a single launch: a decode step's new rows cost no launch of their
+ * own ([Huny] §2.2 for the cached row, §3.1 for the absorbed query).  Every
+ * argument of both calls is checked before anything is enqueued; n = 0 or
+ * B = 0 skips that part. */
+mla_status_t mla_append_absorb_q(const mla_dims_t *dims, const mla_cache_t *cache, int32_t n,
+                                 const int32_t *seq_ids, const int32_t *new_positions,
+                                 const void *c_kv_new, int64_t c_kv_stride, const void *k_rope_new,
+                                 int64_t k_rope_stride, int32_t B, int32_t n_q, mla_dtype_t dt,
+                                 const void *q_nope, const void *q_rope, const int32_t *positions,
+                                 const void *w_uk, void *q_lat, void *q_pe, void *stream);
+
 /* Static description of a status code. */
 const char *mla_status_string(mla_status_t status);
 

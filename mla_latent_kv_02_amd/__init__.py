@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     load_library,
     mla_absorb_q,
     mla_cache_append,
+    mla_append_absorb_q,
     mla_combine,
     mla_decode,
     mla_num_partials,

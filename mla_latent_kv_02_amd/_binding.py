@@ -18,7 +18,7 @@ MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP = 0, 1, 2, 3
 F32, BF16 = 0, 1
 
 EXPORTED = ("mla_absorb_q", "mla_decode", "mla_combine", "mla_out_proj", "mla_combine_out_proj",
-            "mla_cache_append", "mla_num_partials", "mla_status_string", "mla_version")
+            "mla_cache_append", "mla_append_absorb_q", "mla_num_partials", "mla_status_string", "mla_version")
 
 
 class MlaError(RuntimeError):
@@ -60,6 +60,7 @@ def load_library(path: str = LIB_PATH):
         "mla_out_proj": [DP, I32, I32, P, ctypes.c_int, P, P, V],
         "mla_combine_out_proj": [DP, I32, I32, P, I32, P, P, ctypes.c_int, P, P, P, V],
         "mla_cache_append": [DP, CP, I32, P, P, P, I64, P, I64, V],
+        "mla_append_absorb_q": [DP, CP, I32, P, P, P, I64, P, I64, I32, I32, ctypes.c_int, P, P, P, P, P, P, V],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -158,9 +159,8 @@ def mla_num_partials(B: int, num_splits: int) -> int:
     return int(load_library().mla_num_partials(B, num_splits))
 
 
-def mla_absorb_q(dims: Dims, q_nope, q_rope, positions, w_uk, q_lat, q_pe, stream=None) -> None:
+def _absorb_checks(dims: Dims, q_nope, q_rope, positions, w_uk, q_lat, q_pe):
     B, n_q = q_nope.shape[0], q_nope.shape[1]
-    dt = _dtype(q_nope)
     for t, n in ((q_nope, "q_nope"), (q_rope, "q_rope"), (w_uk, "w_uk"), (q_lat, "q_lat"), (q_pe, "q_pe")):
         _dev(t, n, q_nope.dtype)
     _dev(positions, "positions", _torch().int32)
@@ -170,6 +170,12 @@ def mla_absorb_q(dims: Dims, q_nope, q_rope, positions, w_uk, q_lat, q_pe, strea
     _shape(w_uk, "w_uk", (dims.n_h, dims.d_c, dims.d_nope))
     _shape(q_lat, "q_lat", (B, n_q, dims.n_h, dims.d_c))
     _shape(q_pe, "q_pe", (B, n_q, dims.n_h, dims.d_rope))
+    return B, n_q
+
+
+def mla_absorb_q(dims: Dims, q_nope, q_rope, positions, w_uk, q_lat, q_pe, stream=None) -> None:
+    B, n_q = _absorb_checks(dims, q_nope, q_rope, positions, w_uk, q_lat, q_pe)
+    dt = _dtype(q_nope)
     d = dims._c()
     _check("mla_absorb_q", load_library().mla_absorb_q(
         ctypes.byref(d), B, n_q, dt, q_nope.data_ptr(), q_rope.data_ptr(), positions.data_ptr(),
@@ -263,6 +269,30 @@ def mla_cache_append(dims: Dims, cache: LatentCache, seq_ids, positions, c_kv_ne
                      stream=None) -> None:
     """c_kv_new [n][>= d_c] and k_rope_new [n][>= d_rope] (row strides taken from
     the tensors, so both may be column slices of one [n][d_c + d_rope] array)."""
+    n = _append_checks(dims, cache, seq_ids, positions, c_kv_new, k_rope_new)
+    d, c = dims._c(), cache._c()
+    _check("mla_cache_append", load_library().mla_cache_append(
+        ctypes.byref(d), ctypes.byref(c), n, seq_ids.data_ptr(), positions.data_ptr(),
+        c_kv_new.data_ptr(), c_kv_new.stride(0), k_rope_new.data_ptr(), k_rope_new.stride(0),
+        _stream(stream)))
+
+
+def mla_append_absorb_q(dims: Dims, cache: LatentCache, seq_ids, new_positions, c_kv_new, k_rope_new,
+                        q_nope, q_rope, positions, w_uk, q_lat, q_pe, stream=None) -> None:
+    """mla_cache_append(cache, seq_ids, new_positions, c_kv_new, k_rope_new) then
+    mla_absorb_q(q_nope, q_rope, positions, w_uk, q_lat, q_pe), in one launch
+    where the library has the fused kernel."""
+    n = _append_checks(dims, cache, seq_ids, new_positions, c_kv_new, k_rope_new)
+    B, n_q = _absorb_checks(dims, q_nope, q_rope, positions, w_uk, q_lat, q_pe)
+    d, c = dims._c(), cache._c()
+    _check("mla_append_absorb_q", load_library().mla_append_absorb_q(
+        ctypes.byref(d), ctypes.byref(c), n, seq_ids.data_ptr(), new_positions.data_ptr(),
+        c_kv_new.data_ptr(), c_kv_new.stride(0), k_rope_new.data_ptr(), k_rope_new.stride(0),
+        B, n_q, _dtype(q_nope), q_nope.data_ptr(), q_rope.data_ptr(), positions.data_ptr(),
+        w_uk.data_ptr(), q_lat.data_ptr(), q_pe.data_ptr(), _stream(stream)))
+
+
+def _append_checks(dims: Dims, cache: LatentCache, seq_ids, positions, c_kv_new, k_rope_new) -> int:
     torch = _torch()
     n = seq_ids.shape[0]
     _dev(seq_ids, "seq_ids", torch.int32)
@@ -275,8 +305,4 @@ def mla_cache_append(dims: Dims, cache: LatentCache, seq_ids, positions, c_kv_ne
             raise ValueError(f"{name} must have {n} rows")
     if c_kv_new.shape[1] != dims.d_c or k_rope_new.shape[1] != dims.d_rope:
         raise ValueError("c_kv_new / k_rope_new widths must be d_c / d_rope")
-    d, c = dims._c(), cache._c()
-    _check("mla_cache_append", load_library().mla_cache_append(
-        ctypes.byref(d), ctypes.byref(c), n, seq_ids.data_ptr(), positions.data_ptr(),
-        c_kv_new.data_ptr(), c_kv_new.stride(0), k_rope_new.data_ptr(), k_rope_new.stride(0),
-        _stream(stream)))
+    return n

@@ -94,5 +94,8 @@ struct AppendParams {
   float rope_base;
 };
 hipError_t launch_cache_append(const AppendParams& p, hipStream_t stream);
+// mla_cache_append then the bf16 MFMA absorption, in one launch where the
+// absorption takes its one-pass kernel and the cache is bf16 (ap may be null).
+hipError_t launch_append_absorb_mfma(const AbsorbParams& p, const AppendParams* ap, hipStream_t stream);
 
 }  // namespace mla

@@ -44,6 +44,46 @@ mla::CacheView view_of(const mla_cache_t* c, const mla_dims_t* d) {
 
 mla_status_t from_hip(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 
+// Checks the arguments of mla_absorb_q and fills *p (p->B == 0: nothing to do).
+mla_status_t absorb_args(const mla_dims_t* dims, int32_t B, int32_t n_q, mla_dtype_t dt, const void* q_nope,
+                         const void* q_rope, const int32_t* positions, const void* w_uk, void* q_lat, void* q_pe,
+                         mla::AbsorbParams* p) {
+  if (!dims_ok(dims) || B < 0 || n_q < 1 || !dtype_ok(dt)) return MLA_ERR_INVALID_ARG;
+  p->B = 0;
+  if (B == 0) return MLA_OK;
+  if (!q_nope || !q_rope || !positions || !w_uk || !q_lat || !q_pe) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)B * n_q > (1 << 24)) return MLA_ERR_UNSUPPORTED;
+  if ((size_t)16 * dims->d_nope * sizeof(float) > 64 * 1024) return MLA_ERR_UNSUPPORTED;
+  p->q_nope = q_nope; p->q_rope = q_rope; p->positions = positions; p->w_uk = w_uk;
+  p->q_lat = q_lat; p->q_pe = q_pe;
+  p->B = B; p->n_q = n_q; p->n_h = dims->n_h; p->d_c = dims->d_c; p->d_rope = dims->d_rope;
+  p->d_nope = dims->d_nope; p->bf16 = dt == MLA_BF16; p->rope_base = base_of(dims);
+  return MLA_OK;
+}
+
+// Checks the arguments of mla_cache_append and fills *p (p->n == 0: nothing to do).
+mla_status_t append_args(const mla_dims_t* dims, const mla_cache_t* cache, int32_t n, const int32_t* seq_ids,
+                         const int32_t* positions, const void* c_kv_new, int64_t c_kv_stride,
+                         const void* k_rope_new, int64_t k_rope_stride, mla::AppendParams* p) {
+  if (!dims_ok(dims) || n < 0 || !cache_ok(cache, dims)) return MLA_ERR_INVALID_ARG;
+  p->n = 0;
+  if (n == 0) return MLA_OK;
+  if (!seq_ids || !positions || !c_kv_new || !k_rope_new) return MLA_ERR_INVALID_ARG;
+  if (c_kv_stride < dims->d_c || k_rope_stride < dims->d_rope) return MLA_ERR_INVALID_ARG;
+  p->cache = view_of(cache, dims);
+  p->cache_data = cache->data;
+  p->n = n; p->seq_ids = seq_ids; p->positions = positions;
+  p->c_kv = c_kv_new; p->c_kv_stride = c_kv_stride; p->k_rope = k_rope_new; p->k_rope_stride = k_rope_stride;
+  p->d_c = dims->d_c; p->d_rope = dims->d_rope; p->bf16 = cache->dtype == MLA_BF16;
+  p->rope_base = base_of(dims);
+  return MLA_OK;
+}
+
+mla_status_t launch_absorb_any(const mla::AbsorbParams& p, hipStream_t stream) {
+  if (mla::absorb_mfma_ok(p)) return from_hip(mla::launch_absorb_mfma(p, stream));
+  return from_hip(mla::launch_absorb(p, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -68,18 +108,10 @@ int64_t mla_num_partials(int32_t B, int32_t num_splits) {
 mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t B, int32_t n_q, mla_dtype_t dt,
                           const void* q_nope, const void* q_rope, const int32_t* positions,
                           const void* w_uk, void* q_lat, void* q_pe, void* stream) {
-  if (!dims_ok(dims) || B < 0 || n_q < 1 || !dtype_ok(dt)) return MLA_ERR_INVALID_ARG;
-  if (B == 0) return MLA_OK;
-  if (!q_nope || !q_rope || !positions || !w_uk || !q_lat || !q_pe) return MLA_ERR_INVALID_ARG;
-  if ((int64_t)B * n_q > (1 << 24)) return MLA_ERR_UNSUPPORTED;
   mla::AbsorbParams p;
-  p.q_nope = q_nope; p.q_rope = q_rope; p.positions = positions; p.w_uk = w_uk;
-  p.q_lat = q_lat; p.q_pe = q_pe;
-  p.B = B; p.n_q = n_q; p.n_h = dims->n_h; p.d_c = dims->d_c; p.d_rope = dims->d_rope;
-  p.d_nope = dims->d_nope; p.bf16 = dt == MLA_BF16; p.rope_base = base_of(dims);
-  if ((size_t)16 * p.d_nope * sizeof(float) > 64 * 1024) return MLA_ERR_UNSUPPORTED;
-  if (mla::absorb_mfma_ok(p)) return from_hip(mla::launch_absorb_mfma(p, (hipStream_t)stream));
-  return from_hip(mla::launch_absorb(p, (hipStream_t)stream));
+  const mla_status_t st = absorb_args(dims, B, n_q, dt, q_nope, q_rope, positions, w_uk, q_lat, q_pe, &p);
+  if (st != MLA_OK || p.B == 0) return st;
+  return launch_absorb_any(p, (hipStream_t)stream);
 }
 
 mla_status_t mla_decode(const mla_dims_t* dims, int32_t B, int32_t n_q, const void* q_lat,
@@ -154,18 +186,33 @@ mla_status_t mla_cache_append(const mla_dims_t* dims, const mla_cache_t* cache, 
                               const int32_t* seq_ids, const int32_t* positions,
                               const void* c_kv_new, int64_t c_kv_stride, const void* k_rope_new,
                               int64_t k_rope_stride, void* stream) {
-  if (!dims_ok(dims) || n < 0 || !cache_ok(cache, dims)) return MLA_ERR_INVALID_ARG;
-  if (n == 0) return MLA_OK;
-  if (!seq_ids || !positions || !c_kv_new || !k_rope_new) return MLA_ERR_INVALID_ARG;
-  if (c_kv_stride < dims->d_c || k_rope_stride < dims->d_rope) return MLA_ERR_INVALID_ARG;
   mla::AppendParams p;
-  p.cache = view_of(cache, dims);
-  p.cache_data = cache->data;
-  p.n = n; p.seq_ids = seq_ids; p.positions = positions;
-  p.c_kv = c_kv_new; p.c_kv_stride = c_kv_stride; p.k_rope = k_rope_new; p.k_rope_stride = k_rope_stride;
-  p.d_c = dims->d_c; p.d_rope = dims->d_rope; p.bf16 = cache->dtype == MLA_BF16;
-  p.rope_base = base_of(dims);
+  const mla_status_t st = append_args(dims, cache, n, seq_ids, positions, c_kv_new, c_kv_stride, k_rope_new,
+                                      k_rope_stride, &p);
+  if (st != MLA_OK || p.n == 0) return st;
   return from_hip(mla::launch_cache_append(p, (hipStream_t)stream));
+}
+
+mla_status_t mla_append_absorb_q(const mla_dims_t* dims, const mla_cache_t* cache, int32_t n,
+                                 const int32_t* seq_ids, const int32_t* new_positions, const void* c_kv_new,
+                                 int64_t c_kv_stride, const void* k_rope_new, int64_t k_rope_stride, int32_t B,
+                                 int32_t n_q, mla_dtype_t dt, const void* q_nope, const void* q_rope,
+                                 const int32_t* positions, const void* w_uk, void* q_lat, void* q_pe,
+                                 void* stream) {
+  mla::AppendParams ap;
+  mla::AbsorbParams p;
+  mla_status_t st = append_args(dims, cache, n, seq_ids, new_positions, c_kv_new, c_kv_stride, k_rope_new,
+                                k_rope_stride, &ap);
+  if (st != MLA_OK) return st;
+  st = absorb_args(dims, B, n_q, dt, q_nope, q_rope, positions, w_uk, q_lat, q_pe, &p);
+  if (st != MLA_OK) return st;
+  const hipStream_t s = (hipStream_t)stream;
+  if (p.B > 0 && mla::absorb_mfma_ok(p)) return from_hip(mla::launch_append_absorb_mfma(p, &ap, s));
+  if (ap.n > 0) {
+    st = from_hip(mla::launch_cache_append(ap, s));
+    if (st != MLA_OK) return st;
+  }
+  return p.B > 0 ? launch_absorb_any(p, s) : MLA_OK;
 }
 
 }  // extern "C"

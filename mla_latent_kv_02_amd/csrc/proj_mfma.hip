@@ -18,6 +18,7 @@
 
 #include "mla_device.h"
 #include "launch.h"
+#include "append_row.h"
 
 namespace mla {
 namespace {
@@ -105,9 +106,21 @@ __global__ __launch_bounds__(256) void rope_q_rows_kernel(AbsorbParams p) {
 // mt): lane l holds latents 16t + 4(l/16) + 0..3 of row 16mt + l%16, stored as
 // 8 bytes (a wave writes 128 contiguous bytes of each row).
 // Requires d_nope == 128, d_c % 256 == 0, bf16.
+// Workgroups n_absorb and up take the append role instead: they write the
+// element pairs of the new bf16 cache rows of `ap` (as the append kernel does),
+// on CUs beside the absorption workgroups, so that a step's append costs no
+// launch of its own.
 constexpr int AR_LAT = 256;           // latents per workgroup
 constexpr int AR_ROPE = 8;            // RoPE items per thread whose loads go first
-__global__ __launch_bounds__(256) void absorb_rope_kernel(AbsorbParams p) {
+__global__ __launch_bounds__(256) void absorb_rope_kernel(AbsorbParams p, AppendParams ap, int n_absorb) {
+  if ((int)blockIdx.x >= n_absorb) {
+    const int pairs = (ap.d_c + ap.d_rope) / 2;
+    const int64_t items = (int64_t)ap.n * pairs;
+    const int64_t stride = (int64_t)(gridDim.x - n_absorb) * 256;
+    for (int64_t it = (int64_t)(blockIdx.x - n_absorb) * 256 + threadIdx.x; it < items; it += stride)
+      append_pair<uint16_t>(ap, (int)(it / pairs), (int)(it % pairs));
+    return;
+  }
   __shared__ double theta[64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nslices = p.d_c / AR_LAT;
@@ -322,9 +335,27 @@ bool absorb_mfma_ok(const AbsorbParams& p) {
 }
 
 hipError_t launch_absorb_mfma(const AbsorbParams& p, hipStream_t stream) {
+  return launch_append_absorb_mfma(p, nullptr, stream);
+}
+
+hipError_t launch_append_absorb_mfma(const AbsorbParams& p, const AppendParams* ap, hipStream_t stream) {
   const int M = p.B * p.n_q;
-  if (p.d_nope == 128 && p.d_c % AR_LAT == 0) {
-    hipLaunchKernelGGL(absorb_rope_kernel, dim3(p.n_h * (p.d_c / AR_LAT)), dim3(256), 0, stream, p);
+  const bool append = ap != nullptr && ap->n > 0;
+  const bool one_pass = p.d_nope == 128 && p.d_c % AR_LAT == 0;
+  if (append && !(one_pass && ap->bf16)) {   // the append gets a launch of its own
+    const hipError_t e = launch_cache_append(*ap, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (one_pass) {
+    const int n_absorb = p.n_h * (p.d_c / AR_LAT);
+    AppendParams none{};
+    int n_append = 0;
+    if (append && ap->bf16) {
+      const int64_t blocks = ((int64_t)ap->n * ((ap->d_c + ap->d_rope) / 2) + 255) / 256;
+      n_append = (int)(blocks < 256 ? blocks : 256);
+    }
+    hipLaunchKernelGGL(absorb_rope_kernel, dim3(n_absorb + n_append), dim3(256), 0, stream, p,
+                       n_append > 0 ? *ap : none, n_absorb);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(absorb_mfma_kernel, dim3(p.n_h, p.d_c / 64), dim3(256), 0, stream, p);

@@ -2,15 +2,16 @@
 
     [cache_append of the new tokens] -> absorb_q -> decode -> combine -> out_proj
 
-or, with ``fused_tail``, the last two as the single mla_combine_out_proj call
-(the merged u is then not stored).  ``DecodeStep`` owns the intermediate
+The append and the absorption go through mla_append_absorb_q (one launch where
+the library fuses them); with ``fused_tail`` the last two are the single
+mla_combine_out_proj call (the merged u is then not stored).  ``DecodeStep`` owns the intermediate
 buffers (q_lat, q_pe, the split-KV partials, u, lse) and the output, sized once
 for a batch shape, so that a step allocates nothing.  Every call goes through
 the C ABI.
 """
 from __future__ import annotations
 
-from ._binding import (Dims, LatentCache, mla_absorb_q, mla_cache_append, mla_combine, mla_combine_out_proj,
+from ._binding import (Dims, LatentCache, mla_absorb_q, mla_append_absorb_q, mla_combine, mla_combine_out_proj,
                        mla_decode, mla_num_partials, mla_out_proj)
 
 
@@ -34,8 +35,10 @@ class DecodeStep:
         step's own latents to the cache first."""
         d = self.dims
         if new_tokens is not None:
-            mla_cache_append(d, cache, *new_tokens, stream=stream)
-        mla_absorb_q(d, q_nope, q_rope, positions, w_uk, self.q_lat, self.q_pe, stream=stream)
+            mla_append_absorb_q(d, cache, *new_tokens, q_nope, q_rope, positions, w_uk, self.q_lat, self.q_pe,
+                                stream=stream)
+        else:
+            mla_absorb_q(d, q_nope, q_rope, positions, w_uk, self.q_lat, self.q_pe, stream=stream)
         mla_decode(d, self.q_lat, self.q_pe, cache, positions, self.num_splits, self.u_part,
                    self.lse_part, stream=stream)
         if fused_tail:

@@ -132,6 +132,17 @@ def test_other_entry_points_reject_bad_arguments(lib):
     assert lib.mla_cache_append(d, cr, 3, FAKE, FAKE, FAKE, 100, FAKE, 64, None) == bd.MLA_ERR_INVALID_ARG
     assert lib.mla_cache_append(d, cr, 3, None, FAKE, FAKE, 512, FAKE, 64, None) == bd.MLA_ERR_INVALID_ARG
     assert lib.mla_cache_append(d, cr, 0, None, None, None, 0, None, 0, None) == 0
+    # the fused append + absorption checks both argument sets before anything is enqueued
+    aa = lib.mla_append_absorb_q
+    absorb_ok = (2, 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    append_ok = (3, FAKE, FAKE, FAKE, 512, FAKE, 64)
+    assert aa(d, cr, 3, FAKE, FAKE, FAKE, 100, FAKE, 64, *absorb_ok) == bd.MLA_ERR_INVALID_ARG
+    assert aa(d, cr, -1, FAKE, FAKE, FAKE, 512, FAKE, 64, *absorb_ok) == bd.MLA_ERR_INVALID_ARG
+    assert aa(d, None, *append_ok, *absorb_ok) == bd.MLA_ERR_INVALID_ARG
+    assert aa(d, cr, *append_ok, 2, 0, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == bd.MLA_ERR_INVALID_ARG
+    assert aa(d, cr, *append_ok, 2, 1, 5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == bd.MLA_ERR_INVALID_ARG
+    assert aa(d, cr, *append_ok, 2, 1, 1, FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == bd.MLA_ERR_INVALID_ARG
+    assert aa(d, cr, 0, None, None, None, 0, None, 0, 0, 1, 1, None, None, None, None, None, None, None) == 0
 
 
 def test_binding_refuses_host_tensors(lib):

@@ -312,3 +312,59 @@ def test_graph_replay_matches_eager():
             torch.cuda.synchronize()
             assert torch.equal(step.out, ref_o), (fused, rep)
             assert torch.equal(step.lse, ref_l), (fused, rep)
+
+
+@pytest.mark.parametrize("name,block_size,n_q", [("v3", 0, 1), ("v3", 64, 2), ("tiny", 0, 1)])
+def test_append_absorb_matches_separate_calls(name, block_size, n_q):
+    """mla_append_absorb_q writes the same cache rows, q_lat and q_pe, bit for
+    bit, as mla_cache_append followed by mla_absorb_q (one launch for the bf16
+    V3 shapes, two for the fp32 tiny shapes); the new rows' positional keys
+    are the oracle's rotation to bf16/fp32 resolution."""
+    _need_gpu()
+    import mla_latent_kv_02_amd as mla
+    from workloads.device import stage
+    if name == "tiny":
+        w = W.get("tiny_fp32")
+        st = stage(w)
+    else:
+        w = W.custom(name="append_absorb", seed=28, batch=5, n_q=n_q, ctx=None, ctx_range=(1, 1),
+                     block_size=block_size)
+        st = stage(w, ctx=np.array([130, 3, 64, 1000, 77], np.int32)[: w.batch])
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    ctx = st["ctx_host"]
+    # one new row per sequence, written over its last cached token
+    n = w.batch
+    g = torch.Generator().manual_seed(29)
+    raw = torch.randn(n, w.row, generator=g).to(tdt).cuda()
+    seq = torch.arange(n, dtype=torch.int32).cuda()
+    pos_host = (ctx - 1).astype(np.int32)
+    pos = torch.from_numpy(pos_host).cuda()
+    d = st["dims"]
+    outs = []
+    for fused in (False, True):
+        cache = mla.LatentCache(data=st["cache"].data.clone(), ctx_lens=st["cache"].ctx_lens,
+                                block_table=st["cache"].block_table, block_size=st["cache"].block_size)
+        q_lat = torch.full((w.batch, w.n_q, w.n_h, w.d_c), float("nan"), dtype=tdt, device="cuda")
+        q_pe = torch.full((w.batch, w.n_q, w.n_h, w.d_rope), float("nan"), dtype=tdt, device="cuda")
+        if fused:
+            mla.mla_append_absorb_q(d, cache, seq, pos, raw[:, :w.d_c], raw[:, w.d_c:], st["q_nope"],
+                                    st["q_rope"], st["positions"], st["w_uk"], q_lat, q_pe)
+        else:
+            mla.mla_cache_append(d, cache, seq, pos, raw[:, :w.d_c], raw[:, w.d_c:])
+            mla.mla_absorb_q(d, st["q_nope"], st["q_rope"], st["positions"], st["w_uk"], q_lat, q_pe)
+        torch.cuda.synchronize()
+        outs.append((cache, q_lat, q_pe))
+    bits = (lambda t: t.view(torch.int16)) if tdt == torch.bfloat16 else (lambda t: t.view(torch.int32))
+    for a, b in zip(outs[0], outs[1]):
+        ta, tb = (a.data, b.data) if isinstance(a, mla.LatentCache) else (a, b)
+        assert torch.equal(bits(ta), bits(tb))
+    cache = outs[1][0]
+    data = cache.data.float().cpu().numpy()
+    tbl = None if cache.block_table is None else cache.block_table.cpu().numpy()
+    raw_h = raw.float().cpu().numpy().astype(np.float64)
+    for b in range(n):
+        t = int(pos_host[b])
+        row = data[b, t] if tbl is None else data[tbl[b, t // w.block_size], t % w.block_size]
+        np.testing.assert_array_equal(row[: w.d_c], raw_h[b, : w.d_c])
+        ref = oracle.rope_rotate(raw_h[b : b + 1, w.d_c :], np.array([t]), w.rope_base)[0]
+        assert np.abs(row[w.d_c :] - ref).max() <= (2 ** -8 if tdt == torch.bfloat16 else 1e-6) * np.abs(ref).max()
