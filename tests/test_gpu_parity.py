@@ -142,6 +142,43 @@ def test_v3_paged_nan_poisoned(num_splits):
     _check(w, st, got)
 
 
+@pytest.mark.parametrize("block_size,num_splits", [(16, 1), (16, 5), (40, 1), (40, 4), (96, 3)])
+def test_v3_paged_block_sizes(block_size, num_splits):
+    """Blocks smaller than one 32-token stage (per-lane row addresses) and block
+    sizes that are not powers of two (a stage straddles two blocks at varying
+    offsets), NaN in every unused pool slot."""
+    _need_gpu()
+    from workloads.device import stage
+    w = W.custom(name=f"v3_paged_b{block_size}", seed=30 + block_size, batch=3, n_q=1, ctx=None,
+                 ctx_range=(1, 1), block_size=block_size)
+    st = stage(w, ctx=np.array([150, 17, 97], np.int32))
+    got = _run(st, num_splits)
+    _check(w, st, got)
+
+
+@pytest.mark.parametrize("num_splits", [1, 4])
+def test_v3_three_query_tokens_paged(num_splits):
+    """Three query tokens per sequence (three row groups, causal within the
+    triple) on a paged cache."""
+    _need_gpu()
+    from workloads.device import stage
+    w = W.custom(name="v3_nq3", seed=35, batch=2, n_q=3, ctx=None, ctx_range=(1, 1), block_size=64)
+    st = stage(w, ctx=np.array([131, 3], np.int32))
+    got = _run(st, num_splits)
+    _check(w, st, got)
+
+
+def test_fp32_paged_generic_path():
+    _need_gpu()
+    from workloads.device import stage
+    w = W.custom(name="f32_paged", seed=36, batch=2, n_q=2, n_h=4, d_c=64, d_rope=16, d_nope=32, d_v=32,
+                 dtype="f32", ctx=None, ctx_range=(1, 1), block_size=16)
+    st = stage(w, ctx=np.array([70, 2], np.int32))
+    for ns in (1, 5):
+        got = _run(st, ns)
+        _check(w, st, got)
+
+
 def test_generic_path_bf16_small_dims():
     _need_gpu()
     from workloads.device import stage
