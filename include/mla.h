@@ -8,6 +8,7 @@
  *             원리까지", Huny's Dev Blog.
  *   [Tbr8]    "DeepSeek MLA（多头潜在注意力）深度解析", tbr8.org.
  *   [Ikmyung] the attention / MHA / GQA / DeepSeek MLA guide, ikmyungterran.us.
+ *   [Paldyn]  "MQA와 GQA: KV 캐시 경량화 전략", ailab.paldyn.com.
  *
  * The step, per sequence b, query token j and head i:
  *   q_lat = q^C_i (W_i^UK)^T                     (key absorption, [Huny] §3.1)
@@ -48,7 +49,8 @@ typedef enum {
   MLA_OK = 0,
   MLA_ERR_INVALID_ARG = 1,
   MLA_ERR_UNSUPPORTED = 2,
-  MLA_ERR_HIP = 3
+  MLA_ERR_HIP = 3,
+  MLA_ERR_OUT_OF_BLOCKS = 4    /* block pool: not enough free blocks */
 } mla_status_t;
 
 typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype_t;
@@ -182,6 +184,30 @@ mla_status_t mla_append_absorb_q(const mla_dims_t *dims, const mla_cache_t *cach
                                  int64_t k_rope_stride, int32_t B, int32_t n_q, mla_dtype_t dt,
                                  const void *q_nope, const void *q_rope, const int32_t *positions,
                                  const void *w_uk, void *q_lat, void *q_pe, void *stream);
+
+/* ---- Block pool of a paged cache ([Paldyn], section "PagedAttention과 연속
+ * 배칭": blocks are taken as a sequence grows and handed back when it ends).
+ * Host-only functions (no GPU call) on HOST memory that the caller provides
+ * and owns: mla_block_pool_bytes() bytes, 4-byte aligned.  Block ids are
+ * handed out lowest first from a fresh pool; released blocks are reused
+ * first (last released, first taken).  The table (host, [B][max_blocks]
+ * int32, -1 past a sequence's blocks) is what the caller copies into the
+ * device block table of mla_cache_t.  Not thread-safe: one owner at a time. */
+int64_t mla_block_pool_bytes(int32_t n_blocks, int32_t B, int32_t max_blocks);   /* -1 if invalid */
+/* Set up an empty pool of n_blocks blocks of block_size tokens for B sequences
+ * of at most max_blocks blocks each. */
+mla_status_t mla_block_pool_init(void *pool, int64_t bytes, int32_t n_blocks, int32_t block_size,
+                                 int32_t B, int32_t max_blocks);
+/* Give sequence b blocks for n_tokens tokens in all (it never shrinks).
+ * MLA_ERR_OUT_OF_BLOCKS, with nothing taken, if the free blocks do not
+ * suffice; MLA_ERR_INVALID_ARG if it would need more than max_blocks. */
+mla_status_t mla_block_pool_reserve(void *pool, int32_t b, int32_t n_tokens);
+/* Return every block of sequence b to the pool; its table row becomes -1. */
+mla_status_t mla_block_pool_release(void *pool, int32_t b);
+/* The host block table inside the pool memory (NULL if pool is not one). */
+const int32_t *mla_block_pool_table(const void *pool);
+/* Number of free blocks (-1 if pool is not one). */
+int32_t mla_block_pool_free_count(const void *pool);
 
 /* Static description of a status code. */
 const char *mla_status_string(mla_status_t status);

@@ -6,6 +6,7 @@ the library; the first call does, and fails loudly if it is not built.
 """
 from ._binding import (  # noqa: F401
     BF16,
+    BlockPool,
     EXPORTED,
     F32,
     LIB_PATH,

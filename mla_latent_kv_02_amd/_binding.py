@@ -14,11 +14,13 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmla.so")
 
-MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP = 0, 1, 2, 3
+MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP, MLA_ERR_OUT_OF_BLOCKS = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 
 EXPORTED = ("mla_absorb_q", "mla_decode", "mla_combine", "mla_out_proj", "mla_combine_out_proj",
-            "mla_cache_append", "mla_append_absorb_q", "mla_num_partials", "mla_status_string", "mla_version")
+            "mla_cache_append", "mla_append_absorb_q", "mla_num_partials", "mla_status_string", "mla_version",
+            "mla_block_pool_bytes", "mla_block_pool_init", "mla_block_pool_reserve", "mla_block_pool_release",
+            "mla_block_pool_table", "mla_block_pool_free_count")
 
 
 class MlaError(RuntimeError):
@@ -66,6 +68,17 @@ def load_library(path: str = LIB_PATH):
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
+    for name, args in (("mla_block_pool_init", [P, I64, I32, I32, I32, I32]),
+                       ("mla_block_pool_reserve", [P, I32, I32]), ("mla_block_pool_release", [P, I32])):
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.mla_block_pool_bytes.argtypes = [I32, I32, I32]
+    lib.mla_block_pool_bytes.restype = ctypes.c_int64
+    lib.mla_block_pool_table.argtypes = [P]
+    lib.mla_block_pool_table.restype = ctypes.POINTER(ctypes.c_int32)
+    lib.mla_block_pool_free_count.argtypes = [P]
+    lib.mla_block_pool_free_count.restype = ctypes.c_int32
     lib.mla_num_partials.argtypes = [I32, I32]
     lib.mla_num_partials.restype = ctypes.c_int64
     lib.mla_status_string.argtypes = [ctypes.c_int]
@@ -306,3 +319,32 @@ def _append_checks(dims: Dims, cache: LatentCache, seq_ids, positions, c_kv_new,
     if c_kv_new.shape[1] != dims.d_c or k_rope_new.shape[1] != dims.d_rope:
         raise ValueError("c_kv_new / k_rope_new widths must be d_c / d_rope")
     return n
+
+
+class BlockPool:
+    """The library's block pool of a paged cache (mla_block_pool_*), in a host
+    buffer this object owns.  ``table`` is a NumPy view of the pool's host
+    block table [B][max_blocks] (-1 past a sequence's blocks)."""
+
+    def __init__(self, n_blocks: int, block_size: int, B: int, max_blocks: int):
+        import numpy as np
+        lib = load_library()
+        nbytes = lib.mla_block_pool_bytes(n_blocks, B, max_blocks)
+        if nbytes < 0:
+            raise ValueError("invalid block pool shape")
+        self._buf = np.zeros((nbytes + 3) // 4, dtype=np.int32)
+        self._ptr = self._buf.ctypes.data_as(ctypes.c_void_p)
+        _check("mla_block_pool_init", lib.mla_block_pool_init(self._ptr, nbytes, n_blocks, block_size, B,
+                                                              max_blocks))
+        self.n_blocks, self.block_size, self.B, self.max_blocks = n_blocks, block_size, B, max_blocks
+        self.table = np.ctypeslib.as_array(lib.mla_block_pool_table(self._ptr), shape=(B, max_blocks))
+
+    def reserve(self, b: int, n_tokens: int) -> None:
+        _check("mla_block_pool_reserve", load_library().mla_block_pool_reserve(self._ptr, b, n_tokens))
+
+    def release(self, b: int) -> None:
+        _check("mla_block_pool_release", load_library().mla_block_pool_release(self._ptr, b))
+
+    @property
+    def free_count(self) -> int:
+        return load_library().mla_block_pool_free_count(self._ptr)

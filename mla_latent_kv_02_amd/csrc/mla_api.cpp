@@ -94,6 +94,7 @@ const char* mla_status_string(mla_status_t s) {
     case MLA_ERR_INVALID_ARG: return "invalid argument";
     case MLA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case MLA_ERR_HIP: return "HIP launch error";
+    case MLA_ERR_OUT_OF_BLOCKS: return "block pool has too few free blocks";
   }
   return "unknown status";
 }

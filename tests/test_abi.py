@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    for code in range(4):
+    for code in range(5):
         assert lib.mla_status_string(code)
     assert b"unknown" in lib.mla_status_string(99)
     assert b"gfx950" in lib.mla_version()
