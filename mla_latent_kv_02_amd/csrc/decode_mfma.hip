@@ -121,21 +121,27 @@ enum Layout : int {
 // Contiguous caches use buffer loads: the resource (SGPRs) spans the
 // segment's rows of one sequence, so tokens past the segment end fall out of
 // range and read as zeros (never the cache's padding); each lane keeps one
-// 32-bit offset.  Paged and generic caches clamp such tokens to the last row
-// of the segment and use 64-bit per-lane addresses.
+// 32-bit offset.  Paged caches (block_size >= T) clamp such tokens to the last
+// row of the segment and also use buffer loads, from a resource that starts at
+// the lowest block of the segment (blk_lo); the caller takes this layout only
+// when every block of the segment lies within 4 GiB of that one (else the
+// generic layout).  The generic layout (any block size) uses 64-bit per-lane
+// addresses.
 template <int LAYOUT>
 struct StageLoader {
   const unsigned char* base;   // contiguous: first row of the sequence; else cache base
   __amdgpu_buffer_rsrc_t rsrc;
   const CacheView* c;
-  int b, tok_end;
+  int b, tok_end, blk_lo;
   int lane_off;                // contiguous: byte offset of the lane within a stage
   int tt, chunk_off;
 
-  __device__ __forceinline__ void init(const CacheView& cache, int b_, int tok_end_, int wave, int lane) {
+  __device__ __forceinline__ void init(const CacheView& cache, int b_, int tok_end_, int wave, int lane,
+                                       int blk_lo_) {
     c = &cache;
     b = b_;
     tok_end = tok_end_;
+    blk_lo = blk_lo_;
     tt = 8 * wave + (lane >> 3);
     chunk_off = ((lane & 7) ^ swz(tt)) * 16;
     base = static_cast<const unsigned char*>(cache.data);
@@ -144,6 +150,10 @@ struct StageLoader {
       rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(base), (short)0,
                                                tok_end * (ROW * 2), kBufferWord3);
       lane_off = tt * (ROW * 2) + chunk_off;
+    } else if (LAYOUT == kPaged) {
+      const int64_t block_bytes = (int64_t)cache.block_size * (ROW * 2);
+      rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(base + (int64_t)blk_lo * block_bytes),
+                                               (short)0, (int)0xFFFFFFFF, kBufferWord3);
     }
   }
 
@@ -158,25 +168,23 @@ struct StageLoader {
     }
     int tok = tok0 + tt;
     tok = tok < tok_end ? tok : tok_end - 1;   // rows past the segment repeat a valid row
-    int64_t off;   // elements
     if (LAYOUT == kPaged) {
       // the stage's tokens lie in at most two blocks: those of its first and last token
       const int bs = c->block_size;
       const int last = tok0 + T - 1 < tok_end - 1 ? tok0 + T - 1 : tok_end - 1;
       const int blk0 = block_id_scalar(*c, b, tok0);
       const int blk1 = block_id_scalar(*c, b, last);
-      const int r0 = tok0 % bs;
-      const int rel = r0 + (tok - tok0);
+      const int rel = tok0 % bs + (tok - tok0);
       const bool in0 = rel < bs;
-      off = ((int64_t)(in0 ? blk0 : blk1) * bs + (in0 ? rel : rel - bs)) * ROW;
-    } else {
-      off = cache_row_offset(*c, b, tok);
+      voff = (uint32_t)((in0 ? blk0 : blk1) - blk_lo) * (uint32_t)(bs * (ROW * 2)) +
+             (uint32_t)((in0 ? rel : rel - bs) * (ROW * 2) + chunk_off);
+      return;
     }
-    rowp = base + off * 2 + chunk_off;
+    rowp = base + cache_row_offset(*c, b, tok) * 2 + chunk_off;
   }
   __device__ __forceinline__ void issue_cg(int cg, unsigned char* buf, int wave) {
     unsigned char* dst = buf + wave * 1024 + cg * CG_BYTES;
-    if (LAYOUT == kContiguous)
+    if (LAYOUT == kContiguous || LAYOUT == kPaged)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, (int)voff, cg * 128, 0, 0);
     else
       __builtin_amdgcn_global_load_lds(rowp + cg * 128, (lds_void*)dst, 16, 0, 0);
@@ -187,6 +195,31 @@ struct StageLoader {
     for (int cg = 0; cg < CGROUPS; ++cg) issue_cg(cg, buf, wave);
   }
 };
+
+// Paged cache, tokens t0..t1-1 of sequence b: the lowest block id among their
+// blocks, and whether all of them lie within 4 GiB of it (so that 32-bit
+// buffer offsets from it reach every row).  Each wave reads the block table
+// entries itself and reduces them across its lanes; the result is the same in
+// every wave.
+__device__ __forceinline__ bool paged_span(const CacheView& c, int b, int t0, int t1, int lane, int* blk_lo) {
+  const int bs = c.block_size;
+  const int k0 = t0 / bs, k1 = (t1 - 1) / bs;
+  int lo = INT_MAX, hi = INT_MIN;
+  for (int k = k0 + lane; k <= k1; k += 64) {
+    const int id = c.block_table[(int64_t)b * c.max_blocks + k];
+    lo = id < lo ? id : lo;
+    hi = id > hi ? id : hi;
+  }
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) {
+    const int ol = __shfl_xor(lo, sh, 64), oh = __shfl_xor(hi, sh, 64);
+    lo = ol < lo ? ol : lo;
+    hi = oh > hi ? oh : hi;
+  }
+  *blk_lo = __builtin_amdgcn_readfirstlane(lo);
+  const int64_t span = ((int64_t)__builtin_amdgcn_readfirstlane(hi) - *blk_lo + 1) * bs * (ROW * 2);
+  return span <= (int64_t)0xFFFFFFFF;
+}
 
 // Workgroup barrier that waits only for this wave's LDS operations (a
 // __syncthreads() would also wait for every outstanding global load and so
@@ -272,8 +305,10 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
   const bool active = row0 < rows;
   const int jq = active ? row0 / a.n_h : 0;   // query token of this wave's QK rows
 
-  for_each_segment<NT>(a.ctx_lens, a.B, a.num_splits, w, &sm->plan,
-                       [&](int b, int t0, int t1, int slot) {
+  // one segment (tokens t0..t1-1 of sequence b, partial slot `slot`), its cache
+  // rows read through the stage loader of layout SL
+  auto segment = [&](auto layout_tag, int b, int t0, int t1, int slot, int blk_lo) {
+    constexpr int SL = decltype(layout_tag)::value;
     // ---- query operand (B of QK^T): row row0 + l32, k = 16*ks + 8*h .. +8
     bf16x8 qreg[KSTEPS];
     int limit = t1;
@@ -291,8 +326,8 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
     // The query loads are not waited for here: the first stages' loads are
     // issued behind them, and the wait for stage 0 (vector-memory counter,
     // completed in order) covers them too.
-    StageLoader<LAYOUT> ld;
-    ld.init(a.cache, b, t1, wave, lane);
+    StageLoader<SL> ld;
+    ld.init(a.cache, b, t1, wave, lane, blk_lo);
     // per-lane LDS byte offsets that do not depend on the stage
     const int sw_qk = swz(l32);
     int qk_off[4];
@@ -566,6 +601,20 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
     }
     // (the segment walker's barrier after this call keeps the ring and the
     // exchange buffers until every wave is done with them)
+  };
+  using Contig = std::integral_constant<int, kContiguous>;
+  using Paged = std::integral_constant<int, kPaged>;
+  using Any = std::integral_constant<int, kAnyLayout>;
+  for_each_segment<NT>(a.ctx_lens, a.B, a.num_splits, w, &sm->plan, [&](int b, int t0, int t1, int slot) {
+    if constexpr (LAYOUT == kContiguous) {
+      segment(Contig{}, b, t0, t1, slot, 0);
+    } else if constexpr (LAYOUT == kPaged) {
+      int blk_lo;
+      if (paged_span(a.cache, b, t0, t1, lane, &blk_lo)) segment(Paged{}, b, t0, t1, slot, blk_lo);
+      else segment(Any{}, b, t0, t1, slot, 0);    // blocks 4 GiB or more apart
+    } else {
+      segment(Any{}, b, t0, t1, slot, 0);
+    }
   });
 }
 

@@ -156,6 +156,35 @@ def test_v3_paged_block_sizes(block_size, num_splits):
     _check(w, st, got)
 
 
+def test_v3_paged_pool_over_4gib():
+    """A 4.4 GB pool (60000 blocks of 64 tokens): sequence 0's blocks sit at both
+    ends of the pool, more than 4 GiB apart (its segments take 64-bit row
+    addresses), sequence 1's are neighbours (32-bit buffer offsets from its
+    lowest block), both in one launch."""
+    _need_gpu()
+    import mla_latent_kv_02_amd as mla
+    from workloads.device import stage
+    w = W.custom(name="v3_bigpool", seed=37, batch=2, n_q=1, ctx=None, ctx_range=(1, 1), block_size=64)
+    st = stage(w, ctx=np.array([200, 100], np.int32))
+    n_blocks = 60000
+    assert n_blocks * 64 * w.row * 2 > 2 ** 32
+    big = torch.empty((n_blocks, 64, w.row), dtype=torch.bfloat16, device="cuda")
+    old = st["block_table_host"]
+    new = np.full_like(old, -1)
+    new[0, :4] = [0, n_blocks - 1, 1, n_blocks - 2]
+    new[1, :2] = [30000, 30001]
+    for b, nb in ((0, 4), (1, 2)):
+        for k in range(nb):
+            big[int(new[b, k])] = st["cache"].data[int(old[b, k])]
+    st = dict(st, cache=mla.LatentCache(data=big, ctx_lens=st["cache"].ctx_lens,
+                                        block_table=torch.from_numpy(new).cuda(), block_size=64))
+    for ns in (1, 3):
+        got = _run(st, ns)
+        _check(w, st, got)
+    del big
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("num_splits", [1, 4])
 def test_v3_three_query_tokens_paged(num_splits):
     """Three query tokens per sequence (three row groups, causal within the
