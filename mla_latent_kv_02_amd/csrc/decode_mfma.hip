@@ -91,21 +91,6 @@ struct __attribute__((aligned(16))) DecodeSmem {
   PlanScratch<NT> plan;
 };
 
-// Block id of the paged cache for token `tok` of sequence b, read with a
-// scalar load (the index is wave-uniform).  Scalar loads are counted by
-// lgkmcnt, so waiting for them does not drain the vector-memory queue that
-// holds the in-flight stage loads.
-__device__ __forceinline__ int block_id_scalar(const CacheView& c, int b, int tok) {
-  const int32_t* p = c.block_table + (int64_t)b * c.max_blocks + tok / c.block_size;
-  // readfirstlane returns a signed int: widen through uint32_t (zero-extend)
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)p);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uintptr_t)p >> 32));
-  const uint64_t addr = (uint64_t)lo | ((uint64_t)hi << 32);
-  int v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(addr) : "memory");
-  return v;
-}
-
 // Cache layouts the kernel is compiled for.
 enum Layout : int {
   kContiguous = 0,   // [B][seq_stride] rows; a sequence's rows (plus one stage) span < 4 GiB
@@ -135,6 +120,10 @@ struct StageLoader {
   int b, tok_end, blk_lo;
   int lane_off;                // contiguous: byte offset of the lane within a stage
   int tt, chunk_off;
+  int lane_;
+  int ids, kbase;              // paged: lane l holds the id of block kbase + l of the sequence
+  int ntok, nk, nr;            // paged: the next stage's first token, its block index and row in it
+  uint32_t block_bytes;
 
   __device__ __forceinline__ void init(const CacheView& cache, int b_, int tok_end_, int wave, int lane,
                                        int blk_lo_) {
@@ -142,6 +131,11 @@ struct StageLoader {
     b = b_;
     tok_end = tok_end_;
     blk_lo = blk_lo_;
+    lane_ = lane;
+    kbase = INT_MIN / 2;         // no window loaded yet
+    ids = 0;
+    ntok = INT_MIN;              // next stage unknown
+    nk = nr = 0;
     tt = 8 * wave + (lane >> 3);
     chunk_off = ((lane & 7) ^ swz(tt)) * 16;
     base = static_cast<const unsigned char*>(cache.data);
@@ -151,9 +145,10 @@ struct StageLoader {
                                                tok_end * (ROW * 2), kBufferWord3);
       lane_off = tt * (ROW * 2) + chunk_off;
     } else if (LAYOUT == kPaged) {
-      const int64_t block_bytes = (int64_t)cache.block_size * (ROW * 2);
-      rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(base + (int64_t)blk_lo * block_bytes),
-                                               (short)0, (int)0xFFFFFFFF, kBufferWord3);
+      block_bytes = (uint32_t)cache.block_size * (ROW * 2);
+      rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<unsigned char*>(base + (int64_t)blk_lo * block_bytes), (short)0, (int)0xFFFFFFFF, kBufferWord3);
+      lane_off = tt * (ROW * 2) + chunk_off;
     }
   }
 
@@ -166,20 +161,45 @@ struct StageLoader {
       voff = (uint32_t)lane_off + (uint32_t)tok0 * (uint32_t)(ROW * 2);
       return;
     }
-    int tok = tok0 + tt;
-    tok = tok < tok_end ? tok : tok_end - 1;   // rows past the segment repeat a valid row
     if (LAYOUT == kPaged) {
-      // the stage's tokens lie in at most two blocks: those of its first and last token
+      // The stage's tokens lie in at most two blocks, k0 (from row r0 on) and
+      // k1.  Stages come in order, 32 tokens apart, so (k0, r0) follows from
+      // the previous stage without a division (a restart recomputes it).  The
+      // block ids come from the window of 64 ids in `ids`, reloaded (one
+      // vector load; its wait also covers the stage loads in flight) when the
+      // stage leaves it.  Rows past the segment end repeat its last row.
       const int bs = c->block_size;
-      const int last = tok0 + T - 1 < tok_end - 1 ? tok0 + T - 1 : tok_end - 1;
-      const int blk0 = block_id_scalar(*c, b, tok0);
-      const int blk1 = block_id_scalar(*c, b, last);
-      const int rel = tok0 % bs + (tok - tok0);
-      const bool in0 = rel < bs;
-      voff = (uint32_t)((in0 ? blk0 : blk1) - blk_lo) * (uint32_t)(bs * (ROW * 2)) +
-             (uint32_t)((in0 ? rel : rel - bs) * (ROW * 2) + chunk_off);
+      if (tok0 != ntok) {
+        nk = tok0 / bs;
+        nr = tok0 - nk * bs;
+      }
+      const int k0 = nk, r0 = nr;
+      const int span = T - 1 < tok_end - 1 - tok0 ? T - 1 : tok_end - 1 - tok0;   // last row, from tok0
+      const int k1 = k0 + (r0 + span >= bs ? 1 : 0);
+      ntok = tok0 + T;
+      nr = r0 + T;
+      if (nr >= bs) {   // block_size >= T: at most one block boundary per stage
+        nr -= bs;
+        ++nk;
+      }
+      if (k0 < kbase || k1 - kbase >= 64) {
+        kbase = k0;
+        const int k = k0 + lane_;
+        ids = k <= (tok_end - 1) / bs ? c->block_table[(int64_t)b * c->max_blocks + k] : 0;
+      }
+      const int blk0 = __builtin_amdgcn_readlane(ids, k0 - kbase);
+      const int blk1 = __builtin_amdgcn_readlane(ids, k1 - kbase);
+      // byte offsets from the resource base: row r0 + t of block k0 for t < bs - r0,
+      // else row t - (bs - r0) of block k1 (uint32 arithmetic, exact modulo 2^32)
+      const uint32_t off0 = (uint32_t)(blk0 - blk_lo) * block_bytes + (uint32_t)r0 * (ROW * 2);
+      const uint32_t off1 = (uint32_t)(blk1 - blk_lo) * block_bytes - (uint32_t)(bs - r0) * (ROW * 2);
+      const int t = tt < span ? tt : span;
+      const uint32_t lo = tt < span ? (uint32_t)lane_off : (uint32_t)(span * (ROW * 2) + chunk_off);
+      voff = lo + (r0 + t < bs ? off0 : off1);
       return;
     }
+    int tok = tok0 + tt;
+    tok = tok < tok_end ? tok : tok_end - 1;   // rows past the segment repeat a valid row
     rowp = base + cache_row_offset(*c, b, tok) * 2 + chunk_off;
   }
   __device__ __forceinline__ void issue_cg(int cg, unsigned char* buf, int wave) {
@@ -526,8 +546,8 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
       auto iteration = [&](int it, auto visible_tag) {
         constexpr bool VISIBLE = decltype(visible_tag)::value;
         const bool has_next = it + 1 < nst;
-        // addresses of stage it+3 first: a paged cache looks its block ids up
-        // with scalar loads, whose wait then merges with the barrier's
+        // addresses of stage it+3 first, ahead of the waits (a paged cache takes
+        // its block ids from the register window, reloaded now and then)
         const bool do_load = it + NSTAGE - 1 < nst;
         if (do_load) ld.prepare(t0 + (it + NSTAGE - 1) * T);
         if (has_next) wait_stages_in_flight(it + 2 < nst ? 1 : 0);   // stage it+1 resident
