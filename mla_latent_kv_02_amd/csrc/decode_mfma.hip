@@ -42,7 +42,8 @@
 // combine normalises (exact for any reference).
 //
 // Split-KV: the workgroup walks the segments of its work unit (see
-// for_each_segment) and writes one normalised partial (u, lse) per segment.
+// for_each_segment) and writes one partial per segment: u unnormalised, with
+// its reference and log-sum-exp (the format mla.h states for mla_decode).
 
 #include <climits>
 #include <type_traits>
@@ -76,7 +77,7 @@ struct DecodeArgs {
   const int32_t* ctx_lens;
   const int32_t* positions;  // [B][n_q]
   float* u_part;           // [slots][n_q][n_h][512]
-  float* lse_part;         // [slots][n_q][n_h]
+  float* lse_part;         // [slots][n_q][n_h][2]: (reference, log-sum-exp)
   int B, n_q, n_h, num_splits, n_groups, n_work_pad;
   float scale_log2;        // sm_scale * log2(e)
 };
@@ -278,8 +279,7 @@ static_assert(LOADS_PER_STAGE == 9 && NSTAGE == 4, "wait counts assume 9 loads p
 // Work split inside a workgroup of 4 waves serving 128 query rows:
 //   QK^T and softmax: wave w owns rows 32w .. 32w+31 (its heads' queries stay in
 //     registers as the MFMA B operand); per stage it computes one 32-token x
-//     32-row block S^T with 32x32x16 MFMAs (two accumulation chains over
-//     alternate k-steps).  Lane l holds row l%32 and tokens
+//     32-row block S^T with one chain of 36 32x32x16 MFMAs.  Lane l holds row l%32 and tokens
 //     8*(i/4) + 4*(l/32) + i%4 (i < 16) of the block.
 //   PV: wave w owns latent columns 128w .. 128w+127 for all 128 rows (4 x 4
 //     blocks of 32x32), so each V element is read from LDS once per workgroup.
