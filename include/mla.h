@@ -185,6 +185,41 @@ mla_status_t mla_append_absorb_q(const mla_dims_t *dims, const mla_cache_t *cach
                                  const void *q_nope, const void *q_rope, const int32_t *positions,
                                  const void *w_uk, void *q_lat, void *q_pe, void *stream);
 
+/* ---- Weight folds ([Huny] §3.2, "Value 투영과 Output 투영의 결합 행렬 흡수":
+ * W_i,comb = W_i^UV W_i^O is formed offline and the layer output is one
+ * product with it; [Paldyn], section "MLA": the matrix that expands the keys
+ * can be multiplied into the query projection the same way).  All operands
+ * bf16, fp32 accumulation; arrays 16-byte aligned; MLA_ERR_UNSUPPORTED when
+ * d_v, d_nope, d_q or n_h * d_c (the contraction lengths) are not multiples
+ * of 16.  The folded matrices are stored with their contraction index
+ * innermost, the layout the per-step products read.
+ *
+ * W^O enters as a linear layer's weight: w_o [d_model][n_h][d_v], i.e.
+ * w_o[n][i][v] = (W_i^O)[v][n] with W_i^O the d_v x d_model block of head i. */
+/* w_comb [d_model][n_h][d_c], out: w_comb[n][i][c] = (W_i^UV W_i^O)[c][n]. */
+mla_status_t mla_fold_out(const mla_dims_t *dims, int32_t d_model, const void *w_uv, const void *w_o,
+                          void *w_comb, void *stream);
+/* Layer output through the fold: y[b][j][:] = sum_i u[b][j][i][:] W_i,comb.
+ *   u [B][n_q][n_h][d_c] fp32 (split into bf16 high + residual, ~fp32 accuracy),
+ *   y [B][n_q][d_model] fp32, out. */
+mla_status_t mla_out_proj_folded(const mla_dims_t *dims, int32_t d_model, int32_t B, int32_t n_q,
+                                 const float *u, const void *w_comb, float *y, void *stream);
+/* The same layer output without the fold: y[b][j][:] = sum_i o[b][j][i][:] W_i^O,
+ *   o [B][n_q][n_h][d_v] fp32 (mla_out_proj's output), y [B][n_q][d_model] fp32. */
+mla_status_t mla_o_proj(const mla_dims_t *dims, int32_t d_model, int32_t B, int32_t n_q, const float *o,
+                        const void *w_o, float *y, void *stream);
+/* Query fold: q^C_i = c_q W_i^UQ with c_q the d_q-wide compressed query and
+ *   w_uq [d_q][n_h][d_nope] (W^UQ, head i's columns at [.][i][.]);
+ *   w_kq [n_h][d_c][d_q], out: w_kq[i][c][q] = (W_i^UQ (W_i^UK)^T)[q][c]. */
+mla_status_t mla_fold_q(const mla_dims_t *dims, int32_t d_q, const void *w_uq, const void *w_uk, void *w_kq,
+                        void *stream);
+/* mla_absorb_q from the compressed query through the fold:
+ *   q_lat[b][j][i][:] = c_q[b][j][:] W_i^UQ (W_i^UK)^T,  q_pe = RoPE(q_rope) as in mla_absorb_q.
+ *   c_q [B][n_q][d_q] bf16; q_rope, positions, q_lat, q_pe as for mla_absorb_q (bf16). */
+mla_status_t mla_absorb_q_folded(const mla_dims_t *dims, int32_t d_q, int32_t B, int32_t n_q, const void *c_q,
+                                 const void *q_rope, const int32_t *positions, const void *w_kq, void *q_lat,
+                                 void *q_pe, void *stream);
+
 /* ---- Block pool of a paged cache ([Paldyn], section "PagedAttention과 연속
  * 배칭": blocks are taken as a sequence grows and handed back when it ends).
  * Host-only functions (no GPU call) on HOST memory that the caller provides
@@ -202,6 +237,11 @@ mla_status_t mla_block_pool_init(void *pool, int64_t bytes, int32_t n_blocks, in
  * MLA_ERR_OUT_OF_BLOCKS, with nothing taken, if the free blocks do not
  * suffice; MLA_ERR_INVALID_ARG if it would need more than max_blocks. */
 mla_status_t mla_block_pool_reserve(void *pool, int32_t b, int32_t n_tokens);
+/* mla_block_pool_reserve(pool, b, n_tokens[b]) for every sequence b with
+ * n_tokens[b] >= 0 (host array of B entries), all or nothing: if the free
+ * blocks do not cover every request, MLA_ERR_OUT_OF_BLOCKS and nothing is
+ * taken. */
+mla_status_t mla_block_pool_reserve_all(void *pool, const int32_t *n_tokens);
 /* Return every block of sequence b to the pool; its table row becomes -1. */
 mla_status_t mla_block_pool_release(void *pool, int32_t b);
 /* The host block table inside the pool memory (NULL if pool is not one). */

@@ -22,6 +22,11 @@ from ._binding import (  # noqa: F401
     mla_num_partials,
     mla_out_proj,
     mla_combine_out_proj,
+    mla_fold_out,
+    mla_out_proj_folded,
+    mla_o_proj,
+    mla_fold_q,
+    mla_absorb_q_folded,
 )
 
 __version__ = "0.1.0"

@@ -19,7 +19,9 @@ F32, BF16 = 0, 1
 
 EXPORTED = ("mla_absorb_q", "mla_decode", "mla_combine", "mla_out_proj", "mla_combine_out_proj",
             "mla_cache_append", "mla_append_absorb_q", "mla_num_partials", "mla_status_string", "mla_version",
-            "mla_block_pool_bytes", "mla_block_pool_init", "mla_block_pool_reserve", "mla_block_pool_release",
+            "mla_block_pool_bytes", "mla_block_pool_init", "mla_block_pool_reserve", "mla_block_pool_reserve_all",
+            "mla_block_pool_release", "mla_fold_out", "mla_out_proj_folded", "mla_o_proj", "mla_fold_q",
+            "mla_absorb_q_folded",
             "mla_block_pool_table", "mla_block_pool_free_count")
 
 
@@ -63,13 +65,19 @@ def load_library(path: str = LIB_PATH):
         "mla_combine_out_proj": [DP, I32, I32, P, I32, P, P, ctypes.c_int, P, P, P, V],
         "mla_cache_append": [DP, CP, I32, P, P, P, I64, P, I64, V],
         "mla_append_absorb_q": [DP, CP, I32, P, P, P, I64, P, I64, I32, I32, ctypes.c_int, P, P, P, P, P, P, V],
+        "mla_fold_out": [DP, I32, P, P, P, V],
+        "mla_out_proj_folded": [DP, I32, I32, I32, P, P, P, V],
+        "mla_o_proj": [DP, I32, I32, I32, P, P, P, V],
+        "mla_fold_q": [DP, I32, P, P, P, V],
+        "mla_absorb_q_folded": [DP, I32, I32, I32, P, P, P, P, P, P, V],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
     for name, args in (("mla_block_pool_init", [P, I64, I32, I32, I32, I32]),
-                       ("mla_block_pool_reserve", [P, I32, I32]), ("mla_block_pool_release", [P, I32])):
+                       ("mla_block_pool_reserve", [P, I32, I32]), ("mla_block_pool_reserve_all", [P, P]),
+                       ("mla_block_pool_release", [P, I32])):
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
@@ -342,9 +350,93 @@ class BlockPool:
     def reserve(self, b: int, n_tokens: int) -> None:
         _check("mla_block_pool_reserve", load_library().mla_block_pool_reserve(self._ptr, b, n_tokens))
 
+    def reserve_all(self, n_tokens) -> None:
+        """n_tokens: int32 array of B entries (negative = leave that sequence)."""
+        import numpy as np
+        n = np.ascontiguousarray(n_tokens, dtype=np.int32)
+        if n.shape != (self.B,):
+            raise ValueError(f"n_tokens must have {self.B} entries")
+        _check("mla_block_pool_reserve_all", load_library().mla_block_pool_reserve_all(
+            self._ptr, n.ctypes.data_as(ctypes.c_void_p)))
+
     def release(self, b: int) -> None:
         _check("mla_block_pool_release", load_library().mla_block_pool_release(self._ptr, b))
 
     @property
     def free_count(self) -> int:
         return load_library().mla_block_pool_free_count(self._ptr)
+
+
+# ---- weight folds (mla_fold_out / mla_out_proj_folded / mla_o_proj / mla_fold_q / mla_absorb_q_folded)
+
+def _bf16_dev(t, name, shape):
+    torch = _torch()
+    _dev(t, name, torch.bfloat16)
+    _shape(t, name, shape)
+
+
+def mla_fold_out(dims: Dims, w_uv, w_o, w_comb, stream=None) -> None:
+    """w_uv [n_h][d_c][d_v], w_o [d_model][n_h][d_v] -> w_comb [d_model][n_h][d_c] (all bf16)."""
+    d_model = w_o.shape[0]
+    _bf16_dev(w_uv, "w_uv", (dims.n_h, dims.d_c, dims.d_v))
+    _bf16_dev(w_o, "w_o", (d_model, dims.n_h, dims.d_v))
+    _bf16_dev(w_comb, "w_comb", (d_model, dims.n_h, dims.d_c))
+    d = dims._c()
+    _check("mla_fold_out", load_library().mla_fold_out(ctypes.byref(d), d_model, w_uv.data_ptr(), w_o.data_ptr(),
+                                                       w_comb.data_ptr(), _stream(stream)))
+
+
+def mla_out_proj_folded(dims: Dims, u, w_comb, y, stream=None) -> None:
+    """u [B][n_q][n_h][d_c] fp32, w_comb [d_model][n_h][d_c] bf16 -> y [B][n_q][d_model] fp32."""
+    torch = _torch()
+    B, n_q, d_model = u.shape[0], u.shape[1], w_comb.shape[0]
+    _dev(u, "u", torch.float32)
+    _shape(u, "u", (B, n_q, dims.n_h, dims.d_c))
+    _bf16_dev(w_comb, "w_comb", (d_model, dims.n_h, dims.d_c))
+    _dev(y, "y", torch.float32)
+    _shape(y, "y", (B, n_q, d_model))
+    d = dims._c()
+    _check("mla_out_proj_folded", load_library().mla_out_proj_folded(
+        ctypes.byref(d), d_model, B, n_q, u.data_ptr(), w_comb.data_ptr(), y.data_ptr(), _stream(stream)))
+
+
+def mla_o_proj(dims: Dims, o, w_o, y, stream=None) -> None:
+    """o [B][n_q][n_h][d_v] fp32, w_o [d_model][n_h][d_v] bf16 -> y [B][n_q][d_model] fp32."""
+    torch = _torch()
+    B, n_q, d_model = o.shape[0], o.shape[1], w_o.shape[0]
+    _dev(o, "o", torch.float32)
+    _shape(o, "o", (B, n_q, dims.n_h, dims.d_v))
+    _bf16_dev(w_o, "w_o", (d_model, dims.n_h, dims.d_v))
+    _dev(y, "y", torch.float32)
+    _shape(y, "y", (B, n_q, d_model))
+    d = dims._c()
+    _check("mla_o_proj", load_library().mla_o_proj(ctypes.byref(d), d_model, B, n_q, o.data_ptr(), w_o.data_ptr(),
+                                                   y.data_ptr(), _stream(stream)))
+
+
+def mla_fold_q(dims: Dims, w_uq, w_uk, w_kq, stream=None) -> None:
+    """w_uq [d_q][n_h][d_nope], w_uk [n_h][d_c][d_nope] -> w_kq [n_h][d_c][d_q] (all bf16)."""
+    d_q = w_uq.shape[0]
+    _bf16_dev(w_uq, "w_uq", (d_q, dims.n_h, dims.d_nope))
+    _bf16_dev(w_uk, "w_uk", (dims.n_h, dims.d_c, dims.d_nope))
+    _bf16_dev(w_kq, "w_kq", (dims.n_h, dims.d_c, d_q))
+    d = dims._c()
+    _check("mla_fold_q", load_library().mla_fold_q(ctypes.byref(d), d_q, w_uq.data_ptr(), w_uk.data_ptr(),
+                                                   w_kq.data_ptr(), _stream(stream)))
+
+
+def mla_absorb_q_folded(dims: Dims, c_q, q_rope, positions, w_kq, q_lat, q_pe, stream=None) -> None:
+    """c_q [B][n_q][d_q], w_kq [n_h][d_c][d_q] -> q_lat [B][n_q][n_h][d_c]; q_pe = RoPE(q_rope) (bf16)."""
+    torch = _torch()
+    B, n_q, d_q = c_q.shape
+    _bf16_dev(c_q, "c_q", (B, n_q, d_q))
+    _bf16_dev(q_rope, "q_rope", (B, n_q, dims.n_h, dims.d_rope))
+    _dev(positions, "positions", torch.int32)
+    _shape(positions, "positions", (B, n_q))
+    _bf16_dev(w_kq, "w_kq", (dims.n_h, dims.d_c, d_q))
+    _bf16_dev(q_lat, "q_lat", (B, n_q, dims.n_h, dims.d_c))
+    _bf16_dev(q_pe, "q_pe", (B, n_q, dims.n_h, dims.d_rope))
+    d = dims._c()
+    _check("mla_absorb_q_folded", load_library().mla_absorb_q_folded(
+        ctypes.byref(d), d_q, B, n_q, c_q.data_ptr(), q_rope.data_ptr(), positions.data_ptr(), w_kq.data_ptr(),
+        q_lat.data_ptr(), q_pe.data_ptr(), _stream(stream)))

@@ -35,7 +35,7 @@ EXTRA_FLAGS = {"proj_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 
 SOURCES = ["mla_api.cpp", "decode_mfma.hip", "decode_generic.hip", "combine.hip",
            "absorb.hip", "out_proj.hip", "cache_append.hip", "proj_mfma.hip", "tail_mfma.hip",
-           "block_pool.cpp"]
+           "block_pool.cpp", "gemm_nt.hip"]
 
 
 def _hipcc() -> str:

@@ -80,6 +80,22 @@ mla_status_t mla_block_pool_reserve(void* pool, int32_t b, int32_t n_tokens) {
   return MLA_OK;
 }
 
+mla_status_t mla_block_pool_reserve_all(void* pool, const int32_t* n_tokens) {
+  View v;
+  if (!view_of(pool, &v) || !n_tokens) return MLA_ERR_INVALID_ARG;
+  int64_t extra = 0;
+  for (int32_t b = 0; b < v.B(); ++b) {
+    if (n_tokens[b] < 0) continue;
+    const int64_t need = ((int64_t)n_tokens[b] + v.block_size() - 1) / v.block_size();
+    if (need > v.max_blocks()) return MLA_ERR_INVALID_ARG;
+    if (need > v.held()[b]) extra += need - v.held()[b];
+  }
+  if (extra > v.n_free()) return MLA_ERR_OUT_OF_BLOCKS;   // nothing taken
+  for (int32_t b = 0; b < v.B(); ++b)
+    if (n_tokens[b] >= 0) mla_block_pool_reserve(pool, b, n_tokens[b]);
+  return MLA_OK;
+}
+
 mla_status_t mla_block_pool_release(void* pool, int32_t b) {
   View v;
   if (!view_of(pool, &v) || b < 0 || b >= v.B()) return MLA_ERR_INVALID_ARG;

@@ -52,6 +52,8 @@ struct AbsorbParams {
 hipError_t launch_absorb(const AbsorbParams& p, hipStream_t stream);
 bool absorb_mfma_ok(const AbsorbParams& p);
 hipError_t launch_absorb_mfma(const AbsorbParams& p, hipStream_t stream);
+// q_pe = RoPE(q_rope) alone (fp64 angles), fp32 or bf16.
+hipError_t launch_rope_q(const AbsorbParams& p, hipStream_t stream);
 
 struct OutProjParams {
   const float* u;
@@ -97,5 +99,21 @@ hipError_t launch_cache_append(const AppendParams& p, hipStream_t stream);
 // mla_cache_append then the bf16 MFMA absorption, in one launch where the
 // absorption takes its one-pass kernel and the cache is bf16 (ap may be null).
 hipError_t launch_append_absorb_mfma(const AbsorbParams& p, const AppendParams* ap, hipStream_t stream);
+
+// C[z][m][n] = sum_k A[z][m][k] B[z][n][k] (k contiguous in both operands).
+// A: fp32 (a_f32) or bf16; B: bf16; C: bf16 (c_bf16) or fp32.  Strides in
+// elements; requires K % 16 == 0, lda and ldb multiples of 8 and 16-byte
+// aligned rows.
+struct GemmNT {
+  const void* A;
+  int64_t lda, strideA;
+  const uint16_t* B;
+  int64_t ldb, strideB;
+  void* C;
+  int64_t ldc, strideC;
+  int M, N, K, batch;
+  bool a_f32, c_bf16;
+};
+hipError_t launch_gemm_nt(const GemmNT& g, hipStream_t stream);
 
 }  // namespace mla

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <climits>
 
 #include "../../include/mla.h"
 #include "launch.h"
@@ -214,6 +215,91 @@ mla_status_t mla_append_absorb_q(const mla_dims_t* dims, const mla_cache_t* cach
     if (st != MLA_OK) return st;
   }
   return p.B > 0 ? launch_absorb_any(p, s) : MLA_OK;
+}
+
+// ---- weight folds and the products that use them
+namespace {
+bool al16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+// the launch grid of a product: (N/32, M/64, batch) blocks
+mla_status_t run_gemm(const mla::GemmNT& g, void* stream) {
+  if ((g.M + 63) / 64 > 65535 || g.batch > 65535) return MLA_ERR_UNSUPPORTED;
+  return from_hip(mla::launch_gemm_nt(g, (hipStream_t)stream));
+}
+mla::GemmNT gemm(const void* A, int64_t lda, int64_t sA, const void* B, int64_t ldb, int64_t sB, void* C,
+                 int64_t ldc, int64_t sC, int M, int N, int K, int batch, bool a_f32, bool c_bf16) {
+  mla::GemmNT g;
+  g.A = A; g.lda = lda; g.strideA = sA;
+  g.B = static_cast<const uint16_t*>(B); g.ldb = ldb; g.strideB = sB;
+  g.C = C; g.ldc = ldc; g.strideC = sC;
+  g.M = M; g.N = N; g.K = K; g.batch = batch; g.a_f32 = a_f32; g.c_bf16 = c_bf16;
+  return g;
+}
+}  // namespace
+
+mla_status_t mla_fold_out(const mla_dims_t* dims, int32_t d_model, const void* w_uv, const void* w_o,
+                          void* w_comb, void* stream) {
+  if (!dims_ok(dims) || d_model < 1 || !w_uv || !w_o || !w_comb) return MLA_ERR_INVALID_ARG;
+  const int n_h = dims->n_h, d_c = dims->d_c, d_v = dims->d_v;
+  if (d_v % 16 || !al16(w_uv) || !al16(w_o) || !al16(w_comb) || (int64_t)d_model * n_h * d_c > (1LL << 40))
+    return MLA_ERR_UNSUPPORTED;
+  // z = head i: C[n][c] = sum_v w_o[n][i][v] w_uv[i][c][v], written to w_comb[n][i][c]
+  return run_gemm(
+      gemm(w_o, (int64_t)n_h * d_v, d_v, w_uv, d_v, (int64_t)d_c * d_v, w_comb, (int64_t)n_h * d_c, d_c, d_model,
+           d_c, d_v, n_h, false, true), stream);
+}
+
+mla_status_t mla_out_proj_folded(const mla_dims_t* dims, int32_t d_model, int32_t B, int32_t n_q, const float* u,
+                                 const void* w_comb, float* y, void* stream) {
+  if (!dims_ok(dims) || d_model < 1 || B < 0 || n_q < 1) return MLA_ERR_INVALID_ARG;
+  if (B == 0) return MLA_OK;
+  if (!u || !w_comb || !y) return MLA_ERR_INVALID_ARG;
+  const int64_t K = (int64_t)dims->n_h * dims->d_c;
+  if (K % 16 || K > INT32_MAX || !al16(u) || !al16(w_comb) || (int64_t)B * n_q > INT32_MAX / 2)
+    return MLA_ERR_UNSUPPORTED;
+  return run_gemm(gemm(u, K, 0, w_comb, K, 0, y, d_model, 0, B * n_q, d_model, (int)K, 1, true, false), stream);
+}
+
+mla_status_t mla_o_proj(const mla_dims_t* dims, int32_t d_model, int32_t B, int32_t n_q, const float* o,
+                        const void* w_o, float* y, void* stream) {
+  if (!dims_ok(dims) || d_model < 1 || B < 0 || n_q < 1) return MLA_ERR_INVALID_ARG;
+  if (B == 0) return MLA_OK;
+  if (!o || !w_o || !y) return MLA_ERR_INVALID_ARG;
+  const int64_t K = (int64_t)dims->n_h * dims->d_v;
+  if (K % 16 || K > INT32_MAX || !al16(o) || !al16(w_o) || (int64_t)B * n_q > INT32_MAX / 2)
+    return MLA_ERR_UNSUPPORTED;
+  return run_gemm(gemm(o, K, 0, w_o, K, 0, y, d_model, 0, B * n_q, d_model, (int)K, 1, true, false), stream);
+}
+
+mla_status_t mla_fold_q(const mla_dims_t* dims, int32_t d_q, const void* w_uq, const void* w_uk, void* w_kq,
+                        void* stream) {
+  if (!dims_ok(dims) || d_q < 1 || !w_uq || !w_uk || !w_kq) return MLA_ERR_INVALID_ARG;
+  const int n_h = dims->n_h, d_c = dims->d_c, d_nope = dims->d_nope;
+  if (d_nope % 16 || !al16(w_uq) || !al16(w_uk) || !al16(w_kq)) return MLA_ERR_UNSUPPORTED;
+  // z = head i: C[c][q] = sum_k w_uk[i][c][k] w_uq[q][i][k], written to w_kq[i][c][q]
+  return run_gemm(
+      gemm(w_uk, d_nope, (int64_t)d_c * d_nope, w_uq, (int64_t)n_h * d_nope, d_nope, w_kq, d_q,
+           (int64_t)d_c * d_q, d_c, d_q, d_nope, n_h, false, true), stream);
+}
+
+mla_status_t mla_absorb_q_folded(const mla_dims_t* dims, int32_t d_q, int32_t B, int32_t n_q, const void* c_q,
+                                 const void* q_rope, const int32_t* positions, const void* w_kq, void* q_lat,
+                                 void* q_pe, void* stream) {
+  if (!dims_ok(dims) || d_q < 1 || B < 0 || n_q < 1) return MLA_ERR_INVALID_ARG;
+  if (B == 0) return MLA_OK;
+  if (!c_q || !q_rope || !positions || !w_kq || !q_lat || !q_pe) return MLA_ERR_INVALID_ARG;
+  const int n_h = dims->n_h, d_c = dims->d_c;
+  if (d_q % 16 || !al16(c_q) || !al16(w_kq) || (int64_t)B * n_q > (1 << 24)) return MLA_ERR_UNSUPPORTED;
+  // z = head i: q_lat[m][i][c] = sum_q c_q[m][q] w_kq[i][c][q]
+  mla_status_t st = run_gemm(
+      gemm(c_q, d_q, 0, w_kq, d_q, (int64_t)d_c * d_q, q_lat, (int64_t)n_h * d_c, d_c, B * n_q, d_c, d_q, n_h,
+           false, true), stream);
+  if (st != MLA_OK) return st;
+  mla::AbsorbParams p;
+  p.q_nope = nullptr; p.q_rope = q_rope; p.positions = positions; p.w_uk = nullptr;
+  p.q_lat = q_lat; p.q_pe = q_pe;
+  p.B = B; p.n_q = n_q; p.n_h = n_h; p.d_c = d_c; p.d_rope = dims->d_rope; p.d_nope = dims->d_nope;
+  p.bf16 = true; p.rope_base = base_of(dims);
+  return from_hip(mla::launch_rope_q(p, (hipStream_t)stream));
 }
 
 }  // extern "C"

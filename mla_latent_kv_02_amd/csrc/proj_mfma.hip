@@ -330,6 +330,15 @@ __global__ __launch_bounds__(256) void out_proj_mfma_kernel(OutProjParams p) {
 
 }  // namespace
 
+hipError_t launch_rope_q(const AbsorbParams& p, hipStream_t stream) {
+  const int64_t nthreads = (int64_t)p.B * p.n_q * (p.d_rope / 2) * ((p.n_h + 3) / 4);
+  if (nthreads == 0) return hipSuccess;
+  const dim3 grid((unsigned)((nthreads + 255) / 256));
+  if (p.bf16) hipLaunchKernelGGL(rope_q_rows_kernel<uint16_t>, grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(rope_q_rows_kernel<float>, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
 bool absorb_mfma_ok(const AbsorbParams& p) {
   return p.bf16 && p.d_nope % 32 == 0 && p.d_nope <= 32 * AB_MAXK && p.d_c % 64 == 0;
 }

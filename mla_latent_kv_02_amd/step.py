@@ -80,10 +80,12 @@ class DecodeSession:
     of [Paldyn] = "MQA와 GQA: KV 캐시 경량화 전략", section "PagedAttention과
     연속 배칭"); a released slot takes a new sequence with ``append``.
 
-    Per step the host reserves blocks, then one copy per changed array takes
-    the block table (only when a block was added) and [positions | ctx_lens] to
-    the device from pinned staging (two slots, each reused only after its
-    previous copy is known done), and the step runs as mla_append_absorb_q,
+    Per step the host reserves blocks.  Positions and context lengths advance
+    by n_q on every step, so the device copy [positions | ctx_lens] is just
+    incremented in place; only after a block was added, or after ``append`` /
+    ``release`` changed the host state, do the block table and that array go
+    to the device, from pinned staging (two slots, each reused only after its
+    previous copy is known done).  The step then runs as mla_append_absorb_q,
     mla_decode and the merge + up-projection."""
 
     def __init__(self, dims: Dims, B: int, n_q: int, num_splits: int, dtype, n_blocks: int, block_size: int,
@@ -107,6 +109,7 @@ class DecodeSession:
         self._stage_done = [None, None]
         self._slot = 0
         self._table_dirty = True
+        self._meta_stale = True     # the device [positions | ctx_lens] does not follow from the last step
 
     def _reserve(self, b: int, n_tokens: int) -> None:
         before = self.pool.free_count
@@ -150,6 +153,7 @@ class DecodeSession:
             self.ctx[b] = max(int(self.ctx[b]), top)
         cur_pos = np.maximum(self.ctx[:, None] - self.n_q + np.arange(self.n_q, dtype=np.int32)[None, :], 0)
         self._upload(cur_pos, self.ctx, stream)
+        self._meta_stale = True
         dev = self.data.device
         sid = torch.from_numpy(seq_ids).to(dev)
         pos = torch.from_numpy(positions).to(dev)
@@ -166,11 +170,18 @@ class DecodeSession:
         [B][n_q][n_h][d_v] (fp32, owned by the session, overwritten next step)."""
         import numpy as np
         d, B, n_q = self.dims, self.B, self.n_q
-        for b in range(B):
-            self._reserve(b, int(self.ctx[b]) + n_q)
+        before = self.pool.free_count
+        self.pool.reserve_all(self.ctx + n_q)
+        self._table_dirty |= self.pool.free_count != before
         pos = self.ctx[:, None] + np.arange(n_q, dtype=np.int32)[None, :]
         new_ctx = self.ctx + n_q
-        self._upload(pos, new_ctx, stream)
+        if self._table_dirty or self._meta_stale:
+            self._upload(pos, new_ctx, stream)
+            self._meta_stale = False
+        else:   # last step's positions and lengths, each + n_q
+            import torch
+            with torch.cuda.stream(torch.cuda.current_stream() if stream is None else stream):
+                self._meta_dev.add_(n_q)
         w = self.work
         mla_append_absorb_q(d, self.cache, self.seq_ids, self.positions.view(-1),
                             c_kv_new.reshape(B * n_q, d.d_c), k_rope_new.reshape(B * n_q, d.d_rope), q_nope, q_rope,
@@ -192,3 +203,4 @@ class DecodeSession:
         self.pool.release(b)
         self._table_dirty |= self.pool.free_count != before
         self.ctx[b] = 0
+        self._meta_stale = True

@@ -13,6 +13,10 @@ from .mla_oracle import (  # noqa: F401
     decode_sequence,
     merge_partials,
     value_up_projection,
+    output_projection,
+    fold_output,
+    query_from_compressed,
+    fold_query,
     mla_cache_elements_per_token,
     mla_cache_bytes_per_token,
     mha_cache_bytes_per_token,

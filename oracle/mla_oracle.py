@@ -110,6 +110,45 @@ def value_up_projection(u: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
     return out
 
 
+# --------------------------------------------------------------- weight folds
+def output_projection(o: np.ndarray, w_o: np.ndarray) -> np.ndarray:
+    """Layer output: the heads' outputs concatenated times W^O, i.e.
+    y = sum_i o_i W_i^O with W_i^O the d_v x d block of head i [Huny §3.2].
+    o [..., n_h, d_v], w_o [n_h, d_v, d] -> [..., d]."""
+    o = np.asarray(o, dtype=np.float64)
+    w = np.asarray(w_o, dtype=np.float64)
+    y = np.zeros(o.shape[:-2] + (w.shape[2],), dtype=np.float64)
+    for i in range(w.shape[0]):
+        y += o[..., i, :] @ w[i]
+    return y
+
+
+def fold_output(w_uv: np.ndarray, w_o: np.ndarray) -> np.ndarray:
+    """W_{i,comb} = W_i^UV W_i^O per head, formed offline so that the layer
+    output is u_i W_{i,comb} summed over heads [Huny §3.2].
+    w_uv [n_h, d_c, d_v], w_o [n_h, d_v, d] -> [n_h, d_c, d]."""
+    w_uv = np.asarray(w_uv, dtype=np.float64)
+    w_o = np.asarray(w_o, dtype=np.float64)
+    return np.stack([w_uv[i] @ w_o[i] for i in range(w_uv.shape[0])])
+
+
+def query_from_compressed(c_q: np.ndarray, w_uq: np.ndarray) -> np.ndarray:
+    """q^C_i = c_q W_i^UQ, the per-head content query from the compressed
+    query [Huny §1]; c_q [..., d_q], w_uq [n_h, d_q, d_nope] -> [..., n_h, d_nope]."""
+    c = np.asarray(c_q, dtype=np.float64)
+    w = np.asarray(w_uq, dtype=np.float64)
+    return np.stack([c @ w[i] for i in range(w.shape[0])], axis=-2)
+
+
+def fold_query(w_uq: np.ndarray, w_uk: np.ndarray) -> np.ndarray:
+    """W_{KQ,i} = W_i^UQ (W_i^UK)^T per head: the key expansion folded into the
+    query projection [Paldyn, section MLA], so that q_lat = c_q W_{KQ,i}.
+    w_uq [n_h, d_q, d_nope], w_uk [n_h, d_c, d_nope] -> [n_h, d_q, d_c]."""
+    w_uq = np.asarray(w_uq, dtype=np.float64)
+    w_uk = np.asarray(w_uk, dtype=np.float64)
+    return np.stack([w_uq[i] @ w_uk[i].T for i in range(w_uq.shape[0])])
+
+
 # --------------------------------------------------------------- decode
 def decode_sequence(q_nope, q_rope, q_positions, c_kv, k_rope_raw, w_uk, w_uv,
                     sm_scale: float, rope_base: float,

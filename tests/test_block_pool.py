@@ -99,3 +99,20 @@ def test_random_workload_keeps_the_pool_consistent():
         assert len(owned) == len(set(owned)) and len(owned) + pool.free_count == nb
         for s in range(B):
             np.testing.assert_array_equal(pool.table[s], rows[s] + [-1] * (mb - len(rows[s])))
+
+
+def test_reserve_all_is_all_or_nothing():
+    pool = mla.BlockPool(n_blocks=6, block_size=4, B=3, max_blocks=4)
+    pool.reserve_all(np.array([5, -1, 4]))          # 2 + 1 blocks; sequence 1 untouched
+    np.testing.assert_array_equal(pool.table[:, :2], [[0, 1], [-1, -1], [2, -1]])
+    with pytest.raises(bd.MlaError) as e:
+        pool.reserve_all(np.array([16, 8, 4]))      # needs 2 + 2 more, 3 free
+    assert e.value.status == bd.MLA_ERR_OUT_OF_BLOCKS
+    assert pool.free_count == 3 and (pool.table[1] == -1).all()
+    with pytest.raises(bd.MlaError) as e:
+        pool.reserve_all(np.array([17, 0, 0]))      # more than max_blocks
+    assert e.value.status == bd.MLA_ERR_INVALID_ARG
+    pool.reserve_all(np.array([8, 8, 4]))
+    assert pool.free_count == 1
+    with pytest.raises(ValueError):
+        pool.reserve_all(np.array([1, 2]))

@@ -240,6 +240,63 @@ def test_value_side_identity():
                                rtol=1e-12, atol=1e-14)
 
 
+def test_output_fold_against_scalar_loops():
+    """Layer output through the fold, sum_i u_i (W_i^UV W_i^O), and without it,
+    sum_i (u_i W_i^UV) W_i^O [Huny §3.2], both equal plain scalar loops over
+    every index; a transposed W_i^O block (square, so shapes cannot catch it)
+    changes the result."""
+    rng = np.random.default_rng(41)
+    n_h, d_c, d_v, d = 3, 5, 4, 6
+    u = rng.standard_normal((2, n_h, d_c))
+    w_uv = rng.standard_normal((n_h, d_c, d_v))
+    w_o = rng.standard_normal((n_h, d_v, d))
+    brute = np.zeros((2, d))
+    for m in range(2):
+        for n in range(d):
+            acc = 0.0
+            for i in range(n_h):
+                for c in range(d_c):
+                    for v in range(d_v):
+                        acc += u[m, i, c] * w_uv[i, c, v] * w_o[i, v, n]
+            brute[m, n] = acc
+    unfolded = oracle.output_projection(oracle.value_up_projection(u, w_uv), w_o)
+    comb = oracle.fold_output(w_uv, w_o)
+    folded = sum(u[:, i, :] @ comb[i] for i in range(n_h))
+    np.testing.assert_allclose(unfolded, brute, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(folded, brute, rtol=1e-12, atol=1e-12)
+    w_sq = rng.standard_normal((n_h, d_v, d_v))
+    o = oracle.value_up_projection(u, w_uv)
+    assert np.abs(oracle.output_projection(o, w_sq) - oracle.output_projection(o, w_sq.transpose(0, 2, 1))).max() > 0.1
+
+
+def test_query_fold_against_scalar_loops():
+    """q_lat from the compressed query through the fold, c_q W_i^UQ (W_i^UK)^T
+    [Paldyn, section MLA], equals plain loops and the two-step path (content
+    query, then the absorption of decode_sequence)."""
+    rng = np.random.default_rng(42)
+    n_h, d_q, d_nope, d_c = 2, 6, 4, 5
+    c_q = rng.standard_normal((3, d_q))
+    w_uq = rng.standard_normal((n_h, d_q, d_nope))
+    w_uk = rng.standard_normal((n_h, d_c, d_nope))
+    brute = np.zeros((3, n_h, d_c))
+    for m in range(3):
+        for i in range(n_h):
+            for c in range(d_c):
+                brute[m, i, c] = sum(c_q[m, q] * w_uq[i, q, k] * w_uk[i, c, k]
+                                     for q in range(d_q) for k in range(d_nope))
+    kq = oracle.fold_query(w_uq, w_uk)
+    folded = np.stack([c_q @ kq[i] for i in range(n_h)], axis=1)
+    np.testing.assert_allclose(folded, brute, rtol=1e-12, atol=1e-12)
+    q_nope = oracle.query_from_compressed(c_q, w_uq)
+    np.testing.assert_allclose(oracle.absorb_query(q_nope, w_uk), brute, rtol=1e-12, atol=1e-12)
+    # through a decode step (one token, arbitrary cache): its absorbed query is the same
+    S, d_rope, d_v = 4, 4, 3
+    ref = oracle.decode_sequence(q_nope, rng.standard_normal((3, n_h, d_rope)), np.array([3, 3, 3]),
+                                 rng.standard_normal((S, d_c)), rng.standard_normal((S, d_rope)), w_uk,
+                                 rng.standard_normal((n_h, d_c, d_v)), 0.3, 10000.0)
+    np.testing.assert_allclose(ref["q_lat"], brute, rtol=1e-12, atol=1e-12)
+
+
 def test_decomposition_single_token_closed_form():
     """S = 1: softmax weight 1, so o = c_0 W_UV, u = c_0 and lse = the one score,
     which is the sum of the content and positional dot products."""
