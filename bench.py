@@ -51,6 +51,14 @@ def parse():
                     help="only run a plain fp32 copy kernel (dst = -src) over this many MiB, 5 times: the "
                          "calibration run for the HBM byte counters")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time in the CPU sample")
+    ap.add_argument("--folds", action="store_true",
+                    help="instead of the step bench: the weight folds' per-step products (layer output through "
+                         "W_comb = W_UV W_O vs through W_UV then W_O; q_lat through W_KQ = W_UQ W_UK^T) at the "
+                         "workload's batch, d_model 7168, d_q 1536")
+    ap.add_argument("--session", action="store_true",
+                    help="instead of the step bench: multi-step decode (DecodeSession) over a paged cache that "
+                         "grows by n_q tokens per sequence per step, blocks from the library's block pool; "
+                         "the workload's contexts are the prompts")
     return ap.parse_args()
 
 
@@ -170,6 +178,151 @@ def copy_probe(mib):
     log(f"copy probe: 5 x {mib} MiB read + {mib} MiB written")
 
 
+def folds_bench(args):
+    """Time the per-step products of the weight folds against their bytes."""
+    import numpy as np
+    import torch
+    import mla_latent_kv_02_amd as mla
+    import workloads as W
+    from workloads.device import dims_of, to_device
+
+    w = W.get(args.workload)
+    if w.dtype != "bf16":
+        sys.exit("--folds runs the bf16 V3-shaped workloads")
+    d_model, d_q = 7168, 1536
+    dims = dims_of(w)
+    M = w.batch * w.n_q
+    g = torch.Generator(device="cuda").manual_seed(w.seed)
+    rnd = lambda *shape, scale=1.0: (torch.randn(shape, generator=g, device="cuda") * scale)
+    w_uv = to_device(W.weights(w)["w_uv"], "bf16", "cuda")
+    w_uk = to_device(W.weights(w)["w_uk"], "bf16", "cuda")
+    w_o = rnd(d_model, w.n_h, w.d_v, scale=(w.n_h * w.d_v) ** -0.5).to(torch.bfloat16)
+    w_uq = rnd(d_q, w.n_h, w.d_nope, scale=d_q ** -0.5).to(torch.bfloat16)
+    u = rnd(w.batch, w.n_q, w.n_h, w.d_c)
+    o = torch.empty((w.batch, w.n_q, w.n_h, w.d_v), device="cuda")
+    y = torch.empty((w.batch, w.n_q, d_model), device="cuda")
+    c_q = rnd(w.batch, w.n_q, d_q).to(torch.bfloat16)
+    q_nope = rnd(w.batch, w.n_q, w.n_h, w.d_nope).to(torch.bfloat16)
+    q_rope = rnd(w.batch, w.n_q, w.n_h, w.d_rope).to(torch.bfloat16)
+    pos = torch.zeros((w.batch, w.n_q), dtype=torch.int32, device="cuda")
+    q_lat = torch.empty((w.batch, w.n_q, w.n_h, w.d_c), dtype=torch.bfloat16, device="cuda")
+    q_pe = torch.empty((w.batch, w.n_q, w.n_h, w.d_rope), dtype=torch.bfloat16, device="cuda")
+    w_comb = torch.empty((d_model, w.n_h, w.d_c), dtype=torch.bfloat16, device="cuda")
+    w_kq = torch.empty((w.n_h, w.d_c, d_q), dtype=torch.bfloat16, device="cuda")
+    mla.mla_fold_out(dims, w_uv, w_o, w_comb)
+    mla.mla_fold_q(dims, w_uq, w_uk, w_kq)
+
+    def timed(fn, reps=50):
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3    # us
+
+    nb = lambda t: t.numel() * t.element_size()
+    rows = []
+    def row(name, fn, nbytes):
+        us = timed(fn)
+        rows.append({"product": name, "us": round(us, 2), "bytes": int(nbytes),
+                     "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "frac_of_8TBps": round(nbytes / (us * 1e-6) / 8e12, 3)})
+        log(f"{name}: {us:.1f} us, {nbytes / 1e6:.1f} MB")
+    row("output unfolded: mla_out_proj (u W_UV) + mla_o_proj (o W_O)",
+        lambda: (mla.mla_out_proj(dims, u, w_uv, o), mla.mla_o_proj(dims, o, w_o, y)),
+        nb(u) + nb(w_uv) + 2 * nb(o) + nb(w_o) + nb(y))
+    row("output folded: mla_out_proj_folded (u W_comb)", lambda: mla.mla_out_proj_folded(dims, u, w_comb, y),
+        nb(u) + nb(w_comb) + nb(y))
+    row("query absorbed: mla_absorb_q (q_nope -> q_lat; c_q W_UQ is outside the library)",
+        lambda: mla.mla_absorb_q(dims, q_nope, q_rope, pos, w_uk, q_lat, q_pe),
+        nb(q_nope) + nb(q_rope) + nb(w_uk) + nb(q_lat) + nb(q_pe))
+    row("query folded: mla_absorb_q_folded (c_q W_KQ)",
+        lambda: mla.mla_absorb_q_folded(dims, c_q, q_rope, pos, w_kq, q_lat, q_pe),
+        nb(c_q) + nb(q_rope) + nb(w_kq) + nb(q_lat) + nb(q_pe))
+    result = {"metric": "MLA weight folds: per-step products, time and HBM GB/s (DeepSeek-V3 shapes)",
+              "value": rows[1]["us"], "unit": "us (folded output product)", "higher_is_better": False,
+              "n_gpus": 1, "dtype": "bf16", "data": "synthetic (seeded N(0,1/fan_in) weights)",
+              "config": {"workload": f"{w.name} batch: {M} query rows, d_model {d_model}, d_q {d_q}"},
+              "products": rows}
+    print(json.dumps(result), flush=True)
+
+
+def session_bench(args):
+    """Multi-step decode over a growing paged cache: prefill the workload's
+    contexts through DecodeSession.append, then time --steps steps (after
+    --warmup) of DecodeSession.step, each appending n_q new rows per sequence."""
+    import numpy as np
+    import torch
+    import workloads as W
+    from mla_latent_kv_02_amd.plan import default_num_splits
+    from mla_latent_kv_02_amd.step import DecodeSession
+    from workloads.device import dims_of, to_device
+
+    w = W.get(args.workload)
+    if w.dtype != "bf16":
+        sys.exit("--session runs the bf16 V3-shaped workloads")
+    bs = w.block_size or 64
+    ctx = W.context_lengths(w)
+    grow = (args.warmup + args.steps + 1) * w.n_q
+    need = (ctx.astype(np.int64) + grow + bs - 1) // bs
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    num_splits = args.num_splits or default_num_splits(int(ctx.sum()), w.n_q, w.n_h)
+    sess = DecodeSession(dims_of(w), w.batch, w.n_q, num_splits, tdt, n_blocks=int(need.sum()), block_size=bs,
+                         max_blocks=int(need.max()))
+    log(f"session on {w.name}: prefill {int(ctx.sum())} tokens in blocks of {bs}")
+    t0 = time.perf_counter()
+    seq_all = np.repeat(np.arange(w.batch, dtype=np.int32), ctx)
+    tok_all = np.concatenate([np.arange(c, dtype=np.int32) for c in ctx])
+    table = torch.from_numpy(W.normal_table_bf16_bits().view(np.int16)).cuda() if w.dtype == "bf16" else None
+    chunk = 1 << 20
+    for s0 in range(0, len(seq_all), chunk):
+        sq, tk = seq_all[s0:s0 + chunk], tok_all[s0:s0 + chunk]
+        raw = torch.empty((len(sq), w.row), dtype=tdt, device="cuda")
+        sd, td = torch.from_numpy(sq).cuda(), torch.from_numpy(tk).cuda()
+        W.fill_cache_rows_device(w, sd.data_ptr(), td.data_ptr(), len(sq), table.data_ptr(), raw.data_ptr(),
+                                 torch.cuda.current_stream().cuda_stream)
+        sess.append(sq, tk, raw[:, :w.d_c], raw[:, w.d_c:])
+        del raw
+    log(f"prefilled in {time.perf_counter() - t0:.1f} s")
+    wt, q = W.weights(w), W.queries(w)
+    w_uk, w_uv = to_device(wt["w_uk"], w.dtype, "cuda"), to_device(wt["w_uv"], w.dtype, "cuda")
+    q_nope, q_rope = to_device(q["q_nope"], w.dtype, "cuda"), to_device(q["q_rope"], w.dtype, "cuda")
+    g = torch.Generator(device="cuda").manual_seed(w.seed)
+    new = torch.randn((w.batch, w.n_q, w.row), generator=g, device="cuda").to(tdt)
+    c_new, r_new = new[..., :w.d_c], new[..., w.d_c:]
+    c_new, r_new = c_new.contiguous(), r_new.contiguous()
+    for _ in range(args.warmup):
+        sess.step(c_new, r_new, q_nope, q_rope, w_uk, w_uv)
+    torch.cuda.synchronize()
+    ctx0 = sess.ctx.astype(np.int64).copy()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        sess.step(c_new, r_new, q_nope, q_rope, w_uk, w_uv)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    # cache rows attended over the timed steps (query j of a step sees ctx + j + 1 rows)
+    attended = sum(int(((ctx0 + k * w.n_q)[:, None] + np.arange(1, w.n_q + 1)[None, :]).sum())
+                   for k in range(1, args.steps + 1))
+    row_bytes = w.row * (2 if w.dtype == "bf16" else 4)
+    result = {
+        "metric": "MLA multi-step decode over a growing paged cache: decode tokens/s (DeepSeek-V3 shapes)",
+        "value": round(w.batch * w.n_q / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded Philox N(0,1) prompt latents, N(0,1) new rows and queries)",
+        "config": {"workload": f"{w.name} as prompts, +{w.n_q} token(s) per sequence per step",
+                   "batch": w.batch, "n_q": w.n_q, "block_size": bs, "num_splits": num_splits,
+                   "prompt_tokens": int(ctx.sum()), "blocks": int(need.sum())},
+        "cache_GBps_attended": round(attended / args.steps * row_bytes / (ms * 1e-3) / 1e9, 2),
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -178,6 +331,12 @@ def main():
         sys.exit(2)
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
+        return
+    if args.session:
+        session_bench(args)
+        return
+    if args.folds:
+        folds_bench(args)
         return
     import numpy as np
     import torch
