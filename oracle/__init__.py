@@ -17,6 +17,12 @@ from .mla_oracle import (  # noqa: F401
     fold_output,
     query_from_compressed,
     fold_query,
+    e4m3_value,
+    e4m3_encode,
+    fp8_quantize_latent,
+    fp8_dequantize_latent,
+    FP8_TILE,
+    FP8_MAX,
     mla_cache_elements_per_token,
     mla_cache_bytes_per_token,
     mha_cache_bytes_per_token,

@@ -237,6 +237,67 @@ def merge_partials(u_parts: np.ndarray, lse_parts: np.ndarray):
     return u, lse
 
 
+# ------------------------------------------------------- fp8 latent cache
+# The pages warn that a per-tensor fp8 scale lets outlier channels crush the
+# rest of the compressed latent, and ask for per-channel or per-block (tile)
+# scales instead [Huny, serving checklist, fp8 KV-cache item; Paldyn, KV-cache
+# quantisation].  The reading taken here: each cached token's latent is cut
+# into tiles of 128 channels, and each tile gets its own fp32 scale, its
+# largest magnitude over 448 (the largest e4m3 value).  The element format is
+# the 8-bit e4m3 float: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
+# bits, subnormals at exponent field 0, no infinities, and the all-ones
+# exponent-and-mantissa pattern reserved for NaN.
+FP8_TILE = 128
+FP8_MAX = 448.0
+
+
+def e4m3_value(code) -> np.ndarray:
+    """Value of e4m3 byte(s) per the format definition (NaN for the NaN codes)."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e.astype(np.float64) - 7))
+    return np.where((e == 15) & (m == 7), np.nan, sign * mag)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest e4m3 code to each value (ties to the even code), values first
+    clamped to [-448, 448]: a search over the 127 non-negative finite codes."""
+    x = np.clip(np.asarray(x, dtype=np.float64), -FP8_MAX, FP8_MAX)
+    table = e4m3_value(np.arange(127))                # codes 0x00 .. 0x7E, increasing
+    a = np.abs(x)
+    hi = np.clip(np.searchsorted(table, a, side="left"), 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    d_lo, d_hi = a - table[lo], table[hi] - a
+    pick = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
+    pick = np.where(a == table[hi], hi, pick)
+    return (pick | np.where(np.signbit(x) & (pick != 0), 0x80, 0)).astype(np.uint8)
+
+
+def fp8_quantize_latent(c_kv: np.ndarray):
+    """Codes [S][d_c] (uint8) and scales [S][d_c/128] (fp32) of cached latents.
+    In fp32, as a device computes it: amax = largest magnitude of the tile;
+    scale = amax / 448 (1 for an all-zero tile); code = e4m3(x / scale)."""
+    x = np.asarray(c_kv, dtype=np.float32)
+    S, d_c = x.shape
+    if d_c % FP8_TILE:
+        raise ValueError("d_c must be a multiple of 128")
+    tiles = x.reshape(S, d_c // FP8_TILE, FP8_TILE)
+    amax = np.abs(tiles).max(axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(FP8_MAX), np.float32(1.0)).astype(np.float32)
+    q = (tiles / scale[..., None]).astype(np.float32)
+    return e4m3_encode(q).reshape(S, d_c), scale
+
+
+def fp8_dequantize_latent(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """c_kv as the fp8 cache holds it: e4m3 value times its tile's scale (fp64)."""
+    codes = np.asarray(codes)
+    S, d_c = codes.shape
+    v = e4m3_value(codes).reshape(S, d_c // FP8_TILE, FP8_TILE)
+    return (v * np.asarray(scales, dtype=np.float64)[..., None]).reshape(S, d_c)
+
+
 # ------------------------------------------------------- cache arithmetic
 def mla_cache_elements_per_token(d_c: int, d_rope: int) -> int:
     """Elements cached per token per layer: c^KV plus the shared k^R [Huny §2.2]."""

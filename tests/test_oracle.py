@@ -457,3 +457,66 @@ def test_planted_mistakes_fail_brute_force(mutation):
     prob = _problem(18, n_q=2, n_h=2, d_c=4, d_nope=2, d_rope=4, d_v=4, S=6)
     ok, _, _ = _compare_to_brute(_mutant_decode(mutation), prob, tol=1e-10)
     assert not ok, f"planted mistake {mutation} was not detected"
+
+
+# ------------------------------------------------------------------ fp8 latent cache
+def test_e4m3_format_definition():
+    """Closed forms of the e4m3 format: 448 largest, 2^-6 smallest normal,
+    2^-9 smallest subnormal, 1.0 at exponent field 7, two NaN codes, symmetric,
+    127 increasing non-negative finite values."""
+    v = oracle.e4m3_value(np.arange(256))
+    assert v[0x7E] == 448.0 and v[0x08] == 2.0 ** -6 and v[0x01] == 2.0 ** -9 and v[0x38] == 1.0
+    assert v[0x07] == 7 / 8 * 2.0 ** -6 and v[0x3F] == 1.875 and v[0x40] == 2.0
+    assert np.isnan(v).sum() == 2 and np.isnan(v[0x7F]) and np.isnan(v[0xFF])
+    np.testing.assert_array_equal(v[0x80:0xFF], -v[0x00:0x7F])
+    assert (np.diff(v[:0x7F]) > 0).all()
+
+
+def test_e4m3_encode_rounds_to_nearest_even():
+    v = oracle.e4m3_value(np.arange(256))
+    finite = [c for c in range(256) if not np.isnan(v[c]) and c != 0x80]
+    np.testing.assert_array_equal(oracle.e4m3_encode(v[finite]), finite)
+    assert oracle.e4m3_encode(np.array([-0.0]))[0] == 0x00          # zero keeps no sign
+    pos = v[:0x7F]
+    mid = (pos[:-1] + pos[1:]) / 2
+    lo = np.arange(0x7E)
+    even = np.where(lo % 2 == 0, lo, lo + 1)
+    np.testing.assert_array_equal(oracle.e4m3_encode(mid), even)     # ties go to the even code
+    np.testing.assert_array_equal(oracle.e4m3_encode(np.nextafter(mid, 0)), lo)
+    np.testing.assert_array_equal(oracle.e4m3_encode(np.nextafter(mid, 1e9)), lo + 1)
+    np.testing.assert_array_equal(oracle.e4m3_encode(-mid), np.where(even == 0, 0, even | 0x80))
+    np.testing.assert_array_equal(oracle.e4m3_encode(np.array([500.0, -1e9])), [0x7E, 0xFE])   # clamped
+
+
+def test_fp8_latent_quantisation():
+    """Per-tile scales: the largest magnitude of every tile lands on +-448, an
+    all-zero tile gets scale 1 and zero codes, and every value is recovered
+    within half an e4m3 step of its tile's scale."""
+    rng = np.random.default_rng(60)
+    x = oracle_round_bf16(rng.standard_normal((5, 512)).astype(np.float32) * np.float32(3.0))
+    x[2, 128:256] = 0.0
+    x[3, 0:128] *= np.float32(1e-3)           # a small tile keeps its own resolution
+    codes, scales = oracle.fp8_quantize_latent(x)
+    assert codes.dtype == np.uint8 and scales.shape == (5, 4)
+    assert scales[2, 1] == 1.0 and (codes[2, 128:256] == 0).all()
+    for s in range(5):
+        for g in range(4):
+            tile = x[s, 128 * g:128 * (g + 1)]
+            if not tile.any():
+                continue
+            k = int(np.argmax(np.abs(tile)))
+            assert codes[s, 128 * g + k] == (0x7E if tile[k] > 0 else 0xFE)
+    deq = oracle.fp8_dequantize_latent(codes, scales)
+    v = oracle.e4m3_value(np.arange(0x7F))
+    step = np.diff(v)                                # spacing above each non-negative code
+    a = np.abs(oracle.e4m3_value(codes.astype(np.int64)))
+    idx = np.clip(np.searchsorted(v, a), 0, 0x7D)
+    bound = np.repeat(scales, 128, axis=1) * step[idx] / 2 * (1 + 1e-6)
+    assert (np.abs(deq - x) <= bound + 1e-30).all()
+    # the small tile's error follows its own largest value (half the top e4m3 step, 16 of 448)
+    assert np.abs(deq[3, :128] - x[3, :128]).max() <= np.abs(x[3, :128]).max() * 16 / 448 * (1 + 1e-6)
+
+
+def oracle_round_bf16(x):
+    import workloads as W
+    return W.round_to_bf16(x)
