@@ -19,6 +19,7 @@ from .mla_oracle import (  # noqa: F401
     fold_query,
     e4m3_value,
     e4m3_encode,
+    fp8_tile_scale,
     fp8_quantize_latent,
     fp8_dequantize_latent,
     FP8_TILE,

@@ -242,8 +242,12 @@ def merge_partials(u_parts: np.ndarray, lse_parts: np.ndarray):
 # rest of the compressed latent, and ask for per-channel or per-block (tile)
 # scales instead [Huny, serving checklist, fp8 KV-cache item; Paldyn, KV-cache
 # quantisation].  The reading taken here: each cached token's latent is cut
-# into tiles of 128 channels, and each tile gets its own fp32 scale, its
-# largest magnitude over 448 (the largest e4m3 value).  The element format is
+# into tiles of 128 channels, and each tile gets its own scale, the smallest
+# power of two 2^k with the tile's largest magnitude <= 448 * 2^k (448 is the
+# largest e4m3 value).  A power of two costs a floating-point format no
+# relative precision (every value keeps its 3 mantissa bits) and makes both
+# directions exact: x / 2^k before rounding, code value * 2^k after.  The
+# element format is
 # the 8-bit e4m3 float: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
 # bits, subnormals at exponent field 0, no infinities, and the all-ones
 # exponent-and-mantissa pattern reserved for NaN.
@@ -275,19 +279,30 @@ def e4m3_encode(x) -> np.ndarray:
     return (pick | np.where(np.signbit(x) & (pick != 0), 0x80, 0)).astype(np.uint8)
 
 
+def fp8_tile_scale(amax) -> np.ndarray:
+    """2^k for the smallest integer k with amax <= 448 * 2^k (1 for amax = 0)."""
+    amax = np.asarray(amax, dtype=np.float64)
+    k = np.zeros(amax.shape, dtype=np.int64)
+    pos = amax > 0
+    k[pos] = np.ceil(np.log2(amax[pos] / FP8_MAX)).astype(np.int64)
+    # guard the logarithm's rounding: step k until 448 * 2^(k-1) < amax <= 448 * 2^k
+    for _ in range(2):
+        k = np.where(pos & (amax > FP8_MAX * 2.0 ** k), k + 1, k)
+        k = np.where(pos & (amax <= FP8_MAX * 2.0 ** (k - 1)), k - 1, k)
+    return (2.0 ** k).astype(np.float32)
+
+
 def fp8_quantize_latent(c_kv: np.ndarray):
-    """Codes [S][d_c] (uint8) and scales [S][d_c/128] (fp32) of cached latents.
-    In fp32, as a device computes it: amax = largest magnitude of the tile;
-    scale = amax / 448 (1 for an all-zero tile); code = e4m3(x / scale)."""
+    """Codes [S][d_c] (uint8) and scales [S][d_c/128] (fp32 powers of two) of
+    cached latents: per 128-channel tile, scale = fp8_tile_scale(largest
+    magnitude), code = e4m3(x / scale) (the division is exact)."""
     x = np.asarray(c_kv, dtype=np.float32)
     S, d_c = x.shape
     if d_c % FP8_TILE:
         raise ValueError("d_c must be a multiple of 128")
-    tiles = x.reshape(S, d_c // FP8_TILE, FP8_TILE)
-    amax = np.abs(tiles).max(axis=-1)
-    scale = np.where(amax > 0, amax / np.float32(FP8_MAX), np.float32(1.0)).astype(np.float32)
-    q = (tiles / scale[..., None]).astype(np.float32)
-    return e4m3_encode(q).reshape(S, d_c), scale
+    tiles = x.reshape(S, d_c // FP8_TILE, FP8_TILE).astype(np.float64)
+    scale = fp8_tile_scale(np.abs(tiles).max(axis=-1))
+    return e4m3_encode(tiles / scale[..., None]).reshape(S, d_c), scale
 
 
 def fp8_dequantize_latent(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:

@@ -488,10 +488,21 @@ def test_e4m3_encode_rounds_to_nearest_even():
     np.testing.assert_array_equal(oracle.e4m3_encode(np.array([500.0, -1e9])), [0x7E, 0xFE])   # clamped
 
 
+def test_fp8_tile_scale_is_the_smallest_sufficient_power_of_two():
+    amax = np.array([448.0, 448.0001, 224.0, 224.0001, 1.0, 3.9, 1e-30, 0.0, 7e5], dtype=np.float32)
+    sc = oracle.fp8_tile_scale(amax)
+    np.testing.assert_array_equal(sc, [1.0, 2.0, 0.5, 1.0, 2.0 ** -8, 2.0 ** -6, 2.0 ** -108, 1.0, 2.0 ** 11])
+    k = np.log2(sc[amax > 0].astype(np.float64))
+    assert (k == np.round(k)).all()
+    a = amax[amax > 0].astype(np.float64)
+    assert (a <= 448 * 2.0 ** k).all() and (a > 448 * 2.0 ** (k - 1)).all()
+
+
 def test_fp8_latent_quantisation():
-    """Per-tile scales: the largest magnitude of every tile lands on +-448, an
-    all-zero tile gets scale 1 and zero codes, and every value is recovered
-    within half an e4m3 step of its tile's scale."""
+    """Per-tile power-of-two scales: the largest magnitude of every tile lands
+    in [224, 448], an all-zero tile gets scale 1 and zero codes, every value is
+    recovered within half an e4m3 step of its tile's scale, and a normal-range
+    value within 2^-4 of itself."""
     rng = np.random.default_rng(60)
     x = oracle_round_bf16(rng.standard_normal((5, 512)).astype(np.float32) * np.float32(3.0))
     x[2, 128:256] = 0.0
@@ -505,7 +516,8 @@ def test_fp8_latent_quantisation():
             if not tile.any():
                 continue
             k = int(np.argmax(np.abs(tile)))
-            assert codes[s, 128 * g + k] == (0x7E if tile[k] > 0 else 0xFE)
+            top = oracle.e4m3_value(int(codes[s, 128 * g + k]))
+            assert 224 <= abs(top) <= 448 and np.sign(top) == np.sign(tile[k])
     deq = oracle.fp8_dequantize_latent(codes, scales)
     v = oracle.e4m3_value(np.arange(0x7F))
     step = np.diff(v)                                # spacing above each non-negative code
@@ -513,8 +525,10 @@ def test_fp8_latent_quantisation():
     idx = np.clip(np.searchsorted(v, a), 0, 0x7D)
     bound = np.repeat(scales, 128, axis=1) * step[idx] / 2 * (1 + 1e-6)
     assert (np.abs(deq - x) <= bound + 1e-30).all()
-    # the small tile's error follows its own largest value (half the top e4m3 step, 16 of 448)
-    assert np.abs(deq[3, :128] - x[3, :128]).max() <= np.abs(x[3, :128]).max() * 16 / 448 * (1 + 1e-6)
+    # the small tile's error follows its own largest value (half a top-binade step, 16 of 256)
+    assert np.abs(deq[3, :128] - x[3, :128]).max() <= np.abs(x[3, :128]).max() / 16 * (1 + 1e-6)
+    normal = np.abs(x) >= np.repeat(scales, 128, axis=1) * 2.0 ** -6
+    assert (np.abs(deq - x)[normal] <= np.abs(x)[normal] * 2.0 ** -4 * (1 + 1e-9)).all()
 
 
 def oracle_round_bf16(x):
