@@ -53,7 +53,9 @@ typedef enum {
   MLA_ERR_OUT_OF_BLOCKS = 4    /* block pool: not enough free blocks */
 } mla_status_t;
 
-typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype_t;
+/* MLA_FP8_E4M3 is a cache dtype only (see mla_cache_t); queries, weights and
+ * new cache rows that go with an fp8 cache are bf16. */
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_FP8_E4M3 = 2 } mla_dtype_t;
 
 /* Head geometry.  n_h query heads; d_c latent width; d_rope positional-key
  * width (even); d_nope per-head content width of q/k; d_v per-head value
@@ -74,16 +76,35 @@ typedef struct {
  *     token t of sequence b is row (t % block_size) of block
  *     block_table[b * max_blocks + t / block_size].
  * ctx_lens [B]: number of cached tokens of each sequence (the query tokens'
- * own rows included).  `data` must be 16-byte aligned. */
+ * own rows included).  `data` must be 16-byte aligned.
+ *
+ * fp8 cache (dtype MLA_FP8_E4M3; [Huny], serving checklist, fp8 KV-cache item
+ * and [Paldyn], KV-cache quantisation: per-block scales rather than one
+ * scale per tensor).  A row is mla_cache_row_bytes() = d_c + 2 d_rope +
+ * 4 d_c/128 bytes:
+ *   bytes [0, d_c)                   c_kv as e4m3 codes (OCP FP8: bias 7, max
+ *                                    448, subnormals, 0x7F/0xFF NaN)
+ *   bytes [d_c, d_c + 2 d_rope)      rotated k_rope, bf16 (not quantised)
+ *   then d_c/128 fp32 scales         one per 128-channel tile of c_kv
+ * c_kv[128 g + j] = e4m3(code) * scale[g].  Each scale is the smallest power
+ * of two 2^k, k >= -126, with the tile's largest magnitude <= 448 * 2^k (1
+ * for an all-zero tile), so encoding and decoding are exact scalings and every
+ * element keeps the 3 mantissa bits of e4m3.  Requires d_c % 128 == 0;
+ * seq_stride counts bytes. */
 typedef struct {
   mla_dtype_t dtype;
   void *data;
-  int64_t seq_stride;          /* elements; contiguous layout only */
+  int64_t seq_stride;          /* elements (bytes for fp8); contiguous layout only */
   int32_t block_size;          /* 0 = contiguous */
   const int32_t *block_table;  /* [B][max_blocks], paged layout only */
   int32_t max_blocks;
   const int32_t *ctx_lens;     /* [B] */
 } mla_cache_t;
+
+/* Bytes of one cache row of the given dtype: (d_c + d_rope) * 4 or * 2 for
+ * fp32 / bf16, d_c + 2 d_rope + 4 d_c/128 for MLA_FP8_E4M3; -1 for invalid
+ * dims or dtype (fp8 with d_c not a multiple of 128 included). */
+int64_t mla_cache_row_bytes(const mla_dims_t *dims, mla_dtype_t dtype);
 
 /* Key absorption and query RoPE ([Huny] §3.1, §2.2; [Tbr8] §5.3).
  *   q_nope    [B][n_q][n_h][d_nope]   dtype dt
@@ -115,8 +136,9 @@ int64_t mla_num_partials(int32_t B, int32_t num_splits);
  * r = 0, lse = -inf.  Partials of sequence b occupy consecutive slots p in
  * order of their token ranges; the slot layout is an implementation detail
  * read by mla_combine.
- *   q_lat     [B][n_q][n_h][d_c]      cache dtype (from mla_absorb_q)
- *   q_pe      [B][n_q][n_h][d_rope]   cache dtype, rotated
+ *   q_lat     [B][n_q][n_h][d_c]      cache dtype, bf16 for an fp8 cache
+ *                                     (from mla_absorb_q)
+ *   q_pe      [B][n_q][n_h][d_rope]   as q_lat, rotated
  *   positions [B][n_q]                query j of sequence b attends to tokens
  *                                     t <= positions[b][j]
  *   u_part    [mla_num_partials(B, num_splits)][n_q][n_h][d_c]  fp32, out
@@ -161,7 +183,9 @@ mla_status_t mla_combine_out_proj(const mla_dims_t *dims, int32_t B, int32_t n_q
 /* Write n new tokens into the cache: token k belongs to sequence seq_ids[k]
  * at position positions[k]; its row becomes [c_kv_new[k] | RoPE(k_rope_new[k],
  * positions[k])] ([Huny] §2.2: the positional key is cached rotated).  Inputs
- * have the cache dtype; row k of c_kv_new starts at element k * c_kv_stride
+ * have the cache dtype (bf16 for an fp8 cache, whose rows are quantised as
+ * mla_cache_t states: per-tile power-of-two scale, codes rounded to nearest
+ * with ties to even); row k of c_kv_new starts at element k * c_kv_stride
  * and row k of k_rope_new at element k * k_rope_stride.  The caller makes
  * sure the destination rows exist (block table filled).  ctx_lens is not
  * read or updated. */
@@ -173,7 +197,7 @@ mla_status_t mla_cache_append(const mla_dims_t *dims, const mla_cache_t *cache, 
 /* mla_cache_append (n new tokens, positions new_positions) followed by
  * mla_absorb_q (B sequences, n_q query tokens, positions), with the same
  * results as the two calls made in that order on one stream.  For the V3
- * shapes (bf16, d_nope = 128, d_c a multiple of 256) with a bf16 cache both
+ * shapes (bf16, d_nope = 128, d_c a multiple of 256) with a bf16 or fp8 cache both
  * run in a single launch: a decode step's new rows cost no launch of their
  * own ([Huny] §2.2 for the cached row, §3.1 for the absorbed query).  Every
  * argument of both calls is checked before anything is enqueued; n = 0 or

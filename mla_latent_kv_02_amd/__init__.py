@@ -9,6 +9,7 @@ from ._binding import (  # noqa: F401
     BlockPool,
     EXPORTED,
     F32,
+    FP8_E4M3,
     LIB_PATH,
     Dims,
     LatentCache,
@@ -27,6 +28,7 @@ from ._binding import (  # noqa: F401
     mla_o_proj,
     mla_fold_q,
     mla_absorb_q_folded,
+    mla_cache_row_bytes,
 )
 
 __version__ = "0.1.0"

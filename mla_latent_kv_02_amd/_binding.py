@@ -15,10 +15,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmla.so")
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP, MLA_ERR_OUT_OF_BLOCKS = 0, 1, 2, 3, 4
-F32, BF16 = 0, 1
+F32, BF16, FP8_E4M3 = 0, 1, 2
 
 EXPORTED = ("mla_absorb_q", "mla_decode", "mla_combine", "mla_out_proj", "mla_combine_out_proj",
-            "mla_cache_append", "mla_append_absorb_q", "mla_num_partials", "mla_status_string", "mla_version",
+            "mla_cache_append", "mla_append_absorb_q", "mla_num_partials", "mla_cache_row_bytes",
+            "mla_status_string", "mla_version",
             "mla_block_pool_bytes", "mla_block_pool_init", "mla_block_pool_reserve", "mla_block_pool_reserve_all",
             "mla_block_pool_release", "mla_fold_out", "mla_out_proj_folded", "mla_o_proj", "mla_fold_q",
             "mla_absorb_q_folded",
@@ -89,6 +90,8 @@ def load_library(path: str = LIB_PATH):
     lib.mla_block_pool_free_count.restype = ctypes.c_int32
     lib.mla_num_partials.argtypes = [I32, I32]
     lib.mla_num_partials.restype = ctypes.c_int64
+    lib.mla_cache_row_bytes.argtypes = [DP, ctypes.c_int]
+    lib.mla_cache_row_bytes.restype = ctypes.c_int64
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_version.restype = ctypes.c_char_p
@@ -112,13 +115,30 @@ class Dims:
 
 @dataclasses.dataclass
 class LatentCache:
-    """Device latent cache: ``data`` is [B][S_max][d_c+d_rope] (contiguous) or
-    [n_blocks][block_size][d_c+d_rope] (paged, with ``block_table`` [B][max_blocks]);
-    ``ctx_lens`` [B] int32."""
+    """Device latent cache: ``data`` is [B][S_max][row] (contiguous) or
+    [n_blocks][block_size][row] (paged, with ``block_table`` [B][max_blocks]);
+    ``ctx_lens`` [B] int32.  fp32 / bf16 rows hold d_c + d_rope elements; a
+    uint8 ``data`` tensor is an fp8 e4m3 cache whose rows are
+    mla_cache_row_bytes(dims, FP8_E4M3) bytes (codes | bf16 key | fp32 scales)."""
     data: "torch.Tensor"
     ctx_lens: "torch.Tensor"
     block_table: Optional["torch.Tensor"] = None
     block_size: int = 0
+
+    @property
+    def fp8(self) -> bool:
+        return self.data.dtype == _torch().uint8
+
+    @property
+    def query_dtype(self):
+        """dtype of the queries, new rows and q_lat / q_pe that go with this cache."""
+        return _torch().bfloat16 if self.fp8 else self.data.dtype
+
+    def row_width(self, dims: "Dims") -> int:
+        """Last dimension ``data`` must have for ``dims``."""
+        if self.fp8:
+            return mla_cache_row_bytes(dims, FP8_E4M3)
+        return dims.d_c + dims.d_rope
 
     def _c(self) -> _Cache:
         _dev(self.data, "cache.data")
@@ -129,11 +149,11 @@ class LatentCache:
             _dev(self.block_table, "cache.block_table", _torch().int32)
             if self.data.dim() != 3 or self.data.shape[1] != self.block_size:
                 raise ValueError("paged cache data must be [n_blocks][block_size][row]")
-            return _Cache(_dtype(self.data), self.data.data_ptr(), 0, self.block_size,
+            return _Cache(_cache_dtype(self.data), self.data.data_ptr(), 0, self.block_size,
                           self.block_table.data_ptr(), self.block_table.shape[1], self.ctx_lens.data_ptr())
         if self.data.dim() != 3:
             raise ValueError("contiguous cache data must be [B][S_max][row]")
-        return _Cache(_dtype(self.data), self.data.data_ptr(), self.data.stride(0), 0, None, 0,
+        return _Cache(_cache_dtype(self.data), self.data.data_ptr(), self.data.stride(0), 0, None, 0,
                       self.ctx_lens.data_ptr())
 
 
@@ -149,6 +169,19 @@ def _dtype(t) -> int:
     if t.dtype == torch.bfloat16:
         return BF16
     raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _cache_dtype(t) -> int:
+    return FP8_E4M3 if t.dtype == _torch().uint8 else _dtype(t)
+
+
+def mla_cache_row_bytes(dims: "Dims", dtype: int) -> int:
+    """Bytes of one cache row (mla_cache_row_bytes); raises for an invalid pair."""
+    d = dims._c()
+    n = int(load_library().mla_cache_row_bytes(ctypes.byref(d), dtype))
+    if n < 0:
+        raise ValueError(f"no cache row of dtype {dtype} for {dims}")
+    return n
 
 
 def _dev(t, name, dtype=None):
@@ -207,8 +240,8 @@ def mla_decode(dims: Dims, q_lat, q_pe, cache: LatentCache, positions, num_split
                u_part, lse_part, stream=None) -> None:
     B, n_q = q_lat.shape[0], q_lat.shape[1]
     torch = _torch()
-    _dev(q_lat, "q_lat", cache.data.dtype)
-    _dev(q_pe, "q_pe", cache.data.dtype)
+    _dev(q_lat, "q_lat", cache.query_dtype)
+    _dev(q_pe, "q_pe", cache.query_dtype)
     _dev(positions, "positions", torch.int32)
     _dev(u_part, "u_part", torch.float32)
     _dev(lse_part, "lse_part", torch.float32)
@@ -216,8 +249,8 @@ def mla_decode(dims: Dims, q_lat, q_pe, cache: LatentCache, positions, num_split
     _shape(q_pe, "q_pe", (B, n_q, dims.n_h, dims.d_rope))
     _shape(positions, "positions", (B, n_q))
     _shape(cache.ctx_lens, "cache.ctx_lens", (B,))
-    if cache.data.shape[-1] != dims.d_c + dims.d_rope:
-        raise ValueError("cache rows must hold d_c + d_rope elements")
+    if cache.data.shape[-1] != cache.row_width(dims):
+        raise ValueError(f"cache rows must be {cache.row_width(dims)} wide")
     if cache.block_size == 0 and cache.data.shape[0] < B:
         raise ValueError("contiguous cache holds fewer sequences than B")
     slots = mla_num_partials(B, num_splits)
@@ -320,8 +353,9 @@ def _append_checks(dims: Dims, cache: LatentCache, seq_ids, positions, c_kv_new,
     _dev(positions, "positions", torch.int32)
     _shape(positions, "positions", (n,))
     for t, name in ((c_kv_new, "c_kv_new"), (k_rope_new, "k_rope_new")):
-        if not t.is_cuda or t.dtype != cache.data.dtype or t.dim() != 2 or t.stride(1) != 1:
-            raise ValueError(f"{name} must be a [n][width] device tensor of the cache dtype with unit column stride")
+        if not t.is_cuda or t.dtype != cache.query_dtype or t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(f"{name} must be a [n][width] device tensor of dtype {cache.query_dtype} "
+                             "with unit column stride")
         if t.shape[0] != n:
             raise ValueError(f"{name} must have {n} rows")
     if c_kv_new.shape[1] != dims.d_c or k_rope_new.shape[1] != dims.d_rope:

@@ -1,6 +1,6 @@
-// Decode attention for any head geometry and for fp32 or bf16 caches, in fp32
-// arithmetic.  Used where the MFMA kernel's fixed shape (bf16, d_c = 512,
-// d_rope = 64, heads in groups of 32) does not apply.
+// Decode attention for any head geometry and for fp32, bf16 or fp8 caches, in
+// fp32 arithmetic.  Used where the MFMA kernel's fixed shape (bf16 or fp8,
+// d_c = 512, d_rope = 64, heads in groups of 32) does not apply.
 //
 // Same method as the MFMA kernel ([Huny] = "Multi-Head Latent Attention(MLA)
 // 아키텍처 해부", Huny's Dev Blog, §2.2 and §3): scores against the cached rows
@@ -11,6 +11,7 @@
 
 #include "mla_device.h"
 #include "launch.h"
+#include "fp8.h"
 
 namespace mla {
 namespace {
@@ -38,15 +39,44 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return r;
 }
 
+// Element access to one cache row: latent element e (< d_c) and positional-key
+// element e (< d_rope), as fp32.  Queries have type Q.
 template <typename T>
+struct RowFmt {
+  using Q = T;
+  using Unit = T;   // unit of cache_row_offset
+  __device__ __forceinline__ static float lat(const Unit* row, int e, const DecodeParams&) {
+    return Elem<T>::load(row, e);
+  }
+  __device__ __forceinline__ static float rope(const Unit* row, int e, const DecodeParams& p) {
+    return Elem<T>::load(row, p.d_c + e);
+  }
+};
+// fp8 rows (bytes): e4m3 code times its tile's power-of-two scale (exact in
+// fp32); the positional key is bf16.
+struct Fp8Fmt {
+  using Q = uint16_t;
+  using Unit = unsigned char;
+  __device__ __forceinline__ static float lat(const Unit* row, int e, const DecodeParams& p) {
+    const float* scales = reinterpret_cast<const float*>(row + p.d_c + 2 * p.d_rope);
+    return e4m3_value<0>(row[e]) * scales[e / kFp8Tile];
+  }
+  __device__ __forceinline__ static float rope(const Unit* row, int e, const DecodeParams& p) {
+    return bf16_to_f32(reinterpret_cast<const uint16_t*>(row + p.d_c)[e]);
+  }
+};
+
+template <typename F>
 __global__ __launch_bounds__(NT) void decode_generic_kernel(DecodeParams p) {
+  using T = typename F::Unit;
+  using Q = typename F::Q;
   __shared__ float q_s[MAX_ROW];
   __shared__ float p_s[NT];
   __shared__ float red[4];
   __shared__ PlanScratch<NT> plan;
   const T* cache = static_cast<const T*>(p.cache.data);
-  const T* q_lat = static_cast<const T*>(p.q_lat);
-  const T* q_pe = static_cast<const T*>(p.q_pe);
+  const Q* q_lat = static_cast<const Q*>(p.q_lat);
+  const Q* q_pe = static_cast<const Q*>(p.q_pe);
   const int w = blockIdx.x;
   const int r = blockIdx.y;              // query row = j * n_h + i
   const int jq = r / p.n_h, ih = r % p.n_h;
@@ -57,8 +87,8 @@ __global__ __launch_bounds__(NT) void decode_generic_kernel(DecodeParams p) {
   for_each_segment<NT>(p.ctx_lens, p.B, p.num_splits, w, &plan, [&](int b, int t0, int t1, int slot) {
     const int64_t qrow = ((int64_t)b * p.n_q + jq) * p.n_h + ih;
     for (int e = tid; e < row; e += NT)
-      q_s[e] = e < p.d_c ? Elem<T>::load(q_lat, qrow * p.d_c + e)
-                         : Elem<T>::load(q_pe, qrow * p.d_rope + (e - p.d_c));
+      q_s[e] = e < p.d_c ? Elem<Q>::load(q_lat, qrow * p.d_c + e)
+                         : Elem<Q>::load(q_pe, qrow * p.d_rope + (e - p.d_c));
     const int qpos = p.positions[(int64_t)b * p.n_q + jq];
     const int limit = qpos + 1 < t1 ? qpos + 1 : t1;
     __syncthreads();
@@ -70,7 +100,8 @@ __global__ __launch_bounds__(NT) void decode_generic_kernel(DecodeParams p) {
       if (tok < limit) {
         const T* kr = cache + cache_row_offset(p.cache, b, tok);
         float dot = 0.f;
-        for (int e = 0; e < row; ++e) dot = fmaf(q_s[e], Elem<T>::load(kr, e), dot);
+        for (int e = 0; e < p.d_c; ++e) dot = fmaf(q_s[e], F::lat(kr, e, p), dot);
+        for (int e = 0; e < p.d_rope; ++e) dot = fmaf(q_s[p.d_c + e], F::rope(kr, e, p), dot);
         x = dot * scale_log2;
       }
       const float mt = block_max(x, red);
@@ -90,7 +121,7 @@ __global__ __launch_bounds__(NT) void decode_generic_kernel(DecodeParams p) {
 #pragma unroll
         for (int k = 0; k < MAX_DC_PER_THREAD; ++k) {
           const int d = tid + k * NT;
-          if (d < p.d_c) acc[k] = fmaf(pw, Elem<T>::load(kr, d), acc[k]);
+          if (d < p.d_c) acc[k] = fmaf(pw, F::lat(kr, d, p), acc[k]);
         }
       }
       __syncthreads();
@@ -117,10 +148,12 @@ __global__ __launch_bounds__(NT) void decode_generic_kernel(DecodeParams p) {
 hipError_t launch_decode_generic(const DecodeParams& p, hipStream_t stream) {
   if (p.d_c + p.d_rope > MAX_ROW || p.d_c > NT * MAX_DC_PER_THREAD) return hipErrorInvalidValue;
   dim3 grid(p.num_splits, p.n_q * p.n_h);
-  if (p.bf16)
-    hipLaunchKernelGGL(decode_generic_kernel<uint16_t>, grid, dim3(NT), 0, stream, p);
+  if (p.fp8)
+    hipLaunchKernelGGL(decode_generic_kernel<Fp8Fmt>, grid, dim3(NT), 0, stream, p);
+  else if (p.bf16)
+    hipLaunchKernelGGL(decode_generic_kernel<RowFmt<uint16_t>>, grid, dim3(NT), 0, stream, p);
   else
-    hipLaunchKernelGGL(decode_generic_kernel<float>, grid, dim3(NT), 0, stream, p);
+    hipLaunchKernelGGL(decode_generic_kernel<RowFmt<float>>, grid, dim3(NT), 0, stream, p);
   return hipGetLastError();
 }
 

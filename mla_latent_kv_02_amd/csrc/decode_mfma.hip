@@ -66,6 +66,16 @@ constexpr int CG_BYTES = T * 128;     // one chunk group of a stage: 32 tokens x
 constexpr int STAGE_BYTES = CGROUPS * CG_BYTES;   // 36864
 constexpr int LOADS_PER_STAGE = CGROUPS;          // 16-byte-per-lane loads per wave per stage
 constexpr float REF_HEADROOM = 64.f;  // log2 units a score may exceed its row's reference
+// fp8 cache rows: [512 e4m3 codes | 64 bf16 rotated k_rope | 4 fp32 scales]
+constexpr int RB16 = ROW * 2;                     // bytes of a bf16 row (1152)
+constexpr int RB8 = DC + 2 * DR + 4 * (DC / 128); // bytes of an fp8 row (656)
+constexpr int F8_ROPE = DC, F8_SCALE = DC + 2 * DR;   // byte offsets in an fp8 row
+constexpr int NRAW = 3;               // fp8: stages of raw rows in flight per wave
+// A wave's part of one raw fp8 stage: the codes of its 128-channel tile for
+// the 32 tokens (4 loads of 8 tokens x 128 B), the positional keys of tokens
+// 8w .. 8w+7 (1 load), the tile's scale of every token (1 load of 4 B per lane).
+constexpr int RAW_CODES = 0, RAW_ROPE = 4096, RAW_SCALE = 5120, RAW_WAVE_BYTES = 5376;
+constexpr int FP8_LOADS_PER_STAGE = 6;
 // Word 3 of a raw buffer resource on gfx9-class chips (32-bit data format, no
 // swizzle, offsets in bytes); words 0-2 carry the base and the byte range.
 constexpr int kBufferWord3 = 0x00020000;
@@ -92,11 +102,79 @@ struct __attribute__((aligned(16))) DecodeSmem {
   PlanScratch<NT> plan;
 };
 
+// fp8 caches: two bf16 stages (the layout above), filled by converting the
+// raw fp8 rows that each wave loads into its own part of a raw ring.
+struct __attribute__((aligned(16))) DecodeSmemFp8 {
+  unsigned char stage[2][STAGE_BYTES];
+  unsigned char raw[NRAW][4 * RAW_WAVE_BYTES];
+  bf16x8 pbuf[4][2][64];
+  int flag[4];
+  PlanScratch<NT> plan;
+};
+static_assert(sizeof(DecodeSmemFp8) <= 160 * 1024, "LDS budget");
+
 // Cache layouts the kernel is compiled for.
 enum Layout : int {
   kContiguous = 0,   // [B][seq_stride] rows; a sequence's rows (plus one stage) span < 4 GiB
   kPaged = 1,        // block table, block_size >= T (a stage meets at most two blocks)
   kAnyLayout = 2,    // any block size: per-token row lookup
+};
+
+// Paged addressing of consecutive stages of T tokens (block_size >= T, so a
+// stage meets at most two blocks, k0 from row r0 on, then k1).  Stages come in
+// order, T tokens apart, so (k0, r0) follows from the previous stage without a
+// division (a restart recomputes it).  The block ids come from a window of 64
+// ids, one per lane (`ids`), reloaded (one vector load; its wait also covers
+// the stage loads in flight) when a stage leaves it.  locate() gives the byte
+// offsets, from the resource base at block blk_lo, of the stage's rows: row
+// t < span + 1 of the stage is at off(t), rows past the segment end repeat its
+// last row (uint32 arithmetic, exact modulo 2^32).
+struct PagedCursor {
+  int ids, kbase;              // lane l holds the id of block kbase + l of the sequence
+  int ntok, nk, nr;            // the next stage's first token, its block index and row in it
+  uint32_t off0, off1;         // row r0 of block k0; block k1 shifted back by bs - r0 rows
+  int r0, span, bs;
+  uint32_t rb;                 // row bytes
+
+  __device__ __forceinline__ void init(int block_size, uint32_t row_bytes) {
+    kbase = INT_MIN / 2;         // no window loaded yet
+    ids = 0;
+    ntok = INT_MIN;              // next stage unknown
+    nk = nr = 0;
+    bs = block_size;
+    rb = row_bytes;
+  }
+  __device__ __forceinline__ void locate(const CacheView& c, int b, int tok0, int tok_end, int blk_lo, int lane,
+                                         uint32_t block_bytes) {
+    if (tok0 != ntok) {
+      nk = tok0 / bs;
+      nr = tok0 - nk * bs;
+    }
+    const int k0 = nk;
+    r0 = nr;
+    span = T - 1 < tok_end - 1 - tok0 ? T - 1 : tok_end - 1 - tok0;   // last row, from tok0
+    const int k1 = k0 + (r0 + span >= bs ? 1 : 0);
+    ntok = tok0 + T;
+    nr = r0 + T;
+    if (nr >= bs) {   // block_size >= T: at most one block boundary per stage
+      nr -= bs;
+      ++nk;
+    }
+    if (k0 < kbase || k1 - kbase >= 64) {
+      kbase = k0;
+      const int k = k0 + lane;
+      ids = k <= (tok_end - 1) / bs ? c.block_table[(int64_t)b * c.max_blocks + k] : 0;
+    }
+    const int blk0 = __builtin_amdgcn_readlane(ids, k0 - kbase);
+    const int blk1 = __builtin_amdgcn_readlane(ids, k1 - kbase);
+    off0 = (uint32_t)(blk0 - blk_lo) * block_bytes + (uint32_t)r0 * rb;
+    off1 = (uint32_t)(blk1 - blk_lo) * block_bytes - (uint32_t)(bs - r0) * rb;
+  }
+  // byte offset of stage row t (clamped to the segment's last row) plus `byte`
+  __device__ __forceinline__ uint32_t row(int t, uint32_t byte) const {
+    const int tt = t < span ? t : span;
+    return (r0 + tt < bs ? off0 : off1) + (uint32_t)tt * rb + byte;
+  }
 };
 
 // Issues this wave's share of the global->LDS loads of one stage: stage
@@ -122,8 +200,7 @@ struct StageLoader {
   int lane_off;                // contiguous: byte offset of the lane within a stage
   int tt, chunk_off;
   int lane_;
-  int ids, kbase;              // paged: lane l holds the id of block kbase + l of the sequence
-  int ntok, nk, nr;            // paged: the next stage's first token, its block index and row in it
+  PagedCursor pc;
   uint32_t block_bytes;
 
   __device__ __forceinline__ void init(const CacheView& cache, int b_, int tok_end_, int wave, int lane,
@@ -133,23 +210,20 @@ struct StageLoader {
     tok_end = tok_end_;
     blk_lo = blk_lo_;
     lane_ = lane;
-    kbase = INT_MIN / 2;         // no window loaded yet
-    ids = 0;
-    ntok = INT_MIN;              // next stage unknown
-    nk = nr = 0;
     tt = 8 * wave + (lane >> 3);
     chunk_off = ((lane & 7) ^ swz(tt)) * 16;
     base = static_cast<const unsigned char*>(cache.data);
     if (LAYOUT == kContiguous) {
       base += (int64_t)b * cache.seq_stride * 2;
       rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(base), (short)0,
-                                               tok_end * (ROW * 2), kBufferWord3);
-      lane_off = tt * (ROW * 2) + chunk_off;
+                                               tok_end * RB16, kBufferWord3);
+      lane_off = tt * RB16 + chunk_off;
     } else if (LAYOUT == kPaged) {
-      block_bytes = (uint32_t)cache.block_size * (ROW * 2);
+      pc.init(cache.block_size, RB16);
+      block_bytes = (uint32_t)cache.block_size * RB16;
       rsrc = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<unsigned char*>(base + (int64_t)blk_lo * block_bytes), (short)0, (int)0xFFFFFFFF, kBufferWord3);
-      lane_off = tt * (ROW * 2) + chunk_off;
+      lane_off = tt * RB16 + chunk_off;
     }
   }
 
@@ -159,44 +233,12 @@ struct StageLoader {
   const unsigned char* rowp;
   __device__ __forceinline__ void prepare(int tok0) {
     if (LAYOUT == kContiguous) {
-      voff = (uint32_t)lane_off + (uint32_t)tok0 * (uint32_t)(ROW * 2);
+      voff = (uint32_t)lane_off + (uint32_t)tok0 * (uint32_t)RB16;
       return;
     }
     if (LAYOUT == kPaged) {
-      // The stage's tokens lie in at most two blocks, k0 (from row r0 on) and
-      // k1.  Stages come in order, 32 tokens apart, so (k0, r0) follows from
-      // the previous stage without a division (a restart recomputes it).  The
-      // block ids come from the window of 64 ids in `ids`, reloaded (one
-      // vector load; its wait also covers the stage loads in flight) when the
-      // stage leaves it.  Rows past the segment end repeat its last row.
-      const int bs = c->block_size;
-      if (tok0 != ntok) {
-        nk = tok0 / bs;
-        nr = tok0 - nk * bs;
-      }
-      const int k0 = nk, r0 = nr;
-      const int span = T - 1 < tok_end - 1 - tok0 ? T - 1 : tok_end - 1 - tok0;   // last row, from tok0
-      const int k1 = k0 + (r0 + span >= bs ? 1 : 0);
-      ntok = tok0 + T;
-      nr = r0 + T;
-      if (nr >= bs) {   // block_size >= T: at most one block boundary per stage
-        nr -= bs;
-        ++nk;
-      }
-      if (k0 < kbase || k1 - kbase >= 64) {
-        kbase = k0;
-        const int k = k0 + lane_;
-        ids = k <= (tok_end - 1) / bs ? c->block_table[(int64_t)b * c->max_blocks + k] : 0;
-      }
-      const int blk0 = __builtin_amdgcn_readlane(ids, k0 - kbase);
-      const int blk1 = __builtin_amdgcn_readlane(ids, k1 - kbase);
-      // byte offsets from the resource base: row r0 + t of block k0 for t < bs - r0,
-      // else row t - (bs - r0) of block k1 (uint32 arithmetic, exact modulo 2^32)
-      const uint32_t off0 = (uint32_t)(blk0 - blk_lo) * block_bytes + (uint32_t)r0 * (ROW * 2);
-      const uint32_t off1 = (uint32_t)(blk1 - blk_lo) * block_bytes - (uint32_t)(bs - r0) * (ROW * 2);
-      const int t = tt < span ? tt : span;
-      const uint32_t lo = tt < span ? (uint32_t)lane_off : (uint32_t)(span * (ROW * 2) + chunk_off);
-      voff = lo + (r0 + t < bs ? off0 : off1);
+      pc.locate(*c, b, tok0, tok_end, blk_lo, lane_, block_bytes);
+      voff = pc.row(tt, chunk_off);
       return;
     }
     int tok = tok0 + tt;
@@ -217,12 +259,152 @@ struct StageLoader {
   }
 };
 
+// The fp8 counterpart of StageLoader: wave w loads, for one stage, exactly
+// the bytes it will convert (so its raw ring needs no workgroup barrier):
+//   loads 0-3: codes of tile w, tokens 8i + lane/8, 16 bytes at 128w + 16(lane%8)
+//              (8 lanes read 128 contiguous bytes of a row);
+//   load 4:    positional key of token 8w + lane/8, chunk (lane%8) ^ s(token)
+//              (already in its bf16 stage slot order);
+//   load 5:    scale of tile w of token lane%32 (4 bytes; lanes 32-63 repeat).
+// LDS destination: the wave's part of a raw stage, 1 KiB per load in lane
+// order (the scale load 256 B).  Rows past the segment end read as zeros
+// (contiguous) or repeat its last row (paged, generic), as for bf16 rows.
+template <int LAYOUT>
+struct Fp8Loader {
+  const unsigned char* base;
+  __amdgpu_buffer_rsrc_t rsrc;
+  const CacheView* c;
+  int b, tok_end, blk_lo, lane_, wave_;
+  PagedCursor pc;
+  uint32_t block_bytes;
+  uint32_t lc[3];              // contiguous: lane offsets of the codes, key and scale loads in a stage
+  uint32_t sbase;              // contiguous: byte offset of the stage's first row
+  uint32_t rowidx[FP8_LOADS_PER_STAGE];   // generic layout: row of load i, counted from the cache start
+
+  __device__ __forceinline__ int token(int i) const {   // stage token of load i for this lane
+    return i < 4 ? 8 * i + (lane_ >> 3) : (i == 4 ? 8 * wave_ + (lane_ >> 3) : (lane_ & 31));
+  }
+  __device__ __forceinline__ uint32_t byte(int i) const {   // byte offset of load i in its row
+    return i < 4 ? 128 * wave_ + 16 * (lane_ & 7)
+                 : (i == 4 ? F8_ROPE + 16 * ((lane_ & 7) ^ swz(8 * wave_ + (lane_ >> 3))) : F8_SCALE + 4 * wave_);
+  }
+  __device__ __forceinline__ void init(const CacheView& cache, int b_, int tok_end_, int wave, int lane,
+                                       int blk_lo_) {
+    c = &cache;
+    b = b_;
+    tok_end = tok_end_;
+    blk_lo = blk_lo_;
+    lane_ = lane;
+    wave_ = wave;
+    base = static_cast<const unsigned char*>(cache.data);
+    if (LAYOUT == kContiguous) {
+      base += (int64_t)b * cache.seq_stride;    // bytes
+      rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(base), (short)0, tok_end * RB8,
+                                               kBufferWord3);
+#pragma unroll
+      for (int k = 0; k < 3; ++k) lc[k] = (uint32_t)token(k == 0 ? 0 : k + 3) * RB8 + byte(k == 0 ? 0 : k + 3);
+    } else if (LAYOUT == kPaged) {
+      pc.init(cache.block_size, RB8);
+      block_bytes = (uint32_t)cache.block_size * RB8;
+      rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<unsigned char*>(base + (int64_t)blk_lo * block_bytes), (short)0, (int)0xFFFFFFFF, kBufferWord3);
+    }
+  }
+  // per-stage state: uniform values only, except the generic layout's pointers
+  __device__ __forceinline__ void prepare(int tok0) {
+    if (LAYOUT == kContiguous) {
+      sbase = (uint32_t)tok0 * RB8;
+    } else if (LAYOUT == kPaged) {
+      pc.locate(*c, b, tok0, tok_end, blk_lo, lane_, block_bytes);
+    } else {
+#pragma unroll
+      for (int i = 0; i < FP8_LOADS_PER_STAGE; ++i) {
+        int tok = tok0 + token(i);
+        tok = tok < tok_end ? tok : tok_end - 1;
+        rowidx[i] = (uint32_t)(cache_row_offset(*c, b, tok) / RB8);   // rows counted in bytes
+      }
+    }
+  }
+  // load i of the prepared stage into `dst`, this wave's part of a raw stage
+  __device__ __forceinline__ void issue_cg(int i, unsigned char* dst, int) {
+    lds_void* d = (lds_void*)(dst + (i < 4 ? RAW_CODES + 1024 * i : (i == 4 ? RAW_ROPE : RAW_SCALE)));
+    if (LAYOUT == kContiguous || LAYOUT == kPaged) {
+      int vo, so;
+      if (LAYOUT == kContiguous) {
+        vo = (int)lc[i < 4 ? 0 : i - 3];
+        so = (int)(sbase + (i < 4 ? 8u * i * RB8 : 0u));
+      } else {
+        vo = (int)pc.row(token(i), byte(i));
+        so = 0;
+      }
+      if (i < 5) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, d, 16, vo, so, 0, 0);
+      else __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, d, 4, vo, so, 0, 0);
+    } else {
+      const unsigned char* src = base + (uint64_t)rowidx[i] * RB8 + byte(i);
+      if (i < 5) __builtin_amdgcn_global_load_lds(src, d, 16, 0, 0);
+      else __builtin_amdgcn_global_load_lds(src, d, 4, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void issue(int tok0, unsigned char* dst, int wave) {
+    prepare(tok0);
+#pragma unroll
+    for (int i = 0; i < FP8_LOADS_PER_STAGE; ++i) issue_cg(i, dst, wave);
+  }
+};
+
+// Converts this wave's part of a raw fp8 stage into the bf16 stage `bf`: the
+// 128 latents of tile w (chunk groups 2w, 2w+1) of all 32 tokens, and the
+// positional keys of tokens 8w .. 8w+7 (chunk group 8).  A lane converts the
+// 16-byte pieces it loaded: piece i holds latents 128w + 16(lane%8) .. +16 of
+// token 8i + lane/8, i.e. bf16 chunks 2(lane%8) and 2(lane%8)+1 of the tile.
+// Codes times the power-of-two scale are exact in bf16 (3 of its 7 mantissa
+// bits; the scaled conversion applies the scale as an exponent offset).
+__device__ __forceinline__ void convert_fp8_stage(const unsigned char* rw, unsigned char* bf, int wave, int lane) {
+  typedef __attribute__((address_space(3))) const u32x4 lds_cu32x4;
+  typedef __attribute__((address_space(3))) const float lds_cf32;
+  typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  const auto L = [](const unsigned char* p) { return (__attribute__((address_space(3))) unsigned char*)p; };
+  // The lane-dependent offsets below are cheap to form; an opaque copy of the
+  // lane index keeps the compiler from hoisting them out of the stage loop,
+  // where they would hold registers for the whole loop.
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  const int p8 = ln & 7, tq = ln >> 3;
+  // token 8i + tq: s(8i + tq) = s(tq) for even i and s(tq) ^ 2 for odd i
+  // (P[x + 4] = P[x] ^ 2), so the write slots of both chunks of every piece
+  // are x, x^1, x^2, x^3 with x = 2(p8 % 4) ^ s(tq), plus 1024 i.
+  const int x = (2 * (p8 & 3)) ^ swz(tq);
+  unsigned char* wbase = bf + (2 * wave + (p8 >> 2)) * CG_BYTES + tq * 128;
+  const unsigned char* rbase = rw + RAW_CODES + 16 * ln;
+  const unsigned char* sbase = rw + RAW_SCALE + 4 * tq;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float sc = *(lds_cf32*)L(sbase + 32 * i);
+    const u32x4 w = *(lds_cu32x4*)L(rbase + 1024 * i);
+    bf16x8 o[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const auto a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h], sc, false);
+      const auto a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h], sc, true);
+      const auto a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h + 1], sc, false);
+      const auto a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h + 1], sc, true);
+      o[h] = bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+    }
+    const int xi = x ^ (i & 1 ? 2 : 0);
+    *(lds_bf16x8*)L(wbase + 1024 * i + (xi << 4)) = o[0];
+    *(lds_bf16x8*)L(wbase + 1024 * i + ((xi ^ 1) << 4)) = o[1];
+  }
+  *(lds_u32x4*)L(bf + 8 * CG_BYTES + 1024 * wave + 16 * ln) = *(lds_cu32x4*)L(rw + RAW_ROPE + 16 * ln);
+}
+
 // Paged cache, tokens t0..t1-1 of sequence b: the lowest block id among their
 // blocks, and whether all of them lie within 4 GiB of it (so that 32-bit
 // buffer offsets from it reach every row).  Each wave reads the block table
 // entries itself and reduces them across its lanes; the result is the same in
 // every wave.
-__device__ __forceinline__ bool paged_span(const CacheView& c, int b, int t0, int t1, int lane, int* blk_lo) {
+__device__ __forceinline__ bool paged_span(const CacheView& c, int b, int t0, int t1, int lane, int row_bytes,
+                                           int* blk_lo) {
   const int bs = c.block_size;
   const int k0 = t0 / bs, k1 = (t1 - 1) / bs;
   int lo = INT_MAX, hi = INT_MIN;
@@ -238,7 +420,7 @@ __device__ __forceinline__ bool paged_span(const CacheView& c, int b, int t0, in
     hi = oh > hi ? oh : hi;
   }
   *blk_lo = __builtin_amdgcn_readfirstlane(lo);
-  const int64_t span = ((int64_t)__builtin_amdgcn_readfirstlane(hi) - *blk_lo + 1) * bs * (ROW * 2);
+  const int64_t span = ((int64_t)__builtin_amdgcn_readfirstlane(hi) - *blk_lo + 1) * bs * row_bytes;
   return span <= (int64_t)0xFFFFFFFF;
 }
 
@@ -254,6 +436,8 @@ __device__ __forceinline__ void lds_barrier() {
 // vmcnt[5:4] << 14) that wait on vector memory only.  Issued through the
 // builtin so that the compiler's own wait insertion sees them.
 constexpr int kWaitVm0 = 0x0F70, kWaitVm9 = 0x0F79, kWaitVm18 = 0x4F72;
+constexpr int kWaitVm6 = 0x0F76, kWaitVm12 = 0x0F7C;   // fp8: 6 loads per stage
+static_assert(FP8_LOADS_PER_STAGE == 6 && NRAW == 3, "fp8 wait counts assume 6 loads per stage, 3 raw stages");
 
 // O += A . B for one 32x32 block of the PV product, with the accumulator pinned
 // to AGPRs.  O needs all 256 AGPRs; the QK^T accumulators (built-in MFMAs,
@@ -294,10 +478,18 @@ static_assert(LOADS_PER_STAGE == 9 && NSTAGE == 4, "wait counts assume 9 loads p
 // reference by more than REF_HEADROOM (log2 units; weights stay below
 // 2^REF_HEADROOM, far from fp32/bf16 overflow), the segment is computed again
 // with the row's true maximum as the reference.
-template <int LAYOUT>
+//
+// fp8 caches (FP8): the bf16 stages alternate between two buffers; wave w
+// converts tile w of raw stage it+2 into the buffer of stage it right after
+// its own PV of stage it (which reads only tile w of that buffer, and the QK
+// reads of it ended at the previous iteration's second barrier), so the
+// conversion needs no barrier of its own: the next iteration's first barrier
+// publishes it.  Raw stage it+1+NRAW is loaded during the QK of iteration it.
+template <int LAYOUT, bool FP8>
 __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
-  __shared__ DecodeSmem smem;
-  DecodeSmem* sm = &smem;
+  using Smem = std::conditional_t<FP8, DecodeSmemFp8, DecodeSmem>;
+  __shared__ Smem smem;
+  Smem* sm = &smem;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -346,8 +538,25 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
     // The query loads are not waited for here: the first stages' loads are
     // issued behind them, and the wait for stage 0 (vector-memory counter,
     // completed in order) covers them too.
-    StageLoader<SL> ld;
+    std::conditional_t<FP8, Fp8Loader<SL>, StageLoader<SL>> ld;
     ld.init(a.cache, b, t1, wave, lane, blk_lo);
+    // bf16 stage s (ring of NSTAGE, or two buffers for fp8); this wave's part of raw stage s
+    auto stage_buf = [&](int s) -> unsigned char* {
+      if constexpr (FP8) return sm->stage[s & 1];
+      else return sm->stage[s % NSTAGE];
+    };
+    auto raw_buf = [&](int s) -> unsigned char* {
+      if constexpr (FP8) return sm->raw[s % NRAW] + wave * RAW_WAVE_BYTES;
+      else return nullptr;
+    };
+    // fp8: wait until raw stage s (of stages issued up to `last`) has landed, then convert it
+    auto convert_stage = [&](int s, int last) {
+      const int after = last - s;   // stages issued after s, still allowed in flight
+      if (after >= 2) __builtin_amdgcn_s_waitcnt(kWaitVm12);
+      else if (after == 1) __builtin_amdgcn_s_waitcnt(kWaitVm6);
+      else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      convert_fp8_stage(raw_buf(s), stage_buf(s), wave, lane);
+    };
     // per-lane LDS byte offsets that do not depend on the stage
     const int sw_qk = swz(l32);
     int qk_off[4];
@@ -395,9 +604,15 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
         for (int hb = 0; hb < 4; ++hb) o[mb][hb] = f32x16{};
       l_run = 0.f;
       bool over = false;
+      if constexpr (!FP8) {
 #pragma unroll
-      for (int s = 0; s < NSTAGE - 1; ++s)
-        if (s < nst) ld.issue(t0 + s * T, sm->stage[s], wave);
+        for (int s = 0; s < NSTAGE - 1; ++s)
+          if (s < nst) ld.issue(t0 + s * T, stage_buf(s), wave);
+      } else {
+#pragma unroll
+        for (int s = 0; s < NRAW; ++s)
+          if (s < nst) ld.issue(t0 + s * T, raw_buf(s), wave);
+      }
 
       // Pipeline, iteration it: publish the weights of stage it (computed in
       // the previous iteration), S^T of stage it+1 (MFMA only), then PV of
@@ -422,7 +637,11 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
           const bf16x8 kk = kring[ks % PF];
           if (ks + PF < KSTEPS) kring[ks % PF] = rd_k(sb, ks + PF);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qreg[ks], acc, 0, 0, 0);
-          if (LOADS && (ks & 3) == 1) ld.issue_cg(ks >> 2, ldst, wave);
+          if constexpr (LOADS && !FP8) {
+            if ((ks & 3) == 1) ld.issue_cg(ks >> 2, ldst, wave);
+          } else if constexpr (LOADS) {
+            if (ks % 6 == 1) ld.issue_cg(ks / 6, ldst, wave);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
         s_nx = acc;
@@ -504,10 +723,21 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
       auto lane_lim = [&](int tok0) { return limit - tok0 - 4 * h; };
 
       // ---- prologue: scores and weights of stage 0
-      wait_stages_in_flight(nst - 1 < NSTAGE - 2 ? nst - 1 : NSTAGE - 2);
+      if constexpr (!FP8) {
+        wait_stages_in_flight(nst - 1 < NSTAGE - 2 ? nst - 1 : NSTAGE - 2);
+      } else {
+        // stages 0 and 1 into the two bf16 buffers; raw stage NRAW reuses stage 0's slot
+        int last = nst - 1 < NRAW - 1 ? nst - 1 : NRAW - 1;
+        convert_stage(0, last);
+        if (NRAW < nst) {
+          ld.issue(t0 + NRAW * T, raw_buf(NRAW), wave);
+          last = NRAW;
+        }
+        if (nst > 1) convert_stage(1, last);
+      }
       lds_barrier();
       if (active && t0 < limit) {
-        qk(sm->stage[0], NoLoads{}, nullptr);
+        qk(stage_buf(0), NoLoads{}, nullptr);
         const int lim = lane_lim(t0);
 #pragma unroll
         for (int k = 0; k < PIECES_MASKED; ++k) sm_piece(k, lim);
@@ -546,35 +776,50 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
       auto iteration = [&](int it, auto visible_tag) {
         constexpr bool VISIBLE = decltype(visible_tag)::value;
         const bool has_next = it + 1 < nst;
-        // addresses of stage it+3 first, ahead of the waits (a paged cache takes
-        // its block ids from the register window, reloaded now and then)
-        const bool do_load = it + NSTAGE - 1 < nst;
-        if (do_load) ld.prepare(t0 + (it + NSTAGE - 1) * T);
-        if (has_next) wait_stages_in_flight(it + 2 < nst ? 1 : 0);   // stage it+1 resident
-        lds_barrier();   // every wave is done with the weights of stage it-1
+        // addresses of the stage to load first, ahead of the waits (a paged cache
+        // takes its block ids from the register window, reloaded now and then):
+        // bf16 stage it+3 into the ring slot stage it-1 freed; fp8 raw stage
+        // it+1+NRAW into the raw slot of stage it+1 (converted last iteration)
+        const int ld_stage = FP8 ? it + 1 + NRAW : it + NSTAGE - 1;
+        // fp8 rows in the generic layout: the 6 loads go out at once (their
+        // per-lane rows would otherwise stay live through the QK chain)
+        constexpr bool kIssueNow = FP8 && SL == kAnyLayout;
+        const bool do_load = ld_stage < nst;
+        if (do_load) {
+          if constexpr (kIssueNow) ld.issue(t0 + ld_stage * T, raw_buf(ld_stage), wave);
+          else ld.prepare(t0 + ld_stage * T);
+        }
+        if constexpr (!FP8) {
+          if (has_next) wait_stages_in_flight(it + 2 < nst ? 1 : 0);   // stage it+1 resident
+        }
+        lds_barrier();   // every wave is done with the weights of stage it-1 (fp8: and
+                         // has converted its part of stage it+1)
         // ------------ publish the weights of stage it (B-operand layout, per k-step)
         sm->pbuf[wave][0][lane] = pb[0];
         sm->pbuf[wave][1][lane] = pb[1];
         pb[0] = bf16x8{};
         pb[1] = bf16x8{};
-        // stage it+3 goes into the slot stage it-1 freed; its loads ride along
-        // with the MFMAs of S^T(it+1) when there are any
-        unsigned char* ldst = sm->stage[(it + NSTAGE - 1) % NSTAGE];
+        // the loads ride along with the MFMAs of S^T(it+1) when there are any
+        unsigned char* ldst = FP8 ? raw_buf(ld_stage) : stage_buf(ld_stage);
         const int tok_nx = t0 + (it + 1) * T;
         const bool qk_next = VISIBLE || (active && has_next && tok_nx < limit);    // scores of stage it+1
         if (qk_next) {
-          if (do_load) qk(sm->stage[(it + 1) % NSTAGE], WithLoads{}, ldst);
-          else qk(sm->stage[(it + 1) % NSTAGE], NoLoads{}, nullptr);
-        } else if (do_load) {
+          if (do_load && !kIssueNow) qk(stage_buf(it + 1), WithLoads{}, ldst);
+          else qk(stage_buf(it + 1), NoLoads{}, nullptr);
+        } else if (do_load && !kIssueNow) {
 #pragma unroll
-          for (int cg = 0; cg < CGROUPS; ++cg) ld.issue_cg(cg, ldst, wave);
+          for (int cg = 0; cg < (FP8 ? FP8_LOADS_PER_STAGE : CGROUPS); ++cg) ld.issue_cg(cg, ldst, wave);
         }
         lds_barrier();   // weights of stage it visible to all waves
-        const unsigned char* sb = sm->stage[it % NSTAGE];
+        const unsigned char* sb = stage_buf(it);
         mt = -INFINITY;
         psum[0] = psum[1] = 0.f;
         pv_stage(sb, visible_tag, qk_next ? lane_lim(tok_nx) : INT_MIN);
         l_run += psum[0] + psum[1];
+        if constexpr (FP8) {
+          // stage it+2 into the buffer of stage it (this wave's tile is done)
+          if (it + 2 < nst) convert_stage(it + 2, it + 1 + NRAW < nst - 1 ? it + 1 + NRAW : nst - 1);
+        }
       };
       // Iterations whose next stage is entirely visible (stage it+1 ends at or
       // before the limit) take the unmasked schedule; every wave runs the same
@@ -630,7 +875,7 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
       segment(Contig{}, b, t0, t1, slot, 0);
     } else if constexpr (LAYOUT == kPaged) {
       int blk_lo;
-      if (paged_span(a.cache, b, t0, t1, lane, &blk_lo)) segment(Paged{}, b, t0, t1, slot, blk_lo);
+      if (paged_span(a.cache, b, t0, t1, lane, FP8 ? RB8 : RB16, &blk_lo)) segment(Paged{}, b, t0, t1, slot, blk_lo);
       else segment(Any{}, b, t0, t1, slot, 0);    // blocks 4 GiB or more apart
     } else {
       segment(Any{}, b, t0, t1, slot, 0);
@@ -640,7 +885,20 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
 
 }  // namespace
 
-int decode_mfma_smem_bytes() { return (int)sizeof(DecodeSmem); }
+int decode_mfma_smem_bytes(bool fp8) { return fp8 ? (int)sizeof(DecodeSmemFp8) : (int)sizeof(DecodeSmem); }
+
+template <bool FP8>
+static void launch_decode_layout(const DecodeArgs& a, const DecodeParams& p, int grid, hipStream_t stream) {
+  const int64_t rb = FP8 ? RB8 : RB16;
+  const int64_t stride_bytes = p.cache.seq_stride * (FP8 ? 1 : 2);
+  // buffer offsets are 32-bit: a sequence plus one stage of overrun must fit
+  if (p.cache.block_size == 0 && stride_bytes + (int64_t)T * rb <= (int64_t)0xFFFFFFFF)
+    hipLaunchKernelGGL((decode_mfma_kernel<kContiguous, FP8>), dim3(grid), dim3(NT), 0, stream, a);
+  else if (p.cache.block_size >= T)
+    hipLaunchKernelGGL((decode_mfma_kernel<kPaged, FP8>), dim3(grid), dim3(NT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<kAnyLayout, FP8>), dim3(grid), dim3(NT), 0, stream, a);
+}
 
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
   DecodeArgs a;
@@ -659,13 +917,8 @@ hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
   a.n_work_pad = (p.num_splits + 7) / 8 * 8;
   a.scale_log2 = p.sm_scale * kLog2e;
   const int grid = a.n_work_pad * a.n_groups;
-  // buffer offsets are 32-bit: a sequence plus one stage of overrun must fit
-  if (p.cache.block_size == 0 && (p.cache.seq_stride + (int64_t)T * ROW) * 2 <= (int64_t)0xFFFFFFFF)
-    hipLaunchKernelGGL(decode_mfma_kernel<kContiguous>, dim3(grid), dim3(NT), 0, stream, a);
-  else if (p.cache.block_size >= T)
-    hipLaunchKernelGGL(decode_mfma_kernel<kPaged>, dim3(grid), dim3(NT), 0, stream, a);
-  else
-    hipLaunchKernelGGL(decode_mfma_kernel<kAnyLayout>, dim3(grid), dim3(NT), 0, stream, a);
+  if (p.fp8) launch_decode_layout<true>(a, p, grid, stream);
+  else launch_decode_layout<false>(a, p, grid, stream);
   return hipGetLastError();
 }
 

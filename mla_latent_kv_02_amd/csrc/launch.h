@@ -18,14 +18,15 @@ struct DecodeParams {
   float* u_part;
   float* lse_part;
   int B, n_q, n_h, d_c, d_rope, num_splits;
-  bool bf16;
+  bool bf16;             // bf16 cache (queries bf16)
+  bool fp8;              // fp8 e4m3 cache (queries bf16); neither: fp32
   float sm_scale;
 };
 
-// bf16 cache, d_c = 512, d_rope = 64, n_h % 32 == 0.
+// bf16 or fp8 cache, d_c = 512, d_rope = 64, n_h % 32 == 0.
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
-int decode_mfma_smem_bytes();
-// Any dims, fp32 or bf16 cache (fp32 arithmetic).
+int decode_mfma_smem_bytes(bool fp8);
+// Any dims, fp32, bf16 or fp8 cache (fp32 arithmetic).
 hipError_t launch_decode_generic(const DecodeParams& p, hipStream_t stream);
 
 struct CombineParams {
@@ -92,7 +93,8 @@ struct AppendParams {
   const void* k_rope;
   int64_t k_rope_stride;
   int d_c, d_rope;
-  bool bf16;
+  bool bf16;             // bf16 cache and inputs
+  bool fp8;              // fp8 cache, bf16 inputs; neither: fp32
   float rope_base;
 };
 hipError_t launch_cache_append(const AppendParams& p, hipStream_t stream);

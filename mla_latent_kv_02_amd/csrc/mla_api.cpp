@@ -19,13 +19,22 @@ bool dims_ok(const mla_dims_t* d) {
          isfinite(d->sm_scale) && d->sm_scale >= 0.f && isfinite(d->rope_base) && d->rope_base >= 0.f;
 }
 bool dtype_ok(mla_dtype_t t) { return t == MLA_F32 || t == MLA_BF16; }
+bool cache_dtype_ok(mla_dtype_t t) { return dtype_ok(t) || t == MLA_FP8_E4M3; }
+// bytes of one cache row; -1 if the dtype does not fit the dims
+int64_t row_bytes(const mla_dims_t* d, mla_dtype_t t) {
+  if (t == MLA_FP8_E4M3) return d->d_c % 128 ? -1 : (int64_t)d->d_c + 2 * d->d_rope + 4 * (d->d_c / 128);
+  if (t == MLA_BF16) return 2 * (int64_t)(d->d_c + d->d_rope);
+  if (t == MLA_F32) return 4 * (int64_t)(d->d_c + d->d_rope);
+  return -1;
+}
 float scale_of(const mla_dims_t* d) {
   return d->sm_scale > 0.f ? d->sm_scale : 1.0f / sqrtf((float)(d->d_nope + d->d_rope));
 }
 float base_of(const mla_dims_t* d) { return d->rope_base > 0.f ? d->rope_base : 10000.0f; }
 
 bool cache_ok(const mla_cache_t* c, const mla_dims_t* d) {
-  if (!c || !c->data || !c->ctx_lens || !dtype_ok(c->dtype)) return false;
+  if (!c || !c->data || !c->ctx_lens || !cache_dtype_ok(c->dtype)) return false;
+  if (row_bytes(d, c->dtype) < 0) return false;
   if (reinterpret_cast<uintptr_t>(c->data) % 16) return false;
   if (c->block_size < 0) return false;
   if (c->block_size > 0) return c->block_table && c->max_blocks >= 1;
@@ -39,7 +48,8 @@ mla::CacheView view_of(const mla_cache_t* c, const mla_dims_t* d) {
   v.block_table = c->block_table;
   v.block_size = c->block_size;
   v.max_blocks = c->max_blocks;
-  v.row = d->d_c + d->d_rope;
+  // elements per row; for fp8 rows (mixed element types) the unit is the byte
+  v.row = c->dtype == MLA_FP8_E4M3 ? (int32_t)row_bytes(d, c->dtype) : d->d_c + d->d_rope;
   return v;
 }
 
@@ -76,6 +86,7 @@ mla_status_t append_args(const mla_dims_t* dims, const mla_cache_t* cache, int32
   p->n = n; p->seq_ids = seq_ids; p->positions = positions;
   p->c_kv = c_kv_new; p->c_kv_stride = c_kv_stride; p->k_rope = k_rope_new; p->k_rope_stride = k_rope_stride;
   p->d_c = dims->d_c; p->d_rope = dims->d_rope; p->bf16 = cache->dtype == MLA_BF16;
+  p->fp8 = cache->dtype == MLA_FP8_E4M3;
   p->rope_base = base_of(dims);
   return MLA_OK;
 }
@@ -101,6 +112,11 @@ const char* mla_status_string(mla_status_t s) {
 }
 
 const char* mla_version(void) { return "mla-mi355x 0.1.0 (gfx950)"; }
+
+int64_t mla_cache_row_bytes(const mla_dims_t* dims, mla_dtype_t dtype) {
+  if (!dims_ok(dims) || !cache_dtype_ok(dtype)) return -1;
+  return row_bytes(dims, dtype);
+}
 
 int64_t mla_num_partials(int32_t B, int32_t num_splits) {
   if (B < 0 || num_splits < 1) return -1;
@@ -129,8 +145,9 @@ mla_status_t mla_decode(const mla_dims_t* dims, int32_t B, int32_t n_q, const vo
   p.q_lat = q_lat; p.q_pe = q_pe; p.cache = view_of(cache, dims); p.ctx_lens = cache->ctx_lens;
   p.positions = positions; p.u_part = u_part; p.lse_part = lse_part;
   p.B = B; p.n_q = n_q; p.n_h = dims->n_h; p.d_c = dims->d_c; p.d_rope = dims->d_rope;
-  p.num_splits = num_splits; p.bf16 = cache->dtype == MLA_BF16; p.sm_scale = scale_of(dims);
-  const bool fast = p.bf16 && p.d_c == 512 && p.d_rope == 64 && p.n_h % 32 == 0;
+  p.num_splits = num_splits; p.bf16 = cache->dtype == MLA_BF16; p.fp8 = cache->dtype == MLA_FP8_E4M3;
+  p.sm_scale = scale_of(dims);
+  const bool fast = (p.bf16 || p.fp8) && p.d_c == 512 && p.d_rope == 64 && p.n_h % 32 == 0;
   if (fast) return from_hip(mla::launch_decode_mfma(p, (hipStream_t)stream));
   if (p.d_c + p.d_rope > 2048 || p.d_c > 1024) return MLA_ERR_UNSUPPORTED;
   return from_hip(mla::launch_decode_generic(p, (hipStream_t)stream));

@@ -106,14 +106,20 @@ __global__ __launch_bounds__(256) void rope_q_rows_kernel(AbsorbParams p) {
 // mt): lane l holds latents 16t + 4(l/16) + 0..3 of row 16mt + l%16, stored as
 // 8 bytes (a wave writes 128 contiguous bytes of each row).
 // Requires d_nope == 128, d_c % 256 == 0, bf16.
-// Workgroups n_absorb and up take the append role instead: they write the
-// element pairs of the new bf16 cache rows of `ap` (as the append kernel does),
+// Workgroups n_absorb and up take the append role instead: they write the new
+// bf16 or fp8 cache rows of `ap` (as the append kernel does),
 // on CUs beside the absorption workgroups, so that a step's append costs no
 // launch of its own.
 constexpr int AR_LAT = 256;           // latents per workgroup
 constexpr int AR_ROPE = 8;            // RoPE items per thread whose loads go first
 __global__ __launch_bounds__(256) void absorb_rope_kernel(AbsorbParams p, AppendParams ap, int n_absorb) {
   if ((int)blockIdx.x >= n_absorb) {
+    if (ap.fp8) {   // one wave per new row
+      const int stride = (gridDim.x - n_absorb) * 4;
+      for (int k = (blockIdx.x - n_absorb) * 4 + (threadIdx.x >> 6); k < ap.n; k += stride)
+        append_row_fp8(ap, k, threadIdx.x & 63);
+      return;
+    }
     const int pairs = (ap.d_c + ap.d_rope) / 2;
     const int64_t items = (int64_t)ap.n * pairs;
     const int64_t stride = (int64_t)(gridDim.x - n_absorb) * 256;
@@ -351,7 +357,8 @@ hipError_t launch_append_absorb_mfma(const AbsorbParams& p, const AppendParams* 
   const int M = p.B * p.n_q;
   const bool append = ap != nullptr && ap->n > 0;
   const bool one_pass = p.d_nope == 128 && p.d_c % AR_LAT == 0;
-  if (append && !(one_pass && ap->bf16)) {   // the append gets a launch of its own
+  const bool fused = one_pass && (ap != nullptr) && (ap->bf16 || ap->fp8);
+  if (append && !fused) {   // the append gets a launch of its own
     const hipError_t e = launch_cache_append(*ap, stream);
     if (e != hipSuccess) return e;
   }
@@ -359,8 +366,9 @@ hipError_t launch_append_absorb_mfma(const AbsorbParams& p, const AppendParams* 
     const int n_absorb = p.n_h * (p.d_c / AR_LAT);
     AppendParams none{};
     int n_append = 0;
-    if (append && ap->bf16) {
-      const int64_t blocks = ((int64_t)ap->n * ((ap->d_c + ap->d_rope) / 2) + 255) / 256;
+    if (append && fused) {
+      const int64_t blocks = ap->fp8 ? ((int64_t)ap->n + 3) / 4
+                                     : ((int64_t)ap->n * ((ap->d_c + ap->d_rope) / 2) + 255) / 256;
       n_append = (int)(blocks < 256 ? blocks : 256);
     }
     hipLaunchKernelGGL(absorb_rope_kernel, dim3(n_absorb + n_append), dim3(256), 0, stream, p,

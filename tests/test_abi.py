@@ -151,3 +151,31 @@ def test_binding_refuses_host_tensors(lib):
     x = torch.zeros(1, 1, 4, 64)
     with pytest.raises(ValueError):
         mla.mla_out_proj(dims, x, torch.zeros(4, 64, 32), torch.zeros(1, 1, 4, 32))
+
+
+def test_cache_row_bytes(lib):
+    small = bd._Dims(4, 64, 16, 32, 32, 0.0, 0.0)
+    assert lib.mla_cache_row_bytes(ctypes.byref(V3), bd.FP8_E4M3) == 512 + 128 + 16
+    assert lib.mla_cache_row_bytes(ctypes.byref(V3), bd.BF16) == 1152
+    assert lib.mla_cache_row_bytes(ctypes.byref(V3), bd.F32) == 2304
+    assert lib.mla_cache_row_bytes(ctypes.byref(small), bd.FP8_E4M3) == -1   # d_c not a multiple of 128
+    assert lib.mla_cache_row_bytes(ctypes.byref(V3), 7) == -1
+    assert lib.mla_cache_row_bytes(None, bd.BF16) == -1
+
+
+def test_fp8_cache_argument_checks(lib):
+    """fp8 is a cache dtype only, and needs d_c % 128 == 0."""
+    small = bd._Dims(4, 64, 16, 32, 32, 0.0, 0.0)
+    c = _cache(dtype=bd.FP8_E4M3, seq_stride=656 * 16)
+    st = lib.mla_decode(ctypes.byref(small), 2, 1, FAKE, FAKE, ctypes.byref(c), FAKE, 4, FAKE, FAKE, None)
+    assert st == bd.MLA_ERR_INVALID_ARG
+    st = lib.mla_cache_append(ctypes.byref(small), ctypes.byref(c), 1, FAKE, FAKE, FAKE, 64, FAKE, 16, None)
+    assert st == bd.MLA_ERR_INVALID_ARG
+    # queries and weights are never fp8
+    st = lib.mla_absorb_q(ctypes.byref(V3), 1, 1, bd.FP8_E4M3, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == bd.MLA_ERR_INVALID_ARG
+    st = lib.mla_out_proj(ctypes.byref(V3), 1, 1, FAKE, bd.FP8_E4M3, FAKE, FAKE, None)
+    assert st == bd.MLA_ERR_INVALID_ARG
+    # a valid fp8 cache with a bad split count is still rejected on the host
+    st = lib.mla_decode(ctypes.byref(V3), 2, 1, FAKE, FAKE, ctypes.byref(c), FAKE, 0, FAKE, FAKE, None)
+    assert st == bd.MLA_ERR_INVALID_ARG

@@ -53,9 +53,12 @@ def _run(st, num_splits):
 
 def _oracle(w, st, b, heads=None):
     rows = W.cache_rows(w, b, 0, int(st["ctx_host"][b]))
+    c_kv = rows["c_kv"]
+    if w.cache_dtype == "fp8":   # the latents as an fp8 cache holds them
+        c_kv = oracle.fp8_dequantize_latent(*oracle.fp8_quantize_latent(c_kv))
     wt = W.weights(w)
     q = W.queries(w)
-    return oracle.decode_sequence(q["q_nope"][b], q["q_rope"][b], st["positions_host"][b], rows["c_kv"],
+    return oracle.decode_sequence(q["q_nope"][b], q["q_rope"][b], st["positions_host"][b], c_kv,
                                   rows["k_rope_raw"], wt["w_uk"], wt["w_uv"], w.sm_scale, w.rope_base,
                                   heads=heads)
 

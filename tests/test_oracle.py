@@ -492,6 +492,9 @@ def test_fp8_tile_scale_is_the_smallest_sufficient_power_of_two():
     amax = np.array([448.0, 448.0001, 224.0, 224.0001, 1.0, 3.9, 1e-30, 0.0, 7e5], dtype=np.float32)
     sc = oracle.fp8_tile_scale(amax)
     np.testing.assert_array_equal(sc, [1.0, 2.0, 0.5, 1.0, 2.0 ** -8, 2.0 ** -6, 2.0 ** -108, 1.0, 2.0 ** 11])
+    # the lower bound 2^-126 (a normal fp32 scale) for tiles below 448 * 2^-126
+    tiny = np.array([448 * 2.0 ** -126, 447 * 2.0 ** -126, 1e-40], dtype=np.float32)
+    np.testing.assert_array_equal(oracle.fp8_tile_scale(tiny), [2.0 ** -126] * 3)
     k = np.log2(sc[amax > 0].astype(np.float64))
     assert (k == np.round(k)).all()
     a = amax[amax > 0].astype(np.float64)

@@ -164,10 +164,22 @@ class Workload:
     d_q: Optional[int] = None  # hidden size when queries come from h @ W_UQ
     rope_base: float = 10000.0
     description: str = ""
+    cache: str = ""       # cache storage: "" = dtype; "fp8" = e4m3 codes with per-tile scales (bf16 inputs)
 
     @property
     def row(self) -> int:
         return self.d_c + self.d_rope
+
+    @property
+    def cache_dtype(self) -> str:
+        return self.cache or self.dtype
+
+    @property
+    def cache_row_bytes(self) -> int:
+        """Bytes of one cache row: fp8 rows are [d_c codes | d_rope bf16 | d_c/128 fp32 scales]."""
+        if self.cache_dtype == "fp8":
+            return self.d_c + 2 * self.d_rope + 4 * (self.d_c // 128)
+        return self.row * (2 if self.dtype == "bf16" else 4)
 
     @property
     def sm_scale(self) -> float:
@@ -200,6 +212,14 @@ WORKLOADS = {
 
 def get(name: str) -> Workload:
     return WORKLOADS[name]
+
+
+def with_fp8_cache(w: Workload) -> Workload:
+    """The same workload over an fp8 e4m3 latent cache (bf16 queries and weights)."""
+    if w.dtype != "bf16":
+        raise ValueError("fp8 caches go with bf16 queries and weights")
+    return dataclasses.replace(w, name=w.name + "_fp8", cache="fp8",
+                               description=w.description + ", fp8 e4m3 cache with per-128-channel scales")
 
 
 def custom(**kw) -> Workload:

@@ -53,15 +53,24 @@ def stage(w: Workload, device="cuda", chunk_tokens: int = 1 << 20, ctx: Optional
         "positions": torch.from_numpy(pos).to(dev), "ctx_lens": torch.from_numpy(ctx).to(dev),
     }
     B, row = w.batch, w.row
+    fp8 = w.cache_dtype == "fp8"
+
+    def poisoned(shape):
+        # unused slots hold NaN: bf16 / fp32 NaN, or 0xFF bytes for fp8 rows
+        # (NaN codes, NaN bf16 key, NaN fp32 scales)
+        if fp8:
+            return torch.full(shape[:-1] + (w.cache_row_bytes,), 0xFF, dtype=torch.uint8, device=dev)
+        return torch.full(shape, float("nan"), dtype=tdt, device=dev)
+
     if w.block_size:
         table, n_blocks = block_table(w, ctx)
-        data = torch.full((n_blocks, w.block_size, row), float("nan"), dtype=tdt, device=dev)
+        data = poisoned((n_blocks, w.block_size, row))
         tbl = torch.from_numpy(table).to(dev)
         cache = mla.LatentCache(data=data, ctx_lens=out["ctx_lens"], block_table=tbl, block_size=w.block_size)
         out["block_table_host"] = table
     else:
         s_max = int(ctx.max()) if len(ctx) else 1
-        data = torch.full((B, max(s_max, 1), row), float("nan"), dtype=tdt, device=dev)
+        data = poisoned((B, max(s_max, 1), row))
         cache = mla.LatentCache(data=data, ctx_lens=out["ctx_lens"])
     out["cache"] = cache
 
