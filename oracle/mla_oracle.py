@@ -243,8 +243,8 @@ def merge_partials(u_parts: np.ndarray, lse_parts: np.ndarray):
 # scales instead [Huny, serving checklist, fp8 KV-cache item; Paldyn, KV-cache
 # quantisation].  The reading taken here: each cached token's latent is cut
 # into tiles of 128 channels, and each tile gets its own scale, the smallest
-# power of two 2^k with the tile's largest magnitude <= 448 * 2^k (448 is the
-# largest e4m3 value).  A power of two costs a floating-point format no
+# power of two 2^k (k >= -126) with the tile's largest magnitude <= 448 * 2^k
+# (448 is the largest e4m3 value).  A power of two costs a floating-point format no
 # relative precision (every value keeps its 3 mantissa bits) and makes both
 # directions exact: x / 2^k before rounding, code value * 2^k after.  The
 # element format is
@@ -280,7 +280,9 @@ def e4m3_encode(x) -> np.ndarray:
 
 
 def fp8_tile_scale(amax) -> np.ndarray:
-    """2^k for the smallest integer k with amax <= 448 * 2^k (1 for amax = 0)."""
+    """2^k for the smallest integer k >= -126 with amax <= 448 * 2^k (1 for
+    amax = 0).  The bound keeps the scale a normal fp32 number; it binds only
+    for tiles whose largest magnitude is below 448 * 2^-126 (about 5e-36)."""
     amax = np.asarray(amax, dtype=np.float64)
     k = np.zeros(amax.shape, dtype=np.int64)
     pos = amax > 0
@@ -289,6 +291,7 @@ def fp8_tile_scale(amax) -> np.ndarray:
     for _ in range(2):
         k = np.where(pos & (amax > FP8_MAX * 2.0 ** k), k + 1, k)
         k = np.where(pos & (amax <= FP8_MAX * 2.0 ** (k - 1)), k - 1, k)
+    k = np.maximum(k, -126)
     return (2.0 ** k).astype(np.float32)
 
 
