@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40,
                     help="untimed steps first; the clock settles within ~10 ms of load")
     ap.add_argument("--workload", default="v3_b64")
+    ap.add_argument("--cache", choices=("native", "fp8"), default="native",
+                    help="cache storage: the workload's own dtype, or fp8 e4m3 with per-128-channel scales")
     ap.add_argument("--num-splits", type=int, default=0, help="0 = library default for the batch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
@@ -66,12 +68,12 @@ def algorithmic_bytes(w, ctx):
     """Bytes the method itself must move (no partials, padding or re-reads)."""
     eb = 2 if w.dtype == "bf16" else 4
     B, nq = w.batch, w.n_q
-    cache = int(ctx.sum()) * w.row * eb
+    cache = int(ctx.sum()) * w.cache_row_bytes
     q_in = B * nq * w.n_h * (w.d_nope + w.d_rope) * eb
     q_abs = B * nq * w.n_h * (w.d_c + w.d_rope) * eb
     wts = w.n_h * w.d_c * (w.d_nope + w.d_v) * eb
     out = B * nq * w.n_h * w.d_v * 4
-    append = B * nq * w.row * eb * 2
+    append = B * nq * (w.row * eb + w.cache_row_bytes)   # new raw rows in, cache rows out
     u_lse = B * nq * w.n_h * (w.d_c + 1) * 4
     return {"step": cache + q_in + wts + out + append, "decode": cache + q_abs + u_lse, "cache": cache}
 
@@ -106,28 +108,34 @@ def cpu_baseline(w, min_seconds=10.0, head_group=16):
     order = list(dict.fromkeys(order))
     wt, q = W.weights(w), W.queries(w)
     pos = W.positions(w, ctx)
-    eb = 2 if w.dtype == "bf16" else 4
+    fp8 = w.cache_dtype == "fp8"
     spent, sample_bytes, head_rows, done = 0.0, 0.0, 0, []
     for b in order:
         rows = W.cache_rows(w, b, 0, int(ctx[b]))
+        c_kv = rows["c_kv"]
+        if fp8:   # the oracle's quantisation of the sequence, timed with its decode
+            t0 = time.perf_counter()
+            c_kv = oracle.fp8_dequantize_latent(*oracle.fp8_quantize_latent(c_kv))
+            spent += time.perf_counter() - t0
         heads_done = 0
         for h0 in range(0, w.n_h, head_group):
             heads = list(range(h0, min(h0 + head_group, w.n_h)))
             t0 = time.perf_counter()
-            oracle.decode_sequence(q["q_nope"][b], q["q_rope"][b], pos[b], rows["c_kv"], rows["k_rope_raw"],
+            oracle.decode_sequence(q["q_nope"][b], q["q_rope"][b], pos[b], c_kv, rows["k_rope_raw"],
                                    wt["w_uk"], wt["w_uv"], w.sm_scale, w.rope_base, heads=heads)
             spent += time.perf_counter() - t0
             heads_done += len(heads)
             if spent >= min_seconds:
                 break
-        sample_bytes += int(ctx[b]) * w.row * eb * heads_done / w.n_h
+        sample_bytes += int(ctx[b]) * w.cache_row_bytes * heads_done / w.n_h
         head_rows += heads_done * w.n_q
         done.append(f"{b}(ctx {int(ctx[b])}, {heads_done} heads)")
         if spent >= min_seconds:
             break
     return {"value": round(sample_bytes / spent / 1e9, 6), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
             "sample": f"sequences {', '.join(done)} of {w.name}, all {w.n_q} query token(s), heads in groups of "
-                      f"{head_group}; fp64 reconstruct-then-attend; GB/s = attended cache bytes x heads done/"
+                      f"{head_group}; {'fp8 quantise + dequantise, ' if fp8 else ''}fp64 reconstruct-then-attend; "
+                      f"GB/s = attended cache bytes x heads done/"
                       f"{w.n_h} / oracle time",
             "seconds": round(spent, 3),
             "head_rows_per_s": round(head_rows / spent, 3)}
@@ -347,6 +355,8 @@ def main():
     from workloads.device import stage
 
     w = W.get(args.workload)
+    if args.cache == "fp8":
+        w = W.with_fp8_cache(w)
     log(f"staging {w.name}: {w.description}")
     t0 = time.perf_counter()
     st = stage(w)
@@ -451,6 +461,17 @@ def main():
     flops = decode_flops(w, ctx, pos)
     value = nbytes["step"] / (ms_step * 1e-3) / 1e9
     achieved = nbytes["decode"] / (dec_avg * 1e-3) / 1e9
+    tflops = flops / (dec_avg * 1e-3) / 1e12
+    # the bound is whichever roofline takes longer at peak rates
+    mfma_bound = flops / (MFMA_BF16_PEAK_TFS * 1e12) > nbytes["decode"] / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": round(tflops / MFMA_BF16_PEAK_TFS, 4), "hbm_gbs": round(achieved, 2),
+                "hbm_frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "mfma_tflops": round(tflops, 2),
+                "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFS, 4)}
     result = {
         "metric": "MLA decode latent-cache GB/s + tokens/s (DeepSeek-V3 shapes), % of roofline",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -461,16 +482,15 @@ def main():
                    "fused_append": not args.separate_append,
                    "step_launch": "graph" if graph is not None else "eager", "batch": w.batch, "n_q": w.n_q,
                    "n_h": w.n_h, "d_c": w.d_c, "d_rope": w.d_rope, "d_nope": w.d_nope, "d_v": w.d_v,
-                   "context_tokens": int(ctx.sum()), "block_size": w.block_size, "num_splits": num_splits},
+                   "context_tokens": int(ctx.sum()), "block_size": w.block_size, "num_splits": num_splits,
+                   "cache": w.cache_dtype, "cache_row_bytes": w.cache_row_bytes},
         "tokens_per_s": round(w.batch * w.n_q / (ms_step * 1e-3), 1),
         "kv_tokens_per_s": round(float(ctx.sum()) / (ms_step * 1e-3), 1),
         "step_bytes": nbytes["step"],
-        "roofline": {"kernel": "mla_decode (decode_mfma_kernel)", "bound": "hbm", "achieved": round(achieved, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(w.name), "bytes_per_launch": nbytes["decode"], "avg_launch_us": round(dec_avg * 1e3, 3),
-                     "launches_timed": len(dec_ms),
-                     "mfma_tflops": round(flops / (dec_avg * 1e-3) / 1e12, 2),
-                     "mfma_frac": round(flops / (dec_avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4)},
+        "roofline": {"kernel": "mla_decode (decode_mfma_kernel)", **roof,
+                     "traffic": measured_traffic(w.name), "bytes_per_launch": nbytes["decode"],
+                     "flops_per_launch": flops, "avg_launch_us": round(dec_avg * 1e3, 3),
+                     "launches_timed": len(dec_ms)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -378,24 +378,32 @@ __device__ __forceinline__ void convert_fp8_stage(const unsigned char* rw, unsig
   unsigned char* wbase = bf + (2 * wave + (p8 >> 2)) * CG_BYTES + tq * 128;
   const unsigned char* rbase = rw + RAW_CODES + 16 * ln;
   const unsigned char* sbase = rw + RAW_SCALE + 4 * tq;
+  // every read first (the raw and bf16 stages could alias as far as the
+  // compiler knows, so it would not move a read above an earlier write)
+  float sc[4];
+  u32x4 w[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float sc = *(lds_cf32*)L(sbase + 32 * i);
-    const u32x4 w = *(lds_cu32x4*)L(rbase + 1024 * i);
+    sc[i] = *(lds_cf32*)L(sbase + 32 * i);
+    w[i] = *(lds_cu32x4*)L(rbase + 1024 * i);
+  }
+  const u32x4 key = *(lds_cu32x4*)L(rw + RAW_ROPE + 16 * ln);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
     bf16x8 o[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const auto a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h], sc, false);
-      const auto a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h], sc, true);
-      const auto a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h + 1], sc, false);
-      const auto a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h + 1], sc, true);
+      const auto a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i][2 * h], sc[i], false);
+      const auto a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i][2 * h], sc[i], true);
+      const auto a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i][2 * h + 1], sc[i], false);
+      const auto a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i][2 * h + 1], sc[i], true);
       o[h] = bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
     }
     const int xi = x ^ (i & 1 ? 2 : 0);
     *(lds_bf16x8*)L(wbase + 1024 * i + (xi << 4)) = o[0];
     *(lds_bf16x8*)L(wbase + 1024 * i + ((xi ^ 1) << 4)) = o[1];
   }
-  *(lds_u32x4*)L(bf + 8 * CG_BYTES + 1024 * wave + 16 * ln) = *(lds_cu32x4*)L(rw + RAW_ROPE + 16 * ln);
+  *(lds_u32x4*)L(bf + 8 * CG_BYTES + 1024 * wave + 16 * ln) = key;
 }
 
 // Paged cache, tokens t0..t1-1 of sequence b: the lowest block id among their
