@@ -367,6 +367,29 @@ def test_causal_mask_pair():
         np.testing.assert_allclose(got[key][0], ref[key][0], rtol=1e-13)
 
 
+def test_prefill_chunk_brute_force():
+    """A prefill chunk: the last 6 of 8 cached tokens are queries, each attending
+    causally to every cached token up to its own position."""
+    prob = _problem(30, n_q=6, n_h=2, d_c=4, d_nope=2, d_rope=4, d_v=3, S=8)
+    ok, key, err = _compare_to_brute(oracle.decode_sequence, prob, tol=1e-13)
+    assert ok, (key, err)
+
+
+def test_prefill_rows_are_single_query_decodes():
+    """Row j of a chunk of 8 equals one decode query at position pos_j over the
+    cache cut after pos_j (queries are independent; the causal mask is the cut)."""
+    prob = _problem(31, n_q=8, n_h=3, d_c=8, d_nope=4, d_rope=4, d_v=5, S=20)
+    ref = oracle.decode_sequence(**prob)
+    for j in range(8):
+        pos = int(prob["q_positions"][j])
+        one = dict(prob, q_nope=prob["q_nope"][j:j + 1], q_rope=prob["q_rope"][j:j + 1],
+                   q_positions=prob["q_positions"][j:j + 1], c_kv=prob["c_kv"][:pos + 1],
+                   k_rope_raw=prob["k_rope_raw"][:pos + 1])
+        got = oracle.decode_sequence(**one)
+        for key in ("o", "u", "lse"):
+            np.testing.assert_allclose(got[key][0], ref[key][j], rtol=1e-13, atol=1e-15)
+
+
 def test_low_rank_bound():
     """Keys rebuilt from d_c-wide latents span at most d_c dimensions (case 2)."""
     r = _rng(15)
