@@ -209,6 +209,49 @@ mla_status_t mla_append_absorb_q(const mla_dims_t *dims, const mla_cache_t *cach
                                  const void *q_nope, const void *q_rope, const int32_t *positions,
                                  const void *w_uk, void *q_lat, void *q_pe, void *stream);
 
+/* ---- Prefill and chunked prefill ([Huny] §1 and §2.2: k^C_i = c W_i^UK,
+ * v_i = c W_i^UV, key [k^C_i | k^R]; [Tbr8] §5.2: prefill is compute-bound, so
+ * the per-head keys and values are rebuilt once per call instead of absorbing
+ * W^UK into every query).  The last n_q cached tokens of each sequence are
+ * queries; each attends causally to the cached tokens t <= its position:
+ *   kv[b][t][i][0:d_nope]   = c_t W_i^UK       (bf16 into `workspace`)
+ *   kv[b][t][i][d_nope:]    = c_t W_i^UV
+ *   s_t = scale * ([q^C_i | RoPE(q^R_i, pos)] . [kv[b][t][i][0:d_nope] | k^R_t])
+ *   out[b][j][i][:] = sum_t softmax(s)_t kv[b][t][i][d_nope:],   lse = log sum_t exp(s_t)
+ * i.e. o = a (C W_i^UV), the same output as mla_decode + mla_combine +
+ * mla_out_proj for the same queries.  Compiled for bf16, d_nope = d_v = 128,
+ * d_rope = 64, d_c a multiple of 64, a contiguous cache; other shapes return
+ * MLA_ERR_UNSUPPORTED. */
+
+/* w_kv [n_h][d_nope + d_v][d_c] bf16, out: w_kv[i][d][c] = W_i^UK[c][d] for
+ * d < d_nope, W_i^UV[c][d - d_nope] otherwise (the latent index innermost, the
+ * layout the reconstruction reads).  w_uk [n_h][d_c][d_nope], w_uv [n_h][d_c][d_v]. */
+mla_status_t mla_prefill_weights(const mla_dims_t *dims, const void *w_uk, const void *w_uv, void *w_kv,
+                                 void *stream);
+
+/* Bytes of the workspace of mla_prefill: B * max_ctx * n_h * (d_nope + d_v) * 2
+ * (kv [B][max_ctx][n_h][d_nope + d_v] bf16); -1 for invalid arguments. */
+int64_t mla_prefill_workspace_bytes(const mla_dims_t *dims, int32_t B, int32_t max_ctx);
+
+/*   q_nope    [B][n_q][n_h][d_nope]   bf16
+ *   q_rope    [B][n_q][n_h][d_rope]   bf16, before rotation
+ *   positions [B][n_q]                query j of sequence b sits at positions[b][j]
+ *                                     (normally ctx_lens[b] - n_q + j)
+ *   cache                             bf16, contiguous; ctx_lens[b] <= max_ctx and
+ *                                     max_ctx rows per sequence fit in seq_stride
+ *   w_kv      from mla_prefill_weights
+ *   workspace >= mla_prefill_workspace_bytes(dims, B, max_ctx) bytes, 16-byte
+ *             aligned; holds kv [B][max_ctx][n_h][d_nope + d_v] on return
+ *             (rows t >= ctx_lens[b] hold whatever the cache rows there give)
+ *   q_pe      [B][n_q][n_h][d_rope]   bf16, out: RoPE(q_rope, positions)
+ *   out       [B][n_q][n_h][d_v]      fp32, out
+ *   lse       [B][n_q][n_h]           fp32, out (may be NULL)
+ * Requires 1 <= n_q <= max_ctx and (max_ctx + 32) * n_h * (d_nope + d_v) * 2 < 2^32. */
+mla_status_t mla_prefill(const mla_dims_t *dims, int32_t B, int32_t n_q, int32_t max_ctx, const void *q_nope,
+                         const void *q_rope, const int32_t *positions, const mla_cache_t *cache,
+                         const void *w_kv, void *workspace, int64_t workspace_bytes, void *q_pe, float *out,
+                         float *lse, void *stream);
+
 /* ---- Weight folds ([Huny] §3.2, "Value 투영과 Output 투영의 결합 행렬 흡수":
  * W_i,comb = W_i^UV W_i^O is formed offline and the layer output is one
  * product with it; [Paldyn], section "MLA": the matrix that expands the keys

@@ -29,6 +29,9 @@ from ._binding import (  # noqa: F401
     mla_fold_q,
     mla_absorb_q_folded,
     mla_cache_row_bytes,
+    mla_prefill_weights,
+    mla_prefill_workspace_bytes,
+    mla_prefill,
 )
 
 __version__ = "0.1.0"

@@ -22,7 +22,7 @@ EXPORTED = ("mla_absorb_q", "mla_decode", "mla_combine", "mla_out_proj", "mla_co
             "mla_status_string", "mla_version",
             "mla_block_pool_bytes", "mla_block_pool_init", "mla_block_pool_reserve", "mla_block_pool_reserve_all",
             "mla_block_pool_release", "mla_fold_out", "mla_out_proj_folded", "mla_o_proj", "mla_fold_q",
-            "mla_absorb_q_folded",
+            "mla_absorb_q_folded", "mla_prefill_weights", "mla_prefill_workspace_bytes", "mla_prefill",
             "mla_block_pool_table", "mla_block_pool_free_count")
 
 
@@ -71,6 +71,8 @@ def load_library(path: str = LIB_PATH):
         "mla_o_proj": [DP, I32, I32, I32, P, P, P, V],
         "mla_fold_q": [DP, I32, P, P, P, V],
         "mla_absorb_q_folded": [DP, I32, I32, I32, P, P, P, P, P, P, V],
+        "mla_prefill_weights": [DP, P, P, P, V],
+        "mla_prefill": [DP, I32, I32, I32, P, P, P, CP, P, P, I64, P, P, P, V],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -90,6 +92,8 @@ def load_library(path: str = LIB_PATH):
     lib.mla_block_pool_free_count.restype = ctypes.c_int32
     lib.mla_num_partials.argtypes = [I32, I32]
     lib.mla_num_partials.restype = ctypes.c_int64
+    lib.mla_prefill_workspace_bytes.argtypes = [DP, I32, I32]
+    lib.mla_prefill_workspace_bytes.restype = ctypes.c_int64
     lib.mla_cache_row_bytes.argtypes = [DP, ctypes.c_int]
     lib.mla_cache_row_bytes.restype = ctypes.c_int64
     lib.mla_status_string.argtypes = [ctypes.c_int]
@@ -474,3 +478,55 @@ def mla_absorb_q_folded(dims: Dims, c_q, q_rope, positions, w_kq, q_lat, q_pe, s
     _check("mla_absorb_q_folded", load_library().mla_absorb_q_folded(
         ctypes.byref(d), d_q, B, n_q, c_q.data_ptr(), q_rope.data_ptr(), positions.data_ptr(), w_kq.data_ptr(),
         q_lat.data_ptr(), q_pe.data_ptr(), _stream(stream)))
+
+
+def mla_prefill_weights(dims: Dims, w_uk, w_uv, w_kv, stream=None) -> None:
+    """w_kv [n_h][d_nope + d_v][d_c] bf16 from W_UK [n_h][d_c][d_nope] and W_UV [n_h][d_c][d_v]."""
+    torch = _torch()
+    for t, n in ((w_uk, "w_uk"), (w_uv, "w_uv"), (w_kv, "w_kv")):
+        _dev(t, n, torch.bfloat16)
+    _shape(w_uk, "w_uk", (dims.n_h, dims.d_c, dims.d_nope))
+    _shape(w_uv, "w_uv", (dims.n_h, dims.d_c, dims.d_v))
+    _shape(w_kv, "w_kv", (dims.n_h, dims.d_nope + dims.d_v, dims.d_c))
+    d = dims._c()
+    _check("mla_prefill_weights", load_library().mla_prefill_weights(
+        ctypes.byref(d), w_uk.data_ptr(), w_uv.data_ptr(), w_kv.data_ptr(), _stream(stream)))
+
+
+def mla_prefill_workspace_bytes(dims: Dims, B: int, max_ctx: int) -> int:
+    d = dims._c()
+    return int(load_library().mla_prefill_workspace_bytes(ctypes.byref(d), B, max_ctx))
+
+
+def mla_prefill(dims: Dims, max_ctx: int, q_nope, q_rope, positions, cache: LatentCache, w_kv, workspace,
+                q_pe, out, lse=None, stream=None) -> None:
+    """Prefill of the last n_q cached tokens of each sequence (see mla.h).
+    ``workspace`` is a device tensor of at least mla_prefill_workspace_bytes
+    bytes; on return it holds kv [B][max_ctx][n_h][d_nope + d_v] bf16."""
+    torch = _torch()
+    B, n_q = q_nope.shape[0], q_nope.shape[1]
+    for t, n in ((q_nope, "q_nope"), (q_rope, "q_rope"), (q_pe, "q_pe"), (w_kv, "w_kv")):
+        _dev(t, n, torch.bfloat16)
+    _dev(positions, "positions", torch.int32)
+    _dev(out, "out", torch.float32)
+    _dev(workspace, "workspace")
+    _shape(q_nope, "q_nope", (B, n_q, dims.n_h, dims.d_nope))
+    _shape(q_rope, "q_rope", (B, n_q, dims.n_h, dims.d_rope))
+    _shape(q_pe, "q_pe", (B, n_q, dims.n_h, dims.d_rope))
+    _shape(positions, "positions", (B, n_q))
+    _shape(w_kv, "w_kv", (dims.n_h, dims.d_nope + dims.d_v, dims.d_c))
+    _shape(out, "out", (B, n_q, dims.n_h, dims.d_v))
+    _shape(cache.ctx_lens, "cache.ctx_lens", (B,))
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+        _shape(lse, "lse", (B, n_q, dims.n_h))
+    if cache.data.shape[-1] != cache.row_width(dims):
+        raise ValueError(f"cache rows must be {cache.row_width(dims)} wide")
+    if cache.block_size == 0 and (cache.data.shape[0] < B or cache.data.shape[1] < max_ctx):
+        raise ValueError("the contiguous cache must hold B sequences of max_ctx rows")
+    d, c = dims._c(), cache._c()
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("mla_prefill", load_library().mla_prefill(
+        ctypes.byref(d), B, n_q, max_ctx, q_nope.data_ptr(), q_rope.data_ptr(), positions.data_ptr(),
+        ctypes.byref(c), w_kv.data_ptr(), workspace.data_ptr(), nbytes, q_pe.data_ptr(), out.data_ptr(),
+        None if lse is None else lse.data_ptr(), _stream(stream)))

@@ -31,11 +31,12 @@ DEVICE_FLAGS = [
 # Per-source extra flags: MFMA accumulators of built-in MFMAs in the VGPR form
 # (the decode kernel pins its large accumulator to AGPRs itself).
 EXTRA_FLAGS = {"proj_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-               "decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+               "decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+               "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 SOURCES = ["mla_api.cpp", "decode_mfma.hip", "decode_generic.hip", "combine.hip",
            "absorb.hip", "out_proj.hip", "cache_append.hip", "proj_mfma.hip", "tail_mfma.hip",
-           "block_pool.cpp", "gemm_nt.hip"]
+           "block_pool.cpp", "gemm_nt.hip", "prefill.hip"]
 
 
 def _hipcc() -> str:

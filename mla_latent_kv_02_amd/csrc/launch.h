@@ -118,4 +118,24 @@ struct GemmNT {
 };
 hipError_t launch_gemm_nt(const GemmNT& g, hipStream_t stream);
 
+// Prefill: reconstruction of [c W_i^UK | c W_i^UV] for tokens 0 .. max_ctx-1
+// into kv [B][max_ctx][n_h][256], then causal attention of the n_q query rows
+// of every sequence (V3 head shapes, bf16, contiguous cache).
+struct PrefillParams {
+  const void* q_nope;       // [B][n_q][n_h][128]
+  const void* q_pe;         // [B][n_q][n_h][64], rotated
+  const int32_t* positions; // [B][n_q]
+  const int32_t* ctx_lens;  // [B]
+  CacheView cache;
+  const void* w_kv;         // [n_h][256][d_c]
+  void* kv;
+  float* out;
+  float* lse;
+  int B, n_q, n_h, d_c, max_ctx;
+  float sm_scale;
+};
+hipError_t launch_prefill_weights(const uint16_t* w_uk, const uint16_t* w_uv, uint16_t* w_kv, int n_h, int d_c,
+                                  hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+
 }  // namespace mla

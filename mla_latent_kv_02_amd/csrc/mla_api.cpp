@@ -54,6 +54,7 @@ mla::CacheView view_of(const mla_cache_t* c, const mla_dims_t* d) {
 }
 
 mla_status_t from_hip(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+bool al16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
 // Checks the arguments of mla_absorb_q and fills *p (p->B == 0: nothing to do).
 mla_status_t absorb_args(const mla_dims_t* dims, int32_t B, int32_t n_q, mla_dtype_t dt, const void* q_nope,
@@ -234,9 +235,59 @@ mla_status_t mla_append_absorb_q(const mla_dims_t* dims, const mla_cache_t* cach
   return p.B > 0 ? launch_absorb_any(p, s) : MLA_OK;
 }
 
+// ---- prefill
+namespace {
+bool prefill_dims_ok(const mla_dims_t* d) {
+  return d->d_nope == 128 && d->d_v == 128 && d->d_rope == 64 && d->d_c % 64 == 0;
+}
+}  // namespace
+
+mla_status_t mla_prefill_weights(const mla_dims_t* dims, const void* w_uk, const void* w_uv, void* w_kv,
+                                 void* stream) {
+  if (!dims_ok(dims) || !w_uk || !w_uv || !w_kv) return MLA_ERR_INVALID_ARG;
+  if (!prefill_dims_ok(dims) || dims->n_h > 65535) return MLA_ERR_UNSUPPORTED;
+  return from_hip(mla::launch_prefill_weights(static_cast<const uint16_t*>(w_uk), static_cast<const uint16_t*>(w_uv),
+                                              static_cast<uint16_t*>(w_kv), dims->n_h, dims->d_c, (hipStream_t)stream));
+}
+
+int64_t mla_prefill_workspace_bytes(const mla_dims_t* dims, int32_t B, int32_t max_ctx) {
+  if (!dims_ok(dims) || B < 0 || max_ctx < 0) return -1;
+  return (int64_t)B * max_ctx * dims->n_h * (dims->d_nope + dims->d_v) * 2;
+}
+
+mla_status_t mla_prefill(const mla_dims_t* dims, int32_t B, int32_t n_q, int32_t max_ctx, const void* q_nope,
+                         const void* q_rope, const int32_t* positions, const mla_cache_t* cache,
+                         const void* w_kv, void* workspace, int64_t workspace_bytes, void* q_pe, float* out,
+                         float* lse, void* stream) {
+  if (!dims_ok(dims) || B < 0 || n_q < 1 || max_ctx < n_q) return MLA_ERR_INVALID_ARG;
+  if (B == 0) return MLA_OK;
+  if (!q_nope || !q_rope || !positions || !w_kv || !workspace || !q_pe || !out || !cache_ok(cache, dims))
+    return MLA_ERR_INVALID_ARG;
+  if (workspace_bytes < mla_prefill_workspace_bytes(dims, B, max_ctx) || !al16(workspace))
+    return MLA_ERR_INVALID_ARG;
+  if (!prefill_dims_ok(dims) || cache->dtype != MLA_BF16 || cache->block_size != 0) return MLA_ERR_UNSUPPORTED;
+  if (cache->seq_stride < (int64_t)max_ctx * (dims->d_c + dims->d_rope)) return MLA_ERR_INVALID_ARG;
+  const int64_t kv_tok = (int64_t)dims->n_h * (dims->d_nope + dims->d_v) * 2;
+  if ((int64_t)(max_ctx + 32) * kv_tok >= (1LL << 32) || (int64_t)(max_ctx + 32) * (dims->d_c + dims->d_rope) * 2 >=
+      (1LL << 31) || B > 65535 || (int64_t)B * n_q > (1 << 24))
+    return MLA_ERR_UNSUPPORTED;
+  const hipStream_t s = (hipStream_t)stream;
+  mla::AbsorbParams ap;
+  ap.q_nope = nullptr; ap.q_rope = q_rope; ap.positions = positions; ap.w_uk = nullptr;
+  ap.q_lat = nullptr; ap.q_pe = q_pe;
+  ap.B = B; ap.n_q = n_q; ap.n_h = dims->n_h; ap.d_c = dims->d_c; ap.d_rope = dims->d_rope; ap.d_nope = dims->d_nope;
+  ap.bf16 = true; ap.rope_base = base_of(dims);
+  mla_status_t st = from_hip(mla::launch_rope_q(ap, s));
+  if (st != MLA_OK) return st;
+  mla::PrefillParams p;
+  p.q_nope = q_nope; p.q_pe = q_pe; p.positions = positions; p.ctx_lens = cache->ctx_lens;
+  p.cache = view_of(cache, dims); p.w_kv = w_kv; p.kv = workspace; p.out = out; p.lse = lse;
+  p.B = B; p.n_q = n_q; p.n_h = dims->n_h; p.d_c = dims->d_c; p.max_ctx = max_ctx; p.sm_scale = scale_of(dims);
+  return from_hip(mla::launch_prefill(p, s));
+}
+
 // ---- weight folds and the products that use them
 namespace {
-bool al16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 // the launch grid of a product: (N/32, M/64, batch) blocks
 mla_status_t run_gemm(const mla::GemmNT& g, void* stream) {
   if ((g.M + 63) / 64 > 65535 || g.batch > 65535) return MLA_ERR_UNSUPPORTED;

@@ -1,0 +1,448 @@
+// Prefill (and chunked prefill) of MLA attention: many query tokens per
+// sequence, keys and values rebuilt per head from the cached latents.
+//
+// Method ([Huny] = "Multi-Head Latent Attention(MLA) 아키텍처 해부", Huny's Dev
+// Blog, §1: k^C_i = c W_i^UK, v_i = c W_i^UV; §2.2: the key of head i is
+// [k^C_i | k^R] with the shared rotated positional key; [Tbr8] = "DeepSeek
+// MLA（多头潜在注意力）深度解析", tbr8.org, §5.2: prefill is compute-bound, so
+// the up-projections cost little there, while absorption pays at decode):
+//   kv[t][i] = [c_t W_i^UK | c_t W_i^UV]                 (reconstruct_gemm)
+//   o_j,i    = softmax_{t <= pos_j}(q_j,i . [kv[t][i][:128] | k^R_t] * scale) kv[t][i][128:]
+//                                                      (prefill_attn_kernel)
+// Absorbing W^UK into the query costs 2(d_c + d_rope) + 2 d_c = 2176 FLOPs per
+// (query, token, head) against 2(d_nope + d_rope) + 2 d_v = 640 here; the
+// reconstruction adds 2 d_c (d_nope + d_v) n_h FLOPs per cached token once per
+// call, which a chunk of many queries amortises.
+//
+// V3 head shapes only: d_nope = d_v = 128, d_rope = 64, bf16 operands, fp32
+// accumulation.
+
+#include <climits>
+
+#include "mla_device.h"
+#include "launch.h"
+
+namespace mla {
+namespace {
+
+constexpr int NT = 256;
+constexpr int DN = 128, DV = 128, DR = 64;
+constexpr int KVW = DN + DV;             // elements of one head's reconstructed row
+constexpr int kBufferWord3 = 0x00020000; // raw buffer resource, 32-bit data format, byte offsets
+
+// s(t) = P[(t / 2) % 8], P = (0, 4, 1, 5, 2, 6, 3, 7): 16-byte chunk c of LDS row t
+// sits at slot c ^ s(t), so that 16 consecutive rows read at one chunk hit
+// 16 distinct bank groups (two row parities x 8 slot values).
+__device__ __forceinline__ int swz(int t) { return (0x73625140 >> (4 * ((t >> 1) & 7))) & 7; }
+
+typedef __attribute__((address_space(3))) const bf16x8 lds_cbf16x8;
+__device__ __forceinline__ bf16x8 lds_read16(const unsigned char* p) {
+  return *(lds_cbf16x8*)((__attribute__((address_space(3))) const unsigned char*)p);
+}
+
+// ------------------------------------------------------------ weight layout
+// w_kv[i][d][c] = W_i^UK[c][d] (d < 128), W_i^UV[c][d - 128] (d >= 128): the
+// latent index innermost, the operand layout of the reconstruction product.
+__global__ __launch_bounds__(NT) void prefill_weights_kernel(const uint16_t* __restrict__ w_uk,
+                                                             const uint16_t* __restrict__ w_uv,
+                                                             uint16_t* __restrict__ w_kv, int d_c) {
+  __shared__ uint16_t tile[32][33];
+  const int i = blockIdx.z;
+  const int c0 = blockIdx.x * 32, d0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8
+  const uint16_t* src = d0 < DN ? w_uk + (int64_t)i * d_c * DN : w_uv + (int64_t)i * d_c * DV;
+  const int dd = d0 < DN ? d0 : d0 - DN;
+  for (int r = ty; r < 32; r += 8) tile[r][tx] = src[(int64_t)(c0 + r) * DN + dd + tx];   // [c][d]
+  lds_sync();
+  for (int r = ty; r < 32; r += 8) w_kv[((int64_t)i * KVW + d0 + r) * d_c + c0 + tx] = tile[tx][r];
+}
+
+// ------------------------------------------------------- reconstruction
+// kv[z][m][n] = sum_c A[z][m][c] w_kv[n][c] with A the cached latents of
+// sequence z (rows m < M of the cache, the first d_c elements of each row) and
+// n = i * 256 + d over all heads.  Workgroup tile 128 (m) x 256 (n); wave w
+// takes m rows 64(w%2) .. +64 and n rows 128(w/2) .. +128 (2 x 4 blocks of
+// 32 x 32).  The weight rows are the MFMA's first operand, so a lane's
+// results are 4 consecutive n of one m (one 8-byte store each).  The k range
+// is streamed in chunks of 64 through a 3-stage LDS ring: row r of a stage
+// holds 8 chunks of 16 bytes, chunk c at slot c ^ s(r); a wave's 16-byte
+// global->LDS load writes 8 rows x 128 bytes.
+constexpr int GM = 128, GN = 256, GK = 64, GSTAGES = 3;
+constexpr int GA_BYTES = GM * GK * 2, GB_BYTES = GN * GK * 2;   // 16 KiB, 32 KiB
+constexpr int G_LOADS = (GM + GN) / 8 / 4;                      // 1 KiB loads per wave per stage: 12
+
+struct GemmArgs {
+  const unsigned char* a;   // cache data (bf16 rows)
+  int64_t a_seq_bytes;      // bytes between sequences
+  int a_row_bytes;          // bytes between rows
+  const uint16_t* w;        // w_kv [N][K]
+  uint16_t* c;              // kv [Z][M][N]
+  int M, N, K;
+};
+
+struct __attribute__((aligned(16))) GemmSmem {
+  unsigned char a[GSTAGES][GA_BYTES];
+  unsigned char b[GSTAGES][GB_BYTES];
+};
+
+__global__ __launch_bounds__(NT, 1) void reconstruct_gemm_kernel(GemmArgs g) {
+  __shared__ GemmSmem sm;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, h = lane >> 5;
+  const int m0 = blockIdx.x * GM, n0 = blockIdx.y * GN;
+  const int64_t z = blockIdx.z;
+  // A rows past M read as zeros (buffer range); their results are not stored
+  const unsigned char* abase = g.a + z * g.a_seq_bytes + (int64_t)m0 * g.a_row_bytes;
+  const int a_rows = g.M - m0 < GM ? g.M - m0 : GM;
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(abase), (short)0,
+                                                                      a_rows * g.a_row_bytes, kBufferWord3);
+  const unsigned char* bbase = reinterpret_cast<const unsigned char*>(g.w + (int64_t)n0 * g.K);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(bbase), (short)0,
+                                                                      GN * g.K * 2, kBufferWord3);
+  // this lane's rows in its loads: A row 8j + lane/8 (j = wave, wave+4, ...), B likewise
+  const int lr = lane >> 3, lp = lane & 7;
+  const int nst = g.K / GK;
+  auto issue = [&](int s) {
+    const int slot = s % GSTAGES;
+    const int kb = s * GK * 2;   // byte offset of the chunk within a row
+#pragma unroll
+    for (int q = 0; q < GM / 32; ++q) {   // 4 loads of A rows
+      const int j = wave + 4 * q;
+      const int r = 8 * j + lr;
+      const int off = r * g.a_row_bytes + kb + ((lp ^ swz(r)) << 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sm.a[slot] + 1024 * j), 16, off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < GN / 32; ++q) {   // 8 loads of weight rows
+      const int j = wave + 4 * q;
+      const int r = 8 * j + lr;
+      const int off = r * g.K * 2 + kb + ((lp ^ swz(r)) << 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sm.b[slot] + 1024 * j), 16, off, 0, 0, 0);
+    }
+  };
+  const int wm = wave & 1, wn = wave >> 1;
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = f32x16{};
+  // operand rows of this lane and their swizzles
+  int boff[4], aoff[2], bsw[4], asw[2];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int r = 128 * wn + 32 * nb + l32;
+    boff[nb] = r * 128;
+    bsw[nb] = swz(r);
+  }
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int r = 64 * wm + 32 * mb + l32;
+    aoff[mb] = r * 128;
+    asw[mb] = swz(r);
+  }
+  issue(0);
+  if (nst > 1) issue(1);
+  for (int s = 0; s < nst; ++s) {
+    // this wave's loads of stage s are in; the barrier (LDS only: the loads of
+    // stage s+1 stay in flight) makes every wave's visible and ends every read
+    // of the slot stage s+2 reuses
+    if (s + 1 < nst) __builtin_amdgcn_s_waitcnt(0x0F7C);   // vmcnt(12): stage s+1 may still fly
+    else __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0)
+    lds_sync();
+    if (s + 2 < nst) issue(s + 2);
+    const unsigned char* sa = sm.a[s % GSTAGES];
+    const unsigned char* sb = sm.b[s % GSTAGES];
+#pragma unroll
+    for (int kk = 0; kk < GK / 16; ++kk) {
+      const int c = 2 * kk + h;
+      bf16x8 bo[4], ao[2];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) bo[nb] = lds_read16(sb + boff[nb] + ((c ^ bsw[nb]) << 4));
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) ao[mb] = lds_read16(sa + aoff[mb] + ((c ^ asw[mb]) << 4));
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bo[nb], ao[mb], acc[nb][mb], 0, 0, 0);
+    }
+  }
+  static_assert(G_LOADS == 12, "wait counts assume 12 loads per wave per stage");
+  // acc[nb][mb][i]: n = n0 + 128 wn + 32 nb + 8 (i/4) + 4 h + i%4, m = m0 + 64 wm + 32 mb + l32
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int m = m0 + 64 * wm + 32 * mb + l32;
+    if (m >= g.M) continue;
+    uint16_t* crow = g.c + (z * g.M + m) * (int64_t)g.N + n0 + 128 * wn + 4 * h;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = f32_to_bf16(acc[nb][mb][4 * q + e]);
+        *reinterpret_cast<u16x4*>(crow + 32 * nb + 8 * q) = v;
+      }
+  }
+}
+
+// ------------------------------------------------------------- attention
+// One workgroup = 128 query rows (query tokens) of one head of one sequence;
+// wave w owns rows 32w .. 32w+31 for the whole computation (no exchange of
+// weights between waves).  The cached tokens stream through a 3-stage LDS
+// ring of T = 32 tokens; a stage holds 5 chunk groups of 32 rows x 8 chunks
+// (16 bytes): the key content part (2 groups, from kv), the positional key
+// (1 group, from the cache row) and the value (2 groups, from kv).
+//   S^T[tok][row] = K[tok][0:192] . [q_nope | q_pe]^T   (12 MFMA 32x32x16)
+//   online softmax per row (running maximum, rescaled accumulator)
+//   O^T[dv][row] += V^T[dv][tok] . P^T[tok][row]          (8 MFMA 32x32x16)
+// A lane holds row l%32 and 16 tokens of S^T; its own weights are the B
+// operand of the PV product (the k index of step q maps to tokens
+// 16q + 8(e/4) + 4(l/32) + e%4, the order of the S^T layout), and V^T is read
+// in the same token order by transposed LDS reads.  Two workgroups share a
+// CU (61 KiB of LDS each), so one's softmax runs under the other's MFMAs.
+constexpr int T = 32;
+constexpr int CG = T * 128;                // bytes of one chunk group (4 KiB)
+constexpr int ASTAGE = 5 * CG;             // 20 KiB
+constexpr int ANST = 3;
+constexpr int QK_STEPS = (DN + DR) / 16;   // 12
+
+struct AttnArgs {
+  const uint16_t* q_nope;   // [B][n_q][n_h][128]
+  const uint16_t* q_pe;     // [B][n_q][n_h][64]
+  const int32_t* positions; // [B][n_q]
+  const int32_t* ctx_lens;  // [B]
+  const unsigned char* cache;   // bf16 rows of d_c + 64 elements
+  int64_t cache_seq_bytes;
+  int cache_row_bytes, rope_byte;   // row pitch, byte offset of k^R in a row
+  const unsigned char* kv;  // [B][M][n_h][256] bf16
+  float* out;               // [B][n_q][n_h][128]
+  float* lse;               // [B][n_q][n_h] or null
+  int B, n_q, n_h, M, n_qb, units, units_per_xcd;
+  float scale_log2;
+};
+
+struct __attribute__((aligned(16))) AttnSmem {
+  unsigned char stage[ANST][ASTAGE];
+  int pos_max[4];
+};
+
+__global__ __launch_bounds__(NT, 2) void prefill_attn_kernel(AttnArgs a) {
+  __shared__ AttnSmem sm;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+  const int g4 = lane >> 4, l16 = lane & 15;
+  // workgroups are dealt to the 8 XCDs in turn; XCD x takes the consecutive
+  // units x*U .. x*U+U-1, i.e. the query blocks of a few heads, heaviest
+  // (latest) block first, so the blocks of one head share that XCD's L2
+  const int u = (blockIdx.x & 7) * a.units_per_xcd + (blockIdx.x >> 3);
+  if (u >= a.units) return;
+  const int qb = a.n_qb - 1 - u % a.n_qb;
+  const int hi = (u / a.n_qb) % a.n_h;
+  const int b = u / (a.n_qb * a.n_h);
+  const int j0 = qb * 128;                      // first query row of the block
+  const int ctx = a.ctx_lens[b];
+  // rows past n_q repeat the last query (their results are not stored)
+  const int jr = j0 + 32 * wave + l32;
+  const int jq = jr < a.n_q ? jr : a.n_q - 1;
+  const int64_t qrow = ((int64_t)b * a.n_q + jq) * a.n_h + hi;
+  bf16x8 qreg[QK_STEPS];
+  {
+    const u16x8* qn = reinterpret_cast<const u16x8*>(a.q_nope + qrow * DN);
+    const u16x8* qp = reinterpret_cast<const u16x8*>(a.q_pe + qrow * DR);
+#pragma unroll
+    for (int ks = 0; ks < DN / 16; ++ks) qreg[ks] = __builtin_bit_cast(bf16x8, qn[2 * ks + h]);
+#pragma unroll
+    for (int ks = DN / 16; ks < QK_STEPS; ++ks) qreg[ks] = __builtin_bit_cast(bf16x8, qp[2 * (ks - DN / 16) + h]);
+  }
+  const int pos = a.positions[(int64_t)b * a.n_q + jq];
+  // the stage count follows the workgroup's largest position (every wave runs
+  // the same stages: they share barriers); masking is decided per wave
+  int pmax = pos, pmin = pos;
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) {
+    pmax = max(pmax, __shfl_xor(pmax, sh, 64));
+    pmin = min(pmin, __shfl_xor(pmin, sh, 64));
+  }
+  const int pos_min = __builtin_amdgcn_readfirstlane(pmin);
+  if (lane == 0) sm.pos_max[wave] = pmax;
+  lds_sync();
+  const int pos_last = __builtin_amdgcn_readfirstlane(
+      max(max(sm.pos_max[0], sm.pos_max[1]), max(sm.pos_max[2], sm.pos_max[3])));
+  int n_tok = pos_last + 1 < ctx ? pos_last + 1 : ctx;   // tokens any row sees
+  n_tok = n_tok < a.M ? n_tok : a.M;                      // never past the rows kv holds
+  const int nst = (n_tok + T - 1) / T;
+
+  // loads: wave w fills rows 8w .. 8w+7 of every chunk group of a stage
+  const int tt = 8 * wave + (lane >> 3);
+  const int chunk = ((lane & 7) ^ swz(tt)) << 4;
+  const uint32_t kv_tok = (uint32_t)a.n_h * (KVW * 2);   // bytes between tokens in kv
+  const unsigned char* kvb = a.kv + ((int64_t)b * a.M * a.n_h + hi) * (KVW * 2);
+  const __amdgpu_buffer_rsrc_t rkv = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(kvb), (short)0,
+                                                                       (int)((uint32_t)n_tok * kv_tok), kBufferWord3);
+  const unsigned char* cb = a.cache + (int64_t)b * a.cache_seq_bytes;
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(cb), (short)0,
+                                                                      n_tok * a.cache_row_bytes, kBufferWord3);
+  auto issue = [&](int s) {
+    unsigned char* dst = sm.stage[s % ANST] + 1024 * wave;
+    const uint32_t tok = (uint32_t)(s * T + tt);   // rows past n_tok read as zeros
+    const int vkv = (int)(tok * kv_tok + (uint32_t)chunk);
+    const int vc = (int)(tok * (uint32_t)a.cache_row_bytes + (uint32_t)(a.rope_byte + chunk));
+    // the chunk group's byte offset in the row goes in soffset: an immediate
+    // offset would move the LDS destination as well
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rkv, (lds_void*)(dst + 0 * CG), 16, vkv, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rkv, (lds_void*)(dst + 1 * CG), 16, vkv, 128, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_void*)(dst + 2 * CG), 16, vc, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rkv, (lds_void*)(dst + 3 * CG), 16, vkv, 256, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rkv, (lds_void*)(dst + 4 * CG), 16, vkv, 384, 0, 0);
+  };
+
+  // LDS offsets of this lane's operands
+  const int sw_qk = swz(l32);
+  int qk_off[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) qk_off[r] = l32 * 128 + (((2 * r + h) ^ sw_qk) << 4);
+  const int hq = g4 >> 1;
+  const int tr_tok = 4 * hq + (l16 >> 2);
+  const int sw_tr0 = swz(tr_tok), sw_tr1 = swz(8 + tr_tok);
+  const int half8 = (l16 & 1) * 8;
+  const int cch = 2 * (g4 & 1) + ((l16 & 3) >> 1);
+  auto rd_v = [&](const unsigned char* sb, int q, int db) -> bf16x8 {
+    const int cq = 4 * (db & 1) + cch;
+    bf16x4 v[2];
+#pragma unroll
+    for (int ins = 0; ins < 2; ++ins) {
+      const int t = 16 * q + 8 * ins + tr_tok;
+      const unsigned char* p = sb + (3 + (db >> 1)) * CG + t * 128 + ((cq ^ (ins ? sw_tr1 : sw_tr0)) << 4) + half8;
+      v[ins] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (lds_bf16x4*)((__attribute__((address_space(3))) unsigned char*)p));
+    }
+    return __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+
+  f32x16 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const int lim = pos - 4 * h;   // score i is token 8(i/4) + 4h + i%4 of the stage: visible while <= pos
+
+  issue(0);
+  if (nst > 1) issue(1);
+  for (int s = 0; s < nst; ++s) {
+    if (s + 1 < nst) __builtin_amdgcn_s_waitcnt(0x0F75);   // vmcnt(5): stage s+1 may still fly
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+    lds_sync();
+    if (s + 2 < nst) issue(s + 2);
+    const unsigned char* sb = sm.stage[s % ANST];
+    f32x16 st = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < QK_STEPS; ++ks)
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read16(sb + (ks >> 2) * CG + qk_off[ks & 3]), qreg[ks], st,
+                                                   0, 0, 0);
+    // online softmax of this stage (log2 units)
+    const int tok0 = s * T;
+    const bool masked = tok0 + T - 1 > pos_min;   // some row of this wave may not see all the stage's tokens
+    float mt = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int rel = 8 * (i >> 2) + (i & 3);
+      float x = st[i] * a.scale_log2;
+      if (masked) x = tok0 + rel <= lim ? x : -INFINITY;
+      st[i] = x;
+      mt = fmaxf(mt, x);
+    }
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+      mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const float m_new = fmaxf(m_run, mt);
+    // rows with nothing visible yet keep m = -inf, weights 0 and alpha 1
+    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    const float neg = m_new == -INFINITY ? 0.f : -m_new;
+    m_run = m_new;
+    float psum = 0.f;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = __builtin_amdgcn_exp2f(st[i] + neg);
+      psum += p;
+      pb[i >> 3][i & 7] = (__bf16)p;
+    }
+    l_run = l_run * alpha + psum;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_v(sb, q, db), pb[q], o[db], 0, 0, 0);
+  }
+  // ---- results: o[db][i] = O[row l32][dv 32 db + 8 (i/4) + 4 h + i%4]
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (jr < a.n_q) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float* op = a.out + qrow * DV + 4 * h;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4*>(op + 32 * db + 8 * q) =
+            f32x4{o[db][4 * q] * inv, o[db][4 * q + 1] * inv, o[db][4 * q + 2] * inv, o[db][4 * q + 3] * inv};
+    if (a.lse != nullptr && h == 0)
+      a.lse[qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_weights(const uint16_t* w_uk, const uint16_t* w_uv, uint16_t* w_kv, int n_h, int d_c,
+                                  hipStream_t stream) {
+  hipLaunchKernelGGL(prefill_weights_kernel, dim3(d_c / 32, KVW / 32, n_h), dim3(NT), 0, stream, w_uk, w_uv, w_kv,
+                     d_c);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
+  // 1. keys' content part and values of every head, tokens 0 .. max_ctx-1
+  GemmArgs g;
+  g.a = static_cast<const unsigned char*>(p.cache.data);
+  g.a_seq_bytes = p.cache.seq_stride * 2;
+  g.a_row_bytes = p.cache.row * 2;
+  g.w = static_cast<const uint16_t*>(p.w_kv);
+  g.c = static_cast<uint16_t*>(p.kv);
+  g.M = p.max_ctx;
+  g.N = p.n_h * KVW;
+  g.K = p.d_c;
+  hipLaunchKernelGGL(reconstruct_gemm_kernel, dim3((g.M + GM - 1) / GM, g.N / GN, p.B), dim3(NT), 0, stream, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // 2. attention
+  AttnArgs a;
+  a.q_nope = static_cast<const uint16_t*>(p.q_nope);
+  a.q_pe = static_cast<const uint16_t*>(p.q_pe);
+  a.positions = p.positions;
+  a.ctx_lens = p.ctx_lens;
+  a.cache = static_cast<const unsigned char*>(p.cache.data);
+  a.cache_seq_bytes = p.cache.seq_stride * 2;
+  a.cache_row_bytes = p.cache.row * 2;
+  a.rope_byte = p.d_c * 2;
+  a.kv = static_cast<const unsigned char*>(p.kv);
+  a.out = p.out;
+  a.lse = p.lse;
+  a.B = p.B;
+  a.n_q = p.n_q;
+  a.n_h = p.n_h;
+  a.M = p.max_ctx;
+  a.n_qb = (p.n_q + 127) / 128;
+  a.units = p.B * p.n_h * a.n_qb;
+  a.units_per_xcd = (a.units + 7) / 8;
+  a.scale_log2 = p.sm_scale * kLog2e;
+  hipLaunchKernelGGL(prefill_attn_kernel, dim3(a.units_per_xcd * 8), dim3(NT), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla
