@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40,
                     help="untimed steps first; the clock settles within ~10 ms of load")
     ap.add_argument("--workload", default="v3_b64")
+    ap.add_argument("--prefill", choices=("prompt4k", "chunk1k"), default=None,
+                    help="time mla_prefill instead of the decode step: a 4096-token prompt (B=1), or 1024-token "
+                         "chunks after 7168 cached tokens (B=4)")
     ap.add_argument("--cache", choices=("native", "fp8"), default="native",
                     help="cache storage: the workload's own dtype, or fp8 e4m3 with per-128-channel scales")
     ap.add_argument("--num-splits", type=int, default=0, help="0 = library default for the batch")
@@ -331,6 +334,71 @@ def session_bench(args):
     print(json.dumps(result), flush=True)
 
 
+PREFILL_WORKLOADS = {"prompt4k": (1, 4096, 4096), "chunk1k": (4, 8192, 1024)}   # B, ctx, n_q
+
+
+def prefill_bench(args):
+    """mla_prefill at V3 shapes: the cache holds ctx rows per sequence, the last
+    n_q of them are queries (positions ctx - n_q .. ctx - 1).  Cache rows come
+    from the seeded device generator, queries from a seeded device normal draw.
+    FLOPs = attention 2 (d_nope + d_rope + d_v) per (query, visible token, head)
+    + reconstruction 2 d_c (d_nope + d_v) per (cached token, head)."""
+    import torch
+    import mla_latent_kv_02_amd as mla
+    import workloads as W
+    from workloads.device import stage
+    B, ctx, n_q = PREFILL_WORKLOADS[args.prefill]
+    w = W.custom(name=f"v3_prefill_{args.prefill}", seed=71, batch=B, n_q=1, ctx=ctx,
+                 description=f"DeepSeek-V3 shapes, B={B}, ctx {ctx}, the last {n_q} tokens prefilled")
+    log(f"staging {w.name}")
+    st = stage(w)
+    d = st["dims"]
+    g = torch.Generator(device="cuda").manual_seed(72)
+    bf = torch.bfloat16
+    q_nope = torch.randn((B, n_q, w.n_h, w.d_nope), generator=g, device="cuda").to(bf)
+    q_rope = torch.randn((B, n_q, w.n_h, w.d_rope), generator=g, device="cuda").to(bf)
+    positions = torch.arange(ctx - n_q, ctx, dtype=torch.int32, device="cuda").repeat(B, 1).contiguous()
+    w_kv = torch.empty((w.n_h, w.d_nope + w.d_v, w.d_c), dtype=bf, device="cuda")
+    mla.mla_prefill_weights(d, st["w_uk"], st["w_uv"], w_kv)
+    ws = torch.empty((mla.mla_prefill_workspace_bytes(d, B, ctx) // 2,), dtype=bf, device="cuda")
+    q_pe = torch.empty((B, n_q, w.n_h, w.d_rope), dtype=bf, device="cuda")
+    out = torch.empty((B, n_q, w.n_h, w.d_v), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, n_q, w.n_h), dtype=torch.float32, device="cuda")
+
+    def run():
+        mla.mla_prefill(d, ctx, q_nope, q_rope, positions, st["cache"], w_kv, ws, q_pe, out, lse)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        run()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    visible = B * sum(p + 1 for p in range(ctx - n_q, ctx))
+    f_attn = visible * w.n_h * 2 * (w.d_nope + w.d_rope + w.d_v)
+    f_rec = B * ctx * w.n_h * 2 * w.d_c * (w.d_nope + w.d_v)
+    tflops = (f_attn + f_rec) / (ms * 1e-3) / 1e12
+    log(f"prefill {ms * 1e3:.1f} us; attention {f_attn / 1e9:.1f} GFLOP + reconstruction {f_rec / 1e9:.1f} GFLOP")
+    print(json.dumps({
+        "metric": "MLA prefill TFLOP/s (DeepSeek-V3 shapes)", "value": round(tflops, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Philox N(0,1) cache latents, seeded device N(0,1) queries, N(0,1/d_c) weights)",
+        "config": {"workload": w.name, "description": w.description, "batch": B, "ctx": ctx, "n_q": n_q,
+                   "n_h": w.n_h, "d_c": w.d_c, "d_rope": w.d_rope, "d_nope": w.d_nope, "d_v": w.d_v},
+        "tokens_per_s": round(B * n_q / (ms * 1e-3), 1),
+        "flops_per_call": {"attention": f_attn, "reconstruction": f_rec},
+        "roofline": {"kernel": "mla_prefill (reconstruct_gemm_kernel + prefill_attn_kernel)", "bound": "mfma",
+                     "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFS, 4), "traffic": None},
+        "cpu_baseline": None}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -345,6 +413,9 @@ def main():
         return
     if args.folds:
         folds_bench(args)
+        return
+    if args.prefill:
+        prefill_bench(args)
         return
     import numpy as np
     import torch

@@ -64,12 +64,16 @@ __global__ __launch_bounds__(NT) void prefill_weights_kernel(const uint16_t* __r
 // takes m rows 64(w%2) .. +64 and n rows 128(w/2) .. +128 (2 x 4 blocks of
 // 32 x 32).  The weight rows are the MFMA's first operand, so a lane's
 // results are 4 consecutive n of one m (one 8-byte store each).  The k range
-// is streamed in chunks of 64 through a 3-stage LDS ring: row r of a stage
-// holds 8 chunks of 16 bytes, chunk c at slot c ^ s(r); a wave's 16-byte
-// global->LDS load writes 8 rows x 128 bytes.
-constexpr int GM = 128, GN = 256, GK = 64, GSTAGES = 3;
-constexpr int GA_BYTES = GM * GK * 2, GB_BYTES = GN * GK * 2;   // 16 KiB, 32 KiB
-constexpr int G_LOADS = (GM + GN) / 8 / 4;                      // 1 KiB loads per wave per stage: 12
+// is streamed in chunks of 32 through a 3-stage LDS ring (72 KiB, so two
+// workgroups share a CU): row r of a stage holds 4 chunks of 16 bytes, chunk
+// c at slot c ^ ((r / 4) % 4), which spreads 16 consecutive rows read at one
+// chunk over all 64 banks; a wave's 16-byte global->LDS load writes 16 rows x
+// 64 bytes.
+constexpr int GM = 128, GN = 256, GK = 32, GSTAGES = 3;
+constexpr int GROW = GK * 2;                                    // LDS row: 64 bytes
+constexpr int GA_BYTES = GM * GROW, GB_BYTES = GN * GROW;       // 8 KiB, 16 KiB
+constexpr int G_LOADS = (GM + GN) / 16 / 4;                     // 1 KiB loads per wave per stage: 6
+__device__ __forceinline__ int gswz(int r) { return (r >> 2) & 3; }
 
 struct GemmArgs {
   const unsigned char* a;   // cache data (bf16 rows)
@@ -85,7 +89,7 @@ struct __attribute__((aligned(16))) GemmSmem {
   unsigned char b[GSTAGES][GB_BYTES];
 };
 
-__global__ __launch_bounds__(NT, 1) void reconstruct_gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(NT, 2) void reconstruct_gemm_kernel(GemmArgs g) {
   __shared__ GemmSmem sm;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -100,24 +104,24 @@ __global__ __launch_bounds__(NT, 1) void reconstruct_gemm_kernel(GemmArgs g) {
   const unsigned char* bbase = reinterpret_cast<const unsigned char*>(g.w + (int64_t)n0 * g.K);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(bbase), (short)0,
                                                                       GN * g.K * 2, kBufferWord3);
-  // this lane's rows in its loads: A row 8j + lane/8 (j = wave, wave+4, ...), B likewise
-  const int lr = lane >> 3, lp = lane & 7;
+  // this lane's rows in its loads: A row 16j + lane/4 (j = wave, wave+4), B likewise
+  const int lr = lane >> 2, lp = lane & 3;
   const int nst = g.K / GK;
   auto issue = [&](int s) {
     const int slot = s % GSTAGES;
-    const int kb = s * GK * 2;   // byte offset of the chunk within a row
+    const int kb = s * GROW;   // byte offset of the chunk within a row
 #pragma unroll
-    for (int q = 0; q < GM / 32; ++q) {   // 4 loads of A rows
+    for (int q = 0; q < GM / 64; ++q) {   // 2 loads of A rows
       const int j = wave + 4 * q;
-      const int r = 8 * j + lr;
-      const int off = r * g.a_row_bytes + kb + ((lp ^ swz(r)) << 4);
+      const int r = 16 * j + lr;
+      const int off = r * g.a_row_bytes + kb + ((lp ^ gswz(r)) << 4);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sm.a[slot] + 1024 * j), 16, off, 0, 0, 0);
     }
 #pragma unroll
-    for (int q = 0; q < GN / 32; ++q) {   // 8 loads of weight rows
+    for (int q = 0; q < GN / 64; ++q) {   // 4 loads of weight rows
       const int j = wave + 4 * q;
-      const int r = 8 * j + lr;
-      const int off = r * g.K * 2 + kb + ((lp ^ swz(r)) << 4);
+      const int r = 16 * j + lr;
+      const int off = r * g.K * 2 + kb + ((lp ^ gswz(r)) << 4);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sm.b[slot] + 1024 * j), 16, off, 0, 0, 0);
     }
   };
@@ -132,14 +136,14 @@ __global__ __launch_bounds__(NT, 1) void reconstruct_gemm_kernel(GemmArgs g) {
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const int r = 128 * wn + 32 * nb + l32;
-    boff[nb] = r * 128;
-    bsw[nb] = swz(r);
+    boff[nb] = r * GROW;
+    bsw[nb] = gswz(r);
   }
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     const int r = 64 * wm + 32 * mb + l32;
-    aoff[mb] = r * 128;
-    asw[mb] = swz(r);
+    aoff[mb] = r * GROW;
+    asw[mb] = gswz(r);
   }
   issue(0);
   if (nst > 1) issue(1);
@@ -147,7 +151,7 @@ __global__ __launch_bounds__(NT, 1) void reconstruct_gemm_kernel(GemmArgs g) {
     // this wave's loads of stage s are in; the barrier (LDS only: the loads of
     // stage s+1 stay in flight) makes every wave's visible and ends every read
     // of the slot stage s+2 reuses
-    if (s + 1 < nst) __builtin_amdgcn_s_waitcnt(0x0F7C);   // vmcnt(12): stage s+1 may still fly
+    if (s + 1 < nst) __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6): stage s+1 may still fly
     else __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0)
     lds_sync();
     if (s + 2 < nst) issue(s + 2);
@@ -168,7 +172,7 @@ __global__ __launch_bounds__(NT, 1) void reconstruct_gemm_kernel(GemmArgs g) {
           acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bo[nb], ao[mb], acc[nb][mb], 0, 0, 0);
     }
   }
-  static_assert(G_LOADS == 12, "wait counts assume 12 loads per wave per stage");
+  static_assert(G_LOADS == 6, "wait counts assume 6 loads per wave per stage");
   // acc[nb][mb][i]: n = n0 + 128 wn + 32 nb + 8 (i/4) + 4 h + i%4, m = m0 + 64 wm + 32 mb + l32
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
@@ -341,21 +345,20 @@ __global__ __launch_bounds__(NT, 2) void prefill_attn_kernel(AttnArgs a) {
     for (int ks = 0; ks < QK_STEPS; ++ks)
       st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read16(sb + (ks >> 2) * CG + qk_off[ks & 3]), qreg[ks], st,
                                                    0, 0, 0);
-    // online softmax of this stage (log2 units)
+    // online softmax of this stage (log2 units; the scale is folded into the
+    // exponent's fma, and the row maximum of the raw scores scaled once)
     const int tok0 = s * T;
     const bool masked = tok0 + T - 1 > pos_min;   // some row of this wave may not see all the stage's tokens
     float mt = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int rel = 8 * (i >> 2) + (i & 3);
-      float x = st[i] * a.scale_log2;
-      if (masked) x = tok0 + rel <= lim ? x : -INFINITY;
-      st[i] = x;
-      mt = fmaxf(mt, x);
+      if (masked) st[i] = tok0 + rel <= lim ? st[i] : -INFINITY;
+      mt = fmaxf(mt, st[i]);
     }
     {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
-      mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.scale_log2;
     }
     const float m_new = fmaxf(m_run, mt);
     // rows with nothing visible yet keep m = -inf, weights 0 and alpha 1
@@ -366,7 +369,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_attn_kernel(AttnArgs a) {
     bf16x8 pb[2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float p = __builtin_amdgcn_exp2f(st[i] + neg);
+      const float p = __builtin_amdgcn_exp2f(fmaf(st[i], a.scale_log2, neg));
       psum += p;
       pb[i >> 3][i & 7] = (__bf16)p;
     }

@@ -70,29 +70,85 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(AbsorbParams p) {
   }
 }
 
-// Query RoPE: one thread per (query row m, rotation plane k, group of 4
-// heads); the fp64 angle depends on (m, k) only.
-template <typename T>
+// Query RoPE over rows (query row m, head i) of d_rope elements.  Items are
+// runs of 4 rotation planes (16 bytes of a bf16 row) when the rows allow
+// (d_rope % 8 == 0 and 16-byte aligned arrays; VEC), else single planes; the
+// plane index runs fastest, so a wave reads and writes contiguous bytes.  A
+// grid-stride loop over a few workgroups per CU builds the frequency table
+// once per workgroup (fp64).  fp32 rows take fp64 sin and cos of the angle;
+// bf16 rows the fp32 sin and cos of the fp64-reduced angle in turns (about
+// 1e-6 absolute, far below a bf16 step), as the one-pass kernel does.
+template <typename T, bool VEC>
 __global__ __launch_bounds__(256) void rope_q_rows_kernel(AbsorbParams p) {
+  __shared__ double freq[64];   // turns (bf16) or radians (fp32) per unit of position
   const int half = p.d_rope / 2;
-  const int hgroups = (p.n_h + 3) / 4;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t n = (int64_t)p.B * p.n_q * half * hgroups;
-  if (idx >= n) return;
-  const int hg = (int)(idx % hgroups);
-  const int k = (int)((idx / hgroups) % half);
-  const int64_t m = idx / ((int64_t)hgroups * half);
+  const bool table = half <= 64;
+  if (table && (int)threadIdx.x < half) {
+    const double th = pow((double)p.rope_base, -2.0 * threadIdx.x / p.d_rope);
+    freq[threadIdx.x] = sizeof(T) == 2 ? th * kInv2Pi : th;
+  }
+  __syncthreads();
+  constexpr int PER = VEC ? 4 : 1;   // planes per item
+  const int per_row = half / PER;
+  const int64_t items = (int64_t)p.B * p.n_q * p.n_h * per_row;
   const T* src = static_cast<const T*>(p.q_rope);
   T* dst = static_cast<T*>(p.q_pe);
-  double sd, cd;
-  sincos((double)p.positions[m] * pow((double)p.rope_base, -2.0 * k / p.d_rope), &sd, &cd);
-  const float c = (float)cd, s = (float)sd;
-  for (int i = 4 * hg; i < 4 * hg + 4 && i < p.n_h; ++i) {
-    const int64_t off = ((int64_t)m * p.n_h + i) * p.d_rope + 2 * k;
-    const float x0 = Elem<T>::load(src, off), x1 = Elem<T>::load(src, off + 1);
-    Elem<T>::store(dst, off, x0 * c - x1 * s);
-    Elem<T>::store(dst, off + 1, x0 * s + x1 * c);
+  for (int64_t it = (int64_t)blockIdx.x * 256 + threadIdx.x; it < items; it += (int64_t)gridDim.x * 256) {
+    const int k0 = (int)(it % per_row) * PER;
+    const int64_t mi = it / per_row;             // m * n_h + i
+    const int pos = p.positions[mi / p.n_h];
+    const int64_t off = mi * p.d_rope + 2 * k0;
+    float x[2 * PER], y[2 * PER];
+    if (VEC && sizeof(T) == 2) {
+      const u16x8 v = *reinterpret_cast<const u16x8*>(src + off);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = bf16_to_f32(v[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 2 * PER; ++e) x[e] = Elem<T>::load(src, off + e);
+    }
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int k = k0 + q;
+      float c, s;
+      if (sizeof(T) == 2) {
+        const double turns = table ? freq[k] : pow((double)p.rope_base, -2.0 * k / p.d_rope) * kInv2Pi;
+        sincos_turns(pos, turns, &s, &c);
+      } else {
+        const double th = table ? freq[k] : pow((double)p.rope_base, -2.0 * k / p.d_rope);
+        double sd, cd;
+        sincos((double)pos * th, &sd, &cd);
+        c = (float)cd;
+        s = (float)sd;
+      }
+      y[2 * q] = x[2 * q] * c - x[2 * q + 1] * s;
+      y[2 * q + 1] = x[2 * q] * s + x[2 * q + 1] * c;
+    }
+    if (VEC && sizeof(T) == 2) {
+      u16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = f32_to_bf16(y[e]);
+      *reinterpret_cast<u16x8*>(dst + off) = v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 2 * PER; ++e) Elem<T>::store(dst, off + e, y[e]);
+    }
   }
+}
+
+// Launch of the query RoPE: 16-byte items where the arrays allow.
+template <typename T>
+hipError_t launch_rope_rows(const AbsorbParams& p, hipStream_t stream) {
+  const int64_t rows = (int64_t)p.B * p.n_q * p.n_h;
+  if (rows == 0) return hipSuccess;
+  const bool vec = sizeof(T) == 2 && p.d_rope % 8 == 0 && reinterpret_cast<uintptr_t>(p.q_rope) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(p.q_pe) % 16 == 0;
+  const int64_t items = rows * (p.d_rope / 2) / (vec ? 4 : 1);
+  const int64_t want = (items + 255) / 256;
+  const dim3 grid((unsigned)(want < 2048 ? want : 2048));
+  if (vec) hipLaunchKernelGGL((rope_q_rows_kernel<T, true>), grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL((rope_q_rows_kernel<T, false>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
 }
 
 // ------------------------------------------- absorption + query RoPE, one pass
@@ -337,12 +393,7 @@ __global__ __launch_bounds__(256) void out_proj_mfma_kernel(OutProjParams p) {
 }  // namespace
 
 hipError_t launch_rope_q(const AbsorbParams& p, hipStream_t stream) {
-  const int64_t nthreads = (int64_t)p.B * p.n_q * (p.d_rope / 2) * ((p.n_h + 3) / 4);
-  if (nthreads == 0) return hipSuccess;
-  const dim3 grid((unsigned)((nthreads + 255) / 256));
-  if (p.bf16) hipLaunchKernelGGL(rope_q_rows_kernel<uint16_t>, grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL(rope_q_rows_kernel<float>, grid, dim3(256), 0, stream, p);
-  return hipGetLastError();
+  return p.bf16 ? launch_rope_rows<uint16_t>(p, stream) : launch_rope_rows<float>(p, stream);
 }
 
 bool absorb_mfma_ok(const AbsorbParams& p) {
@@ -376,10 +427,9 @@ hipError_t launch_append_absorb_mfma(const AbsorbParams& p, const AppendParams* 
     return hipGetLastError();
   }
   hipLaunchKernelGGL(absorb_mfma_kernel, dim3(p.n_h, p.d_c / 64), dim3(256), 0, stream, p);
-  const int64_t nthreads = (int64_t)M * (p.d_rope / 2) * ((p.n_h + 3) / 4);
-  hipLaunchKernelGGL(rope_q_rows_kernel<uint16_t>, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0,
-                     stream, p);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_rope_rows<uint16_t>(p, stream);
 }
 
 bool out_proj_mfma_ok(const OutProjParams& p) {
