@@ -246,7 +246,7 @@ int64_t mla_prefill_workspace_bytes(const mla_dims_t *dims, int32_t B, int32_t m
  *   q_pe      [B][n_q][n_h][d_rope]   bf16, out: RoPE(q_rope, positions)
  *   out       [B][n_q][n_h][d_v]      fp32, out
  *   lse       [B][n_q][n_h]           fp32, out (may be NULL)
- * Requires 1 <= n_q <= max_ctx and (max_ctx + 32) * n_h * (d_nope + d_v) * 2 < 2^32. */
+ * Requires 1 <= n_q <= max_ctx and (max_ctx + 64) * n_h * (d_nope + d_v) * 2 < 2^32. */
 mla_status_t mla_prefill(const mla_dims_t *dims, int32_t B, int32_t n_q, int32_t max_ctx, const void *q_nope,
                          const void *q_rope, const int32_t *positions, const mla_cache_t *cache,
                          const void *w_kv, void *workspace, int64_t workspace_bytes, void *q_pe, float *out,

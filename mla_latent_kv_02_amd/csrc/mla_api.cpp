@@ -268,7 +268,7 @@ mla_status_t mla_prefill(const mla_dims_t* dims, int32_t B, int32_t n_q, int32_t
   if (!prefill_dims_ok(dims) || cache->dtype != MLA_BF16 || cache->block_size != 0) return MLA_ERR_UNSUPPORTED;
   if (cache->seq_stride < (int64_t)max_ctx * (dims->d_c + dims->d_rope)) return MLA_ERR_INVALID_ARG;
   const int64_t kv_tok = (int64_t)dims->n_h * (dims->d_nope + dims->d_v) * 2;
-  if ((int64_t)(max_ctx + 32) * kv_tok >= (1LL << 32) || (int64_t)(max_ctx + 32) * (dims->d_c + dims->d_rope) * 2 >=
+  if ((int64_t)(max_ctx + 64) * kv_tok >= (1LL << 32) || (int64_t)(max_ctx + 64) * (dims->d_c + dims->d_rope) * 2 >=
       (1LL << 31) || B > 65535 || (int64_t)B * n_q > (1 << 24))
     return MLA_ERR_UNSUPPORTED;
   const hipStream_t s = (hipStream_t)stream;

@@ -194,23 +194,25 @@ __global__ __launch_bounds__(NT, 2) void reconstruct_gemm_kernel(GemmArgs g) {
 // ------------------------------------------------------------- attention
 // One workgroup = 128 query rows (query tokens) of one head of one sequence;
 // wave w owns rows 32w .. 32w+31 for the whole computation (no exchange of
-// weights between waves).  The cached tokens stream through a 3-stage LDS
-// ring of T = 32 tokens; a stage holds 5 chunk groups of 32 rows x 8 chunks
+// weights between waves).  The cached tokens stream through a 2-stage LDS
+// ring of T = 64 tokens; a stage holds 5 chunk groups of 64 rows x 8 chunks
 // (16 bytes): the key content part (2 groups, from kv), the positional key
-// (1 group, from the cache row) and the value (2 groups, from kv).
-//   S^T[tok][row] = K[tok][0:192] . [q_nope | q_pe]^T   (12 MFMA 32x32x16)
+// (1 group, from the cache row) and the value (2 groups, from kv).  Per stage:
+//   S^T[tok][row] = K[tok][0:192] . [q_nope | q_pe]^T   (2 blocks of 32 tokens,
+//                   two independent chains of 12 MFMA 32x32x16)
 //   online softmax per row (running maximum, rescaled accumulator)
-//   O^T[dv][row] += V^T[dv][tok] . P^T[tok][row]          (8 MFMA 32x32x16)
-// A lane holds row l%32 and 16 tokens of S^T; its own weights are the B
-// operand of the PV product (the k index of step q maps to tokens
+//   O^T[dv][row] += V^T[dv][tok] . P^T[tok][row]          (16 MFMA 32x32x16)
+// A lane holds row l%32 and 16 tokens of each S^T block; its own weights are
+// the B operand of the PV product (the k index of step q maps to tokens
 // 16q + 8(e/4) + 4(l/32) + e%4, the order of the S^T layout), and V^T is read
 // in the same token order by transposed LDS reads.  Two workgroups share a
-// CU (61 KiB of LDS each), so one's softmax runs under the other's MFMAs.
-constexpr int T = 32;
-constexpr int CG = T * 128;                // bytes of one chunk group (4 KiB)
-constexpr int ASTAGE = 5 * CG;             // 20 KiB
-constexpr int ANST = 3;
+// CU (80 KiB of LDS each), so one's softmax runs under the other's MFMAs.
+constexpr int T = 64;
+constexpr int CG = T * 128;                // bytes of one chunk group (8 KiB)
+constexpr int ASTAGE = 5 * CG;             // 40 KiB
+constexpr int ANST = 2;
 constexpr int QK_STEPS = (DN + DR) / 16;   // 12
+constexpr int A_LOADS = 10;                // 1 KiB global->LDS loads per wave per stage
 
 struct AttnArgs {
   const uint16_t* q_nope;   // [B][n_q][n_h][128]
@@ -229,8 +231,8 @@ struct AttnArgs {
 
 struct __attribute__((aligned(16))) AttnSmem {
   unsigned char stage[ANST][ASTAGE];
-  int pos_max[4];
 };
+static_assert(2 * sizeof(AttnSmem) <= 160 * 1024, "two workgroups per CU");
 
 __global__ __launch_bounds__(NT, 2) void prefill_attn_kernel(AttnArgs a) {
   __shared__ AttnSmem sm;
@@ -243,11 +245,14 @@ __global__ __launch_bounds__(NT, 2) void prefill_attn_kernel(AttnArgs a) {
   // (latest) block first, so the blocks of one head share that XCD's L2
   const int u = (blockIdx.x & 7) * a.units_per_xcd + (blockIdx.x >> 3);
   if (u >= a.units) return;
-  const int qb = a.n_qb - 1 - u % a.n_qb;
-  const int hi = (u / a.n_qb) % a.n_h;
-  const int b = u / (a.n_qb * a.n_h);
+  // (readfirstlane: the compiler is told these are uniform, so the buffer
+  // resources built from them stay in scalar registers)
+  const int qb = __builtin_amdgcn_readfirstlane(a.n_qb - 1 - u % a.n_qb);
+  const int hi = __builtin_amdgcn_readfirstlane((u / a.n_qb) % a.n_h);
+  const int b = __builtin_amdgcn_readfirstlane(u / (a.n_qb * a.n_h));
   const int j0 = qb * 128;                      // first query row of the block
-  const int ctx = a.ctx_lens[b];
+  // (a length outside [0, M] is a caller error; clamped, no access leaves kv)
+  const int ctx = __builtin_amdgcn_readfirstlane(min(max(a.ctx_lens[b], 0), a.M));
   // rows past n_q repeat the last query (their results are not stored)
   const int jr = j0 + 32 * wave + l32;
   const int jq = jr < a.n_q ? jr : a.n_q - 1;
@@ -261,9 +266,13 @@ __global__ __launch_bounds__(NT, 2) void prefill_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int ks = DN / 16; ks < QK_STEPS; ++ks) qreg[ks] = __builtin_bit_cast(bf16x8, qp[2 * (ks - DN / 16) + h]);
   }
-  const int pos = a.positions[(int64_t)b * a.n_q + jq];
+  // the last token the row sees: its position, within the sequence's cached tokens
+  const int pos_q = a.positions[(int64_t)b * a.n_q + jq];
+  const int pos = pos_q < ctx ? pos_q : ctx - 1;
   // the stage count follows the workgroup's largest position (every wave runs
-  // the same stages: they share barriers); masking is decided per wave
+  // the same stages: they share barriers); masking is decided per wave.  The
+  // four waves' maxima meet in the first bytes of stage 1, before any load
+  // writes there (the second barrier ends the reads).
   int pmax = pos, pmin = pos;
 #pragma unroll
   for (int sh = 32; sh >= 1; sh >>= 1) {
@@ -271,17 +280,18 @@ __global__ __launch_bounds__(NT, 2) void prefill_attn_kernel(AttnArgs a) {
     pmin = min(pmin, __shfl_xor(pmin, sh, 64));
   }
   const int pos_min = __builtin_amdgcn_readfirstlane(pmin);
-  if (lane == 0) sm.pos_max[wave] = pmax;
+  int* xchg = reinterpret_cast<int*>(sm.stage[1]);
+  if (lane == 0) xchg[wave] = pmax;
   lds_sync();
-  const int pos_last = __builtin_amdgcn_readfirstlane(
-      max(max(sm.pos_max[0], sm.pos_max[1]), max(sm.pos_max[2], sm.pos_max[3])));
-  int n_tok = pos_last + 1 < ctx ? pos_last + 1 : ctx;   // tokens any row sees
-  n_tok = n_tok < a.M ? n_tok : a.M;                      // never past the rows kv holds
+  const int pos_last = __builtin_amdgcn_readfirstlane(max(max(xchg[0], xchg[1]), max(xchg[2], xchg[3])));
+  lds_sync();
+  // tokens any row sees (ctx <= M, the rows kv holds, is checked by the caller)
+  const int n_tok = __builtin_amdgcn_readfirstlane(pos_last + 1);
   const int nst = (n_tok + T - 1) / T;
 
-  // loads: wave w fills rows 8w .. 8w+7 of every chunk group of a stage
-  const int tt = 8 * wave + (lane >> 3);
-  const int chunk = ((lane & 7) ^ swz(tt)) << 4;
+  // loads: wave w fills rows 8w .. 8w+7 and 32+8w .. 32+8w+7 of every chunk group
+  const int tt0 = 8 * wave + (lane >> 3);           // the second rows are tt0 + 32, same swizzle
+  const int chunk = ((lane & 7) ^ swz(tt0)) << 4;
   const uint32_t kv_tok = (uint32_t)a.n_h * (KVW * 2);   // bytes between tokens in kv
   const unsigned char* kvb = a.kv + ((int64_t)b * a.M * a.n_h + hi) * (KVW * 2);
   const __amdgpu_buffer_rsrc_t rkv = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(kvb), (short)0,
@@ -290,20 +300,23 @@ __global__ __launch_bounds__(NT, 2) void prefill_attn_kernel(AttnArgs a) {
   const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(cb), (short)0,
                                                                       n_tok * a.cache_row_bytes, kBufferWord3);
   auto issue = [&](int s) {
-    unsigned char* dst = sm.stage[s % ANST] + 1024 * wave;
-    const uint32_t tok = (uint32_t)(s * T + tt);   // rows past n_tok read as zeros
-    const int vkv = (int)(tok * kv_tok + (uint32_t)chunk);
-    const int vc = (int)(tok * (uint32_t)a.cache_row_bytes + (uint32_t)(a.rope_byte + chunk));
-    // the chunk group's byte offset in the row goes in soffset: an immediate
-    // offset would move the LDS destination as well
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rkv, (lds_void*)(dst + 0 * CG), 16, vkv, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rkv, (lds_void*)(dst + 1 * CG), 16, vkv, 128, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_void*)(dst + 2 * CG), 16, vc, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rkv, (lds_void*)(dst + 3 * CG), 16, vkv, 256, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rkv, (lds_void*)(dst + 4 * CG), 16, vkv, 384, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      unsigned char* dst = sm.stage[s % ANST] + 1024 * wave + 4096 * e;   // rows 8w + 32e ..
+      const uint32_t tok = (uint32_t)(s * T + tt0 + 32 * e);   // rows past n_tok read as zeros
+      const int vkv = (int)(tok * kv_tok + (uint32_t)chunk);
+      const int vc = (int)(tok * (uint32_t)a.cache_row_bytes + (uint32_t)(a.rope_byte + chunk));
+      // the chunk group's byte offset in the row goes in soffset: an immediate
+      // offset would move the LDS destination as well
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rkv, (lds_void*)(dst + 0 * CG), 16, vkv, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rkv, (lds_void*)(dst + 1 * CG), 16, vkv, 128, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_void*)(dst + 2 * CG), 16, vc, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rkv, (lds_void*)(dst + 3 * CG), 16, vkv, 256, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rkv, (lds_void*)(dst + 4 * CG), 16, vkv, 384, 0, 0);
+    }
   };
 
-  // LDS offsets of this lane's operands
+  // LDS offsets of this lane's operands (token l32 of block 0; block 1 is 32 rows on, same swizzle)
   const int sw_qk = swz(l32);
   int qk_off[4];
 #pragma unroll
@@ -313,6 +326,12 @@ __global__ __launch_bounds__(NT, 2) void prefill_attn_kernel(AttnArgs a) {
   const int sw_tr0 = swz(tr_tok), sw_tr1 = swz(8 + tr_tok);
   const int half8 = (l16 & 1) * 8;
   const int cch = 2 * (g4 & 1) + ((l16 & 3) >> 1);
+  // V^T operand of PV step q (tokens 16q .. 16q+15), dv block db, by two
+  // transposed 8-byte LDS reads.  They are issued as inline asm: with the
+  // built-in, the compiler puts a wait for every global->LDS load in flight
+  // in front of them (it cannot tell that they read another stage).  Their
+  // data is waited for explicitly (tr_wait) before the MFMAs use it; the stage
+  // itself is guarded by the stage-top wait and barrier like every other read.
   auto rd_v = [&](const unsigned char* sb, int q, int db) -> bf16x8 {
     const int cq = 4 * (db & 1) + cch;
     bf16x4 v[2];
@@ -320,8 +339,8 @@ __global__ __launch_bounds__(NT, 2) void prefill_attn_kernel(AttnArgs a) {
     for (int ins = 0; ins < 2; ++ins) {
       const int t = 16 * q + 8 * ins + tr_tok;
       const unsigned char* p = sb + (3 + (db >> 1)) * CG + t * 128 + ((cq ^ (ins ? sw_tr1 : sw_tr0)) << 4) + half8;
-      v[ins] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (lds_bf16x4*)((__attribute__((address_space(3))) unsigned char*)p));
+      const uint32_t addr = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const unsigned char*)p);
+      asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v[ins]) : "v"(addr));
     }
     return __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
   };
@@ -330,32 +349,38 @@ __global__ __launch_bounds__(NT, 2) void prefill_attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
-  const int lim = pos - 4 * h;   // score i is token 8(i/4) + 4h + i%4 of the stage: visible while <= pos
+  // score i of block k is token 32k + 8(i/4) + 4h + i%4 of the stage: visible while <= pos
+  const int lim = pos - 4 * h;
 
-  issue(0);
-  if (nst > 1) issue(1);
+  if (nst > 0) issue(0);
   for (int s = 0; s < nst; ++s) {
-    if (s + 1 < nst) __builtin_amdgcn_s_waitcnt(0x0F75);   // vmcnt(5): stage s+1 may still fly
-    else __builtin_amdgcn_s_waitcnt(0x0F70);
+    // this wave's loads of stage s are in (nothing else is in flight); the
+    // barrier makes every wave's visible and ends every read of stage s-1,
+    // whose slot stage s+1 reuses
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     lds_sync();
-    if (s + 2 < nst) issue(s + 2);
+    if (s + 1 < nst) issue(s + 1);
     const unsigned char* sb = sm.stage[s % ANST];
-    f32x16 st = f32x16{};
+    f32x16 st[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int ks = 0; ks < QK_STEPS; ++ks)
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read16(sb + (ks >> 2) * CG + qk_off[ks & 3]), qreg[ks], st,
-                                                   0, 0, 0);
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        st[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read16(sb + (ks >> 2) * CG + 4096 * k + qk_off[ks & 3]),
+                                                        qreg[ks], st[k], 0, 0, 0);
     // online softmax of this stage (log2 units; the scale is folded into the
     // exponent's fma, and the row maximum of the raw scores scaled once)
     const int tok0 = s * T;
     const bool masked = tok0 + T - 1 > pos_min;   // some row of this wave may not see all the stage's tokens
     float mt = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int rel = 8 * (i >> 2) + (i & 3);
-      if (masked) st[i] = tok0 + rel <= lim ? st[i] : -INFINITY;
-      mt = fmaxf(mt, st[i]);
-    }
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rel = 32 * k + 8 * (i >> 2) + (i & 3);
+        if (masked) st[k][i] = tok0 + rel <= lim ? st[k][i] : -INFINITY;
+        mt = fmaxf(mt, st[k][i]);
+      }
     {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
       mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.scale_log2;
@@ -366,24 +391,33 @@ __global__ __launch_bounds__(NT, 2) void prefill_attn_kernel(AttnArgs a) {
     const float neg = m_new == -INFINITY ? 0.f : -m_new;
     m_run = m_new;
     float psum = 0.f;
-    bf16x8 pb[2];
+    bf16x8 pb[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(st[i], a.scale_log2, neg));
-      psum += p;
-      pb[i >> 3][i & 7] = (__bf16)p;
-    }
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(st[k][i], a.scale_log2, neg));
+        psum += p;
+        pb[2 * k + (i >> 3)][i & 7] = (__bf16)p;
+      }
     l_run = l_run * alpha + psum;
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) o[db] *= alpha;
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int q = 0; q < 4; ++q) {
+      bf16x8 va[4];
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_v(sb, q, db), pb[q], o[db], 0, 0, 0);
+      for (int db = 0; db < 4; ++db) va[db] = rd_v(sb, q, db);
+      // tr_wait: the reads above are complete; the MFMAs take their results
+      // through this statement, so they cannot be scheduled ahead of it
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(va[0]), "+v"(va[1]), "+v"(va[2]), "+v"(va[3]));
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], pb[q], o[db], 0, 0, 0);
+    }
   }
+  static_assert(A_LOADS == 10, "one stage = 10 loads per wave");
   // ---- results: o[db][i] = O[row l32][dv 32 db + 8 (i/4) + 4 h + i%4]
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (jr < a.n_q) {
