@@ -60,19 +60,22 @@ __global__ __launch_bounds__(NT) void prefill_weights_kernel(const uint16_t* __r
 // ------------------------------------------------------- reconstruction
 // kv[z][m][n] = sum_c A[z][m][c] w_kv[n][c] with A the cached latents of
 // sequence z (rows m < M of the cache, the first d_c elements of each row) and
-// n = i * 256 + d over all heads.  Workgroup tile 128 (m) x 256 (n); wave w
-// takes m rows 64(w%2) .. +64 and n rows 128(w/2) .. +128 (2 x 4 blocks of
-// 32 x 32).  The weight rows are the MFMA's first operand, so a lane's
-// results are 4 consecutive n of one m (one 8-byte store each).  The k range
-// is streamed in chunks of 32 through a 3-stage LDS ring (72 KiB, so two
-// workgroups share a CU): row r of a stage holds 4 chunks of 16 bytes, chunk
-// c at slot c ^ ((r / 4) % 4), which spreads 16 consecutive rows read at one
-// chunk over all 64 banks; a wave's 16-byte global->LDS load writes 16 rows x
-// 64 bytes.
-constexpr int GM = 128, GN = 256, GK = 32, GSTAGES = 3;
+// n = i * 256 + d over all heads.  Workgroup tile 128 (m) x 256 (n), 4 waves;
+// wave w takes m rows 64(w%2) .. +64 and n rows 128(w/2) .. +128 (2 x 4
+// blocks of 32 x 32).  The weight rows are the MFMA's first operand.  The k
+// range is streamed in chunks of 32 through a 3-stage LDS ring (72 KiB, so two
+// workgroups share a CU and one's barrier waits are covered by the other's
+// MFMAs): row r of a stage holds 4 chunks of 16 bytes, chunk c at slot
+// c ^ ((r / 4) % 4), which spreads 16 consecutive rows read at one chunk over
+// all 64 banks; a wave's 16-byte global->LDS load writes 16 rows x 64 bytes.
+// (A 256 x 256 tile with 8 waves, one workgroup per CU, needs a third fewer
+// L2 reads but measured slower.)
+constexpr int GM = 128, GN = 256, GK = 32, GSTAGES = 3, GWAVES = (GM / 64) * (GN / 128), GNT = 64 * GWAVES;
+constexpr int GWG_PER_CU = 2;
+static_assert(GSTAGES == 3 || GSTAGES == 4, "the stage-top waits cover 3 or 4 stages");
 constexpr int GROW = GK * 2;                                    // LDS row: 64 bytes
 constexpr int GA_BYTES = GM * GROW, GB_BYTES = GN * GROW;       // 8 KiB, 16 KiB
-constexpr int G_LOADS = (GM + GN) / 16 / 4;                     // 1 KiB loads per wave per stage: 6
+constexpr int G_LOADS = (GM + GN) / 16 / GWAVES;                // 1 KiB loads per wave per stage: 6
 __device__ __forceinline__ int gswz(int r) { return (r >> 2) & 3; }
 
 struct GemmArgs {
@@ -82,20 +85,44 @@ struct GemmArgs {
   const uint16_t* w;        // w_kv [N][K]
   uint16_t* c;              // kv [Z][M][N]
   int M, N, K;
+  int mb, nb, tiles, tiles_per_xcd;   // tile grid: mb x nb per sequence, Z * mb * nb in all
 };
+
+// Tile order.  Workgroups are dealt to the 8 XCDs in turn, so XCD x gets
+// blockIdx x, x+8, ...; it is given the consecutive tiles x*T .. x*T+T-1 of
+// the order below, in which 8 consecutive m blocks sweep the n blocks together
+// (tile i of a group of 8 m blocks: m = first + i % 8, n = i / 8).  The tiles
+// an XCD runs at one time then share their A rows and weight rows in its L2.
+constexpr int G_GROUP_M = 8;
+__device__ __forceinline__ bool gemm_tile(const GemmArgs& g, int bid, int* z, int* mi, int* ni) {
+  const int t = (bid & 7) * g.tiles_per_xcd + (bid >> 3);
+  if (t >= g.tiles) return false;
+  const int per_z = g.mb * g.nb;
+  *z = t / per_z;
+  const int r = t - *z * per_z;
+  const int first = (r / (G_GROUP_M * g.nb)) * G_GROUP_M;
+  const int gsize = g.mb - first < G_GROUP_M ? g.mb - first : G_GROUP_M;
+  const int in = r - first * g.nb;
+  *mi = first + in % gsize;
+  *ni = in / gsize;
+  return true;
+}
 
 struct __attribute__((aligned(16))) GemmSmem {
   unsigned char a[GSTAGES][GA_BYTES];
   unsigned char b[GSTAGES][GB_BYTES];
 };
+static_assert(GWG_PER_CU * sizeof(GemmSmem) <= 160 * 1024, "LDS of one CU");
 
-__global__ __launch_bounds__(NT, 2) void reconstruct_gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(GNT, GWG_PER_CU) void reconstruct_gemm_kernel(GemmArgs g) {
   __shared__ GemmSmem sm;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, h = lane >> 5;
-  const int m0 = blockIdx.x * GM, n0 = blockIdx.y * GN;
-  const int64_t z = blockIdx.z;
+  int zi, mi, ni;
+  if (!gemm_tile(g, blockIdx.x, &zi, &mi, &ni)) return;
+  const int m0 = __builtin_amdgcn_readfirstlane(mi * GM), n0 = __builtin_amdgcn_readfirstlane(ni * GN);
+  const int64_t z = __builtin_amdgcn_readfirstlane(zi);
   // A rows past M read as zeros (buffer range); their results are not stored
   const unsigned char* abase = g.a + z * g.a_seq_bytes + (int64_t)m0 * g.a_row_bytes;
   const int a_rows = g.M - m0 < GM ? g.M - m0 : GM;
@@ -104,28 +131,28 @@ __global__ __launch_bounds__(NT, 2) void reconstruct_gemm_kernel(GemmArgs g) {
   const unsigned char* bbase = reinterpret_cast<const unsigned char*>(g.w + (int64_t)n0 * g.K);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(bbase), (short)0,
                                                                       GN * g.K * 2, kBufferWord3);
-  // this lane's rows in its loads: A row 16j + lane/4 (j = wave, wave+4), B likewise
+  // this lane's rows in its loads: A row 16j + lane/4 (j = wave, wave + GWAVES, ..), B likewise
   const int lr = lane >> 2, lp = lane & 3;
   const int nst = g.K / GK;
   auto issue = [&](int s) {
     const int slot = s % GSTAGES;
     const int kb = s * GROW;   // byte offset of the chunk within a row
 #pragma unroll
-    for (int q = 0; q < GM / 64; ++q) {   // 2 loads of A rows
-      const int j = wave + 4 * q;
+    for (int q = 0; q < GM / 16 / GWAVES; ++q) {   // loads of A rows
+      const int j = wave + GWAVES * q;
       const int r = 16 * j + lr;
       const int off = r * g.a_row_bytes + kb + ((lp ^ gswz(r)) << 4);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sm.a[slot] + 1024 * j), 16, off, 0, 0, 0);
     }
 #pragma unroll
-    for (int q = 0; q < GN / 64; ++q) {   // 4 loads of weight rows
-      const int j = wave + 4 * q;
+    for (int q = 0; q < GN / 16 / GWAVES; ++q) {   // loads of weight rows
+      const int j = wave + GWAVES * q;
       const int r = 16 * j + lr;
       const int off = r * g.K * 2 + kb + ((lp ^ gswz(r)) << 4);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sm.b[slot] + 1024 * j), 16, off, 0, 0, 0);
     }
   };
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % (GM / 64), wn = wave / (GM / 64);
   f32x16 acc[4][2];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
@@ -145,16 +172,18 @@ __global__ __launch_bounds__(NT, 2) void reconstruct_gemm_kernel(GemmArgs g) {
     aoff[mb] = r * GROW;
     asw[mb] = gswz(r);
   }
-  issue(0);
-  if (nst > 1) issue(1);
+  static_assert(G_LOADS * (GSTAGES - 2) < 16, "the wait count fits the low vmcnt field");
+  for (int s = 0; s < GSTAGES - 1 && s < nst; ++s) issue(s);
   for (int s = 0; s < nst; ++s) {
     // this wave's loads of stage s are in; the barrier (LDS only: the loads of
-    // stage s+1 stay in flight) makes every wave's visible and ends every read
-    // of the slot stage s+2 reuses
-    if (s + 1 < nst) __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6): stage s+1 may still fly
-    else __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0)
+    // the next stages stay in flight) makes every wave's visible and ends every
+    // read of the slot stage s + GSTAGES - 1 reuses
+    const int ahead = nst - 1 - s;
+    if (ahead >= GSTAGES - 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (G_LOADS * (GSTAGES - 2)));
+    else if (GSTAGES > 3 && ahead == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | G_LOADS);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     lds_sync();
-    if (s + 2 < nst) issue(s + 2);
+    if (s + GSTAGES - 1 < nst) issue(s + GSTAGES - 1);
     const unsigned char* sa = sm.a[s % GSTAGES];
     const unsigned char* sb = sm.b[s % GSTAGES];
 #pragma unroll
@@ -172,13 +201,18 @@ __global__ __launch_bounds__(NT, 2) void reconstruct_gemm_kernel(GemmArgs g) {
           acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bo[nb], ao[mb], acc[nb][mb], 0, 0, 0);
     }
   }
-  static_assert(G_LOADS == 6, "wait counts assume 6 loads per wave per stage");
-  // acc[nb][mb][i]: n = n0 + 128 wn + 32 nb + 8 (i/4) + 4 h + i%4, m = m0 + 64 wm + 32 mb + l32
+  // ---- results.  acc[nb][mb][i] is kv at m = m0 + 64 wm + 32 mb + l32,
+  // n = n0 + 128 wn + 32 nb + 8 (i/4) + 4 h + i%4.  Stored straight from the
+  // registers, a wave's store would touch 32 rows with 16 bytes each; instead
+  // each wave puts its 64 x 128 block in the ring's memory (16 KiB, row r at
+  // 256 r, 16-byte chunk c at c ^ (r % 16)) and writes it back 4 whole rows
+  // (4 x 256 contiguous bytes) per store.
+  static_assert(GWAVES * 64 * 256 <= (int)sizeof(GemmSmem), "the output blocks fit in the ring");
+  lds_sync();   // every wave is done with the ring
+  unsigned char* ob = reinterpret_cast<unsigned char*>(&sm) + 16384 * wave;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
-    const int m = m0 + 64 * wm + 32 * mb + l32;
-    if (m >= g.M) continue;
-    uint16_t* crow = g.c + (z * g.M + m) * (int64_t)g.N + n0 + 128 * wn + 4 * h;
+    const int r = 32 * mb + l32;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
@@ -186,8 +220,19 @@ __global__ __launch_bounds__(NT, 2) void reconstruct_gemm_kernel(GemmArgs g) {
         u16x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = f32_to_bf16(acc[nb][mb][4 * q + e]);
-        *reinterpret_cast<u16x4*>(crow + 32 * nb + 8 * q) = v;
+        *reinterpret_cast<u16x4*>(ob + 256 * r + (((4 * nb + q) ^ (r & 15)) << 4) + 8 * h) = v;
       }
+  }
+  // this wave's block is in (only this wave reads it back; the clobber keeps
+  // the reads below the writes)
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const int rr = lane >> 4, cc = lane & 15;
+  uint16_t* cbase = g.c + (z * g.M + m0 + 64 * wm) * (int64_t)g.N + n0 + 128 * wn + 8 * cc;
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const int r = 4 * it + rr;
+    const u16x8 v = *reinterpret_cast<const u16x8*>(ob + 256 * r + ((cc ^ (r & 15)) << 4));
+    if (m0 + 64 * wm + r < g.M) *reinterpret_cast<u16x8*>(cbase + (int64_t)r * g.N) = v;
   }
 }
 
@@ -454,7 +499,12 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   g.M = p.max_ctx;
   g.N = p.n_h * KVW;
   g.K = p.d_c;
-  hipLaunchKernelGGL(reconstruct_gemm_kernel, dim3((g.M + GM - 1) / GM, g.N / GN, p.B), dim3(NT), 0, stream, g);
+  g.mb = (g.M + GM - 1) / GM;
+  g.nb = g.N / GN;
+  g.tiles = g.mb * g.nb * p.B;
+  g.tiles_per_xcd = (g.tiles + 7) / 8;
+  if (g.tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL(reconstruct_gemm_kernel, dim3(g.tiles_per_xcd * 8), dim3(GNT), 0, stream, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // 2. attention
