@@ -255,7 +255,8 @@ __global__ __launch_bounds__(GNT, GWG_PER_CU) void reconstruct_gemm_kernel(GemmA
 constexpr int T = 64;
 constexpr int CG = T * 128;                // bytes of one chunk group (8 KiB)
 constexpr int ASTAGE = 5 * CG;             // 40 KiB
-constexpr int ANST = 2;
+constexpr int ANST = 2;                    // ring slots: ANST - 1 stages in flight ahead of use
+constexpr int AWG_PER_CU = 2;
 constexpr int QK_STEPS = (DN + DR) / 16;   // 12
 constexpr int A_LOADS = 10;                // 1 KiB global->LDS loads per wave per stage
 
@@ -277,9 +278,45 @@ struct AttnArgs {
 struct __attribute__((aligned(16))) AttnSmem {
   unsigned char stage[ANST][ASTAGE];
 };
-static_assert(2 * sizeof(AttnSmem) <= 160 * 1024, "two workgroups per CU");
+static_assert(AWG_PER_CU * sizeof(AttnSmem) <= 160 * 1024, "LDS of one CU");
+static_assert(ANST == 2 || ANST == 3, "the stage-top wait covers 2 or 3 slots");
 
-__global__ __launch_bounds__(NT, 2) void prefill_attn_kernel(AttnArgs a) {
+// Transposed 8-byte LDS read (4 bf16 of 4 consecutive rows, see the PV
+// operand below) at addr + OFF.  Issued as inline asm: with the built-in, the
+// compiler puts a wait for every global->LDS load in flight in front of it
+// (it cannot tell that those write another stage).  The constant part of the
+// address goes in the offset field, so each read costs no address arithmetic.
+template <int OFF>
+__device__ __forceinline__ bf16x4 lds_read_tr(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "DS offset field");
+  bf16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+// Byte offset, from a stage's start plus a lane's part, of the V^T read half
+// `ins` of PV step q (tokens 16q .. 16q+15) and dv block db (chunk group 3 or 4).
+constexpr int pv_off(int q, int db, int ins) { return (3 + (db >> 1)) * CG + (16 * q + 8 * ins) * 128; }
+__device__ __forceinline__ bf16x8 cat4(bf16x4 x, bf16x4 y) {
+  return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// O^T[dv][row] += V^T[dv][16 tokens of step Q] . P^T: the 4 dv blocks' V^T
+// operands (va[2 (db%2) + half] = the lane's read addresses), one explicit
+// wait for them (the MFMAs take the results through it, so they cannot move
+// ahead of it; the stage itself is guarded by the stage-top wait and barrier),
+// then the 4 MFMAs.
+template <int Q>
+__device__ __forceinline__ void pv_step(f32x16 (&o)[4], const bf16x8& p, const uint32_t (&va)[4]) {
+  bf16x8 v[4];
+  v[0] = cat4(lds_read_tr<pv_off(Q, 0, 0)>(va[0]), lds_read_tr<pv_off(Q, 0, 1)>(va[1]));
+  v[1] = cat4(lds_read_tr<pv_off(Q, 1, 0)>(va[2]), lds_read_tr<pv_off(Q, 1, 1)>(va[3]));
+  v[2] = cat4(lds_read_tr<pv_off(Q, 2, 0)>(va[0]), lds_read_tr<pv_off(Q, 2, 1)>(va[1]));
+  v[3] = cat4(lds_read_tr<pv_off(Q, 3, 0)>(va[2]), lds_read_tr<pv_off(Q, 3, 1)>(va[3]));
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[db], p, o[db], 0, 0, 0);
+}
+
+__global__ __launch_bounds__(NT, AWG_PER_CU) void prefill_attn_kernel(AttnArgs a) {
   __shared__ AttnSmem sm;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -371,24 +408,15 @@ __global__ __launch_bounds__(NT, 2) void prefill_attn_kernel(AttnArgs a) {
   const int sw_tr0 = swz(tr_tok), sw_tr1 = swz(8 + tr_tok);
   const int half8 = (l16 & 1) * 8;
   const int cch = 2 * (g4 & 1) + ((l16 & 3) >> 1);
-  // V^T operand of PV step q (tokens 16q .. 16q+15), dv block db, by two
-  // transposed 8-byte LDS reads.  They are issued as inline asm: with the
-  // built-in, the compiler puts a wait for every global->LDS load in flight
-  // in front of them (it cannot tell that they read another stage).  Their
-  // data is waited for explicitly (tr_wait) before the MFMAs use it; the stage
-  // itself is guarded by the stage-top wait and barrier like every other read.
-  auto rd_v = [&](const unsigned char* sb, int q, int db) -> bf16x8 {
-    const int cq = 4 * (db & 1) + cch;
-    bf16x4 v[2];
+  // Per-lane parts of the addresses of the transposed V reads, one per
+  // (dv block parity, read half); the rest of each address is a constant that
+  // goes in the instruction's offset field (see pv_step).
+  uint32_t v_lane[4];
 #pragma unroll
-    for (int ins = 0; ins < 2; ++ins) {
-      const int t = 16 * q + 8 * ins + tr_tok;
-      const unsigned char* p = sb + (3 + (db >> 1)) * CG + t * 128 + ((cq ^ (ins ? sw_tr1 : sw_tr0)) << 4) + half8;
-      const uint32_t addr = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const unsigned char*)p);
-      asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v[ins]) : "v"(addr));
-    }
-    return __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
-  };
+  for (int d1 = 0; d1 < 2; ++d1)
+#pragma unroll
+    for (int ins = 0; ins < 2; ++ins)
+      v_lane[2 * d1 + ins] = tr_tok * 128 + (((4 * d1 + cch) ^ (ins ? sw_tr1 : sw_tr0)) << 4) + half8;
 
   f32x16 o[4];
 #pragma unroll
@@ -397,14 +425,18 @@ __global__ __launch_bounds__(NT, 2) void prefill_attn_kernel(AttnArgs a) {
   // score i of block k is token 32k + 8(i/4) + 4h + i%4 of the stage: visible while <= pos
   const int lim = pos - 4 * h;
 
-  if (nst > 0) issue(0);
-  for (int s = 0; s < nst; ++s) {
-    // this wave's loads of stage s are in (nothing else is in flight); the
+  // One stage: S^T, online softmax (log2 units; the scale is folded into the
+  // exponent's fma, the row maximum of the raw scores scaled once), PV.
+  // MASKED: some row of this wave may not see every token of the stage.
+  auto stage = [&](int s, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    // this wave's loads of stage s are in (those of stage s+1 may fly); the
     // barrier makes every wave's visible and ends every read of stage s-1,
-    // whose slot stage s+1 reuses
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    // whose slot stage s + ANST - 1 reuses
+    if (ANST == 3 && s + 1 < nst) __builtin_amdgcn_s_waitcnt(0x0F70 | A_LOADS);   // vmcnt(10)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                                       // vmcnt(0)
     lds_sync();
-    if (s + 1 < nst) issue(s + 1);
+    if (s + ANST - 1 < nst) issue(s + ANST - 1);
     const unsigned char* sb = sm.stage[s % ANST];
     f32x16 st[2] = {f32x16{}, f32x16{}};
 #pragma unroll
@@ -413,17 +445,15 @@ __global__ __launch_bounds__(NT, 2) void prefill_attn_kernel(AttnArgs a) {
       for (int k = 0; k < 2; ++k)
         st[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read16(sb + (ks >> 2) * CG + 4096 * k + qk_off[ks & 3]),
                                                         qreg[ks], st[k], 0, 0, 0);
-    // online softmax of this stage (log2 units; the scale is folded into the
-    // exponent's fma, and the row maximum of the raw scores scaled once)
-    const int tok0 = s * T;
-    const bool masked = tok0 + T - 1 > pos_min;   // some row of this wave may not see all the stage's tokens
     float mt = -INFINITY;
 #pragma unroll
     for (int k = 0; k < 2; ++k)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int rel = 32 * k + 8 * (i >> 2) + (i & 3);
-        if (masked) st[k][i] = tok0 + rel <= lim ? st[k][i] : -INFINITY;
+        if constexpr (MASKED) {
+          const int rel = 32 * k + 8 * (i >> 2) + (i & 3);
+          st[k][i] = s * T + rel <= lim ? st[k][i] : -INFINITY;
+        }
         mt = fmaxf(mt, st[k][i]);
       }
     {
@@ -431,9 +461,10 @@ __global__ __launch_bounds__(NT, 2) void prefill_attn_kernel(AttnArgs a) {
       mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.scale_log2;
     }
     const float m_new = fmaxf(m_run, mt);
-    // rows with nothing visible yet keep m = -inf, weights 0 and alpha 1
-    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    const float neg = m_new == -INFINITY ? 0.f : -m_new;
+    // masked stages: rows with nothing visible yet keep m = -inf, weights 0
+    // and alpha 1 (in a whole stage every score is finite)
+    const float alpha = MASKED && m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    const float neg = MASKED && m_new == -INFINITY ? 0.f : -m_new;
     m_run = m_new;
     float psum = 0.f;
     bf16x8 pb[4];
@@ -450,18 +481,22 @@ __global__ __launch_bounds__(NT, 2) void prefill_attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) o[db] *= alpha;
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      bf16x8 va[4];
-#pragma unroll
-      for (int db = 0; db < 4; ++db) va[db] = rd_v(sb, q, db);
-      // tr_wait: the reads above are complete; the MFMAs take their results
-      // through this statement, so they cannot be scheduled ahead of it
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(va[0]), "+v"(va[1]), "+v"(va[2]), "+v"(va[3]));
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], pb[q], o[db], 0, 0, 0);
-    }
-  }
+    const uint32_t sbase = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const unsigned char*)sb);
+    const uint32_t va[4] = {sbase + v_lane[0], sbase + v_lane[1], sbase + v_lane[2], sbase + v_lane[3]};
+    pv_step<0>(o, pb[0], va);
+    pv_step<1>(o, pb[1], va);
+    pv_step<2>(o, pb[2], va);
+    pv_step<3>(o, pb[3], va);
+  };
+  using Whole = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
+  // stages 0 .. n_whole-1 end at or before every row's position (s*T + T-1 <= pos_min);
+  // every wave runs all nst stages, so the barriers inside stay matched
+  const int n_whole = min(nst, max(pos_min + 1, 0) / T);
+  for (int s = 0; s < ANST - 1 && s < nst; ++s) issue(s);
+  int s = 0;
+  for (; s < n_whole; ++s) stage(s, Whole{});
+  for (; s < nst; ++s) stage(s, Masked{});
   static_assert(A_LOADS == 10, "one stage = 10 loads per wave");
   // ---- results: o[db][i] = O[row l32][dv 32 db + 8 (i/4) + 4 h + i%4]
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
