@@ -258,6 +258,7 @@ constexpr int ASTAGE = 5 * CG;             // 40 KiB
 constexpr int ANST = 2;                    // ring slots: ANST - 1 stages in flight ahead of use
 constexpr int AWG_PER_CU = 2;
 constexpr int QK_STEPS = (DN + DR) / 16;   // 12
+constexpr float A_HEADROOM = 32.f;         // log2 units a weight's exponent may exceed 0
 constexpr int A_LOADS = 10;                // 1 KiB global->LDS loads per wave per stage
 
 struct AttnArgs {
@@ -460,10 +461,16 @@ __global__ __launch_bounds__(NT, AWG_PER_CU) void prefill_attn_kernel(AttnArgs a
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
       mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.scale_log2;
     }
-    const float m_new = fmaxf(m_run, mt);
-    // masked stages: rows with nothing visible yet keep m = -inf, weights 0
-    // and alpha 1 (in a whole stage every score is finite)
-    const float alpha = MASKED && m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    // The row's reference m_run moves only when the stage maximum passes it by
+    // more than A_HEADROOM (and at the row's first visible stage, m_run =
+    // -inf): weights are then at most 2^A_HEADROOM, and the accumulator is
+    // rescaled rarely instead of at every new maximum.  Weights and their sum
+    // share the reference, so the normalised result does not depend on it.
+    // Masked stages: rows with nothing visible yet keep m = -inf, weights 0
+    // and alpha 1 (in a whole stage every score is finite).
+    const bool grow = mt > m_run + A_HEADROOM;
+    const float m_new = grow ? mt : m_run;
+    const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
     const float neg = MASKED && m_new == -INFINITY ? 0.f : -m_new;
     m_run = m_new;
     float psum = 0.f;
@@ -477,7 +484,7 @@ __global__ __launch_bounds__(NT, AWG_PER_CU) void prefill_attn_kernel(AttnArgs a
         pb[2 * k + (i >> 3)][i & 7] = (__bf16)p;
       }
     l_run = l_run * alpha + psum;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) o[db] *= alpha;
     }
