@@ -259,6 +259,7 @@ constexpr int ANST = 2;                    // ring slots: ANST - 1 stages in fli
 constexpr int AWG_PER_CU = 2;
 constexpr int QK_STEPS = (DN + DR) / 16;   // 12
 constexpr float A_HEADROOM = 32.f;         // log2 units a weight's exponent may exceed 0
+constexpr int QPF = 2;                     // QK k-steps of K operands read ahead
 constexpr int A_LOADS = 10;                // 1 KiB global->LDS loads per wave per stage
 
 struct AttnArgs {
@@ -300,21 +301,38 @@ constexpr int pv_off(int q, int db, int ins) { return (3 + (db >> 1)) * CG + (16
 __device__ __forceinline__ bf16x8 cat4(bf16x4 x, bf16x4 y) {
   return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
 }
-// O^T[dv][row] += V^T[dv][16 tokens of step Q] . P^T: the 4 dv blocks' V^T
-// operands (va[2 (db%2) + half] = the lane's read addresses), one explicit
-// wait for them (the MFMAs take the results through it, so they cannot move
-// ahead of it; the stage itself is guarded by the stage-top wait and barrier),
-// then the 4 MFMAs.
+// V^T operands of PV step Q (tokens 16Q .. 16Q+15) for the 4 dv blocks
+// (va[2 (db%2) + half] = the lane's read addresses); their data is waited for
+// by pv_mfmas.
 template <int Q>
-__device__ __forceinline__ void pv_step(f32x16 (&o)[4], const bf16x8& p, const uint32_t (&va)[4]) {
-  bf16x8 v[4];
+__device__ __forceinline__ void pv_reads(bf16x8 (&v)[4], const uint32_t (&va)[4]) {
   v[0] = cat4(lds_read_tr<pv_off(Q, 0, 0)>(va[0]), lds_read_tr<pv_off(Q, 0, 1)>(va[1]));
   v[1] = cat4(lds_read_tr<pv_off(Q, 1, 0)>(va[2]), lds_read_tr<pv_off(Q, 1, 1)>(va[3]));
   v[2] = cat4(lds_read_tr<pv_off(Q, 2, 0)>(va[0]), lds_read_tr<pv_off(Q, 2, 1)>(va[1]));
   v[3] = cat4(lds_read_tr<pv_off(Q, 3, 0)>(va[2]), lds_read_tr<pv_off(Q, 3, 1)>(va[3]));
+}
+// Waits for every LDS read in flight (the operands v among them: the MFMAs
+// take them through this statement, so they cannot move ahead of it).
+__device__ __forceinline__ void lds_wait_operands(bf16x8 (&v)[4]) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
+}
+// O^T[dv][row] += V^T[dv][16 tokens] . P^T for the 4 dv blocks.
+__device__ __forceinline__ void pv_mfmas(f32x16 (&o)[4], const bf16x8 (&v)[4], const bf16x8& p) {
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[db], p, o[db], 0, 0, 0);
+}
+// PV of one stage: the reads of step Q+1 go out before the MFMAs of step Q,
+// so their latency runs under those MFMAs (the reads of step 0 were issued by
+// the caller, before the softmax).
+template <int Q>
+__device__ __forceinline__ void pv_pipeline(f32x16 (&o)[4], bf16x8 (&v)[2][4], const bf16x8 (&p)[4],
+                                            const uint32_t (&va)[4]) {
+  lds_wait_operands(v[Q % 2]);
+  if constexpr (Q + 1 < 4) pv_reads<Q + 1>(v[(Q + 1) % 2], va);
+  __builtin_amdgcn_sched_barrier(0);
+  pv_mfmas(o, v[Q % 2], p[Q]);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (Q + 1 < 4) pv_pipeline<Q + 1>(o, v, p, va);
 }
 
 __global__ __launch_bounds__(NT, AWG_PER_CU) void prefill_attn_kernel(AttnArgs a) {
@@ -439,13 +457,32 @@ __global__ __launch_bounds__(NT, AWG_PER_CU) void prefill_attn_kernel(AttnArgs a
     lds_sync();
     if (s + ANST - 1 < nst) issue(s + ANST - 1);
     const unsigned char* sb = sm.stage[s % ANST];
+    // S^T: K operands read QPF k-steps ahead of their MFMAs (the fences keep
+    // that order; the compiler's waits then cover only the oldest reads)
     f32x16 st[2] = {f32x16{}, f32x16{}};
+    auto rd_k = [&](int ks, int k) { return lds_read16(sb + (ks >> 2) * CG + 4096 * k + qk_off[ks & 3]); };
+    bf16x8 kr[QPF][2];
 #pragma unroll
-    for (int ks = 0; ks < QK_STEPS; ++ks)
+    for (int ks = 0; ks < QPF; ++ks) {
+      kr[ks][0] = rd_k(ks, 0);
+      kr[ks][1] = rd_k(ks, 1);
+    }
 #pragma unroll
-      for (int k = 0; k < 2; ++k)
-        st[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read16(sb + (ks >> 2) * CG + 4096 * k + qk_off[ks & 3]),
-                                                        qreg[ks], st[k], 0, 0, 0);
+    for (int ks = 0; ks < QK_STEPS; ++ks) {
+      const bf16x8 a0 = kr[ks % QPF][0], a1 = kr[ks % QPF][1];
+      if (ks + QPF < QK_STEPS) {
+        kr[ks % QPF][0] = rd_k(ks + QPF, 0);
+        kr[ks % QPF][1] = rd_k(ks + QPF, 1);
+      }
+      st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], st[0], 0, 0, 0);
+      st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], st[1], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the V^T operands of PV step 0 go out now, under the softmax
+    const uint32_t sbase = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const unsigned char*)sb);
+    const uint32_t va[4] = {sbase + v_lane[0], sbase + v_lane[1], sbase + v_lane[2], sbase + v_lane[3]};
+    bf16x8 vv[2][4];
+    pv_reads<0>(vv[0], va);
     float mt = -INFINITY;
 #pragma unroll
     for (int k = 0; k < 2; ++k)
@@ -488,12 +525,7 @@ __global__ __launch_bounds__(NT, AWG_PER_CU) void prefill_attn_kernel(AttnArgs a
 #pragma unroll
       for (int db = 0; db < 4; ++db) o[db] *= alpha;
     }
-    const uint32_t sbase = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const unsigned char*)sb);
-    const uint32_t va[4] = {sbase + v_lane[0], sbase + v_lane[1], sbase + v_lane[2], sbase + v_lane[3]};
-    pv_step<0>(o, pb[0], va);
-    pv_step<1>(o, pb[1], va);
-    pv_step<2>(o, pb[2], va);
-    pv_step<3>(o, pb[3], va);
+    pv_pipeline<0>(o, vv, pb, va);
   };
   using Whole = std::integral_constant<bool, false>;
   using Masked = std::integral_constant<bool, true>;
