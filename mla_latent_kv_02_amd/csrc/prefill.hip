@@ -239,8 +239,8 @@ __global__ __launch_bounds__(GNT, GWG_PER_CU) void reconstruct_gemm_kernel(GemmA
 // ------------------------------------------------------------- attention
 // One workgroup = 128 query rows (query tokens) of one head of one sequence;
 // wave w owns rows 32w .. 32w+31 for the whole computation (no exchange of
-// weights between waves).  The cached tokens stream through a 2-stage LDS
-// ring of T = 64 tokens; a stage holds 5 chunk groups of 64 rows x 8 chunks
+// weights between waves).  The cached tokens stream through a 2-slot LDS
+// ring of T = 64-token stages; a stage holds 5 chunk groups of 64 rows x 8 chunks
 // (16 bytes): the key content part (2 groups, from kv), the positional key
 // (1 group, from the cache row) and the value (2 groups, from kv).  Per stage:
 //   S^T[tok][row] = K[tok][0:192] . [q_nope | q_pe]^T   (2 blocks of 32 tokens,
@@ -252,6 +252,9 @@ __global__ __launch_bounds__(GNT, GWG_PER_CU) void reconstruct_gemm_kernel(GemmA
 // 16q + 8(e/4) + 4(l/32) + e%4, the order of the S^T layout), and V^T is read
 // in the same token order by transposed LDS reads.  Two workgroups share a
 // CU (80 KiB of LDS each), so one's softmax runs under the other's MFMAs.
+// Stages that every row of a wave sees whole take a loop without masking.
+// (Measured: one workgroup per CU with a 3-slot ring, and 32-token stages
+// with S^T(s+1) interleaved with the softmax of stage s, were both slower.)
 constexpr int T = 64;
 constexpr int CG = T * 128;                // bytes of one chunk group (8 KiB)
 constexpr int ASTAGE = 5 * CG;             // 40 KiB
@@ -417,7 +420,8 @@ __global__ __launch_bounds__(NT, AWG_PER_CU) void prefill_attn_kernel(AttnArgs a
     }
   };
 
-  // LDS offsets of this lane's operands (token l32 of block 0; block 1 is 32 rows on, same swizzle)
+  // LDS offsets of this lane's S^T operands: token l32 of block 0; block 1 is
+  // 32 rows on, with the same swizzle (s(t) has period 16)
   const int sw_qk = swz(l32);
   int qk_off[4];
 #pragma unroll
@@ -429,7 +433,7 @@ __global__ __launch_bounds__(NT, AWG_PER_CU) void prefill_attn_kernel(AttnArgs a
   const int cch = 2 * (g4 & 1) + ((l16 & 3) >> 1);
   // Per-lane parts of the addresses of the transposed V reads, one per
   // (dv block parity, read half); the rest of each address is a constant that
-  // goes in the instruction's offset field (see pv_step).
+  // goes in the instruction's offset field (see pv_reads).
   uint32_t v_lane[4];
 #pragma unroll
   for (int d1 = 0; d1 < 2; ++d1)
