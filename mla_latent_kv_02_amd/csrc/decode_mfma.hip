@@ -858,19 +858,46 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
         reinterpret_cast<float2*>(a.lse_part)[(int64_t)slot * rows + r] = rl;
       }
     }
-    // o[mb][hb][i] = u[row grow0 + 32 hb + l32][latent 128 wave + 32 mb + 8 (i/4) + 4 h + i%4]
+    // o[mb][hb][i] = u[row grow0 + 32 hb + l32][latent 128 wave + 32 mb + 8 (i/4) + 4 h + i%4].
+    // Stored straight from the registers, an instruction would touch 32 rows
+    // with 32 bytes each (one L2 request per run).  Instead, per head block hb,
+    // each wave puts its 32 rows x 128 latents (16 KiB: row r at 512 r,
+    // 16-byte chunk c at c ^ r) in the ring's memory and stores them back as
+    // 2 rows of 512 contiguous bytes per instruction.
+    lds_barrier();   // every wave is done with the ring
+    // (lane offsets from an opaque copy of the lane index: the compiler cannot
+    // hoist them out of the segment, where they would stay live through the
+    // stage loop)
+    int lane_o;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(lane_o) : "v"(lane));
+    const int ol32 = lane_o & 31, oh = (lane_o >> 5) & 1;
+    unsigned char* ob = &sm->stage[0][0] + 16384 * wave;
+    static_assert(4 * 16384 <= (int)sizeof(sm->stage), "the staging blocks fit in the stage memory");
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
-      const int r = grow0 + 32 * hb + l32;
-      if (r < rows) {
-        float* up = a.u_part + ((int64_t)slot * rows + r) * DC + 128 * wave + 4 * h;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-          for (int i4 = 0; i4 < 4; ++i4)
-            *reinterpret_cast<f32x4*>(up + 32 * mb + 8 * i4) =
-                f32x4{o[mb][hb][4 * i4], o[mb][hb][4 * i4 + 1], o[mb][hb][4 * i4 + 2], o[mb][hb][4 * i4 + 3]};
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int c = 8 * mb + 2 * i4 + oh;
+          *reinterpret_cast<f32x4*>(ob + 512 * ol32 + ((c ^ ol32) << 4)) =
+              f32x4{o[mb][hb][4 * i4], o[mb][hb][4 * i4 + 1], o[mb][hb][4 * i4 + 2], o[mb][hb][4 * i4 + 3]};
+          __builtin_amdgcn_sched_barrier(0);   // accumulator reads one block at a time
+        }
+      // this wave's block is in (only this wave reads it; the clobber keeps
+      // the reads below the writes and the next block's writes below the reads)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      // instruction it stores rows 2 it + oh of the block, 16 bytes per lane
+      float* const ub = a.u_part + ((int64_t)slot * rows + grow0 + 32 * hb) * DC + 128 * wave;
+      const int lo = oh * DC + 4 * ol32;
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int rr = 2 * it + oh;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(ob + 512 * rr + ((ol32 ^ rr) << 4));
+        if (grow0 + 32 * hb + rr < rows) *reinterpret_cast<f32x4*>(ub + 2 * DC * it + lo) = v;
+        __builtin_amdgcn_sched_barrier(0);
       }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
     // (the segment walker's barrier after this call keeps the ring and the
     // exchange buffers until every wave is done with them)
