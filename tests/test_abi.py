@@ -179,3 +179,49 @@ def test_fp8_cache_argument_checks(lib):
     # a valid fp8 cache with a bad split count is still rejected on the host
     st = lib.mla_decode(ctypes.byref(V3), 2, 1, FAKE, FAKE, ctypes.byref(c), FAKE, 0, FAKE, FAKE, None)
     assert st == bd.MLA_ERR_INVALID_ARG
+
+
+def test_prefill_argument_checks(lib):
+    """mla_prefill / mla_prefill_weights / mla_prefill_workspace_bytes reject
+    bad arguments on the host; shapes outside the compiled set (non-V3 head
+    dims, fp8 or paged caches, sizes past the 32-bit buffer offsets) are
+    MLA_ERR_UNSUPPORTED."""
+    d = ctypes.byref(V3)
+    small = ctypes.byref(bd._Dims(4, 64, 16, 32, 32, 0.0, 0.0))
+    ws_bytes = lib.mla_prefill_workspace_bytes(d, 2, 100)
+    assert ws_bytes == 2 * 100 * 128 * 256 * 2
+    assert lib.mla_prefill_workspace_bytes(d, -1, 100) == -1
+    assert lib.mla_prefill_workspace_bytes(None, 2, 100) == -1
+    c = _cache(seq_stride=576 * 100)
+    cr = ctypes.byref(c)
+
+    def call(dims=d, B=2, n_q=10, max_ctx=100, cache=cr, ws=FAKE, ws_bytes=ws_bytes, q_nope=FAKE, out=FAKE):
+        return lib.mla_prefill(dims, B, n_q, max_ctx, q_nope, FAKE, FAKE, cache, FAKE, ws, ws_bytes, FAKE, out,
+                               None, None)
+
+    assert call(B=0, q_nope=None, out=None, ws=None, ws_bytes=0) == 0
+    assert call(n_q=0) == bd.MLA_ERR_INVALID_ARG
+    assert call(B=-1) == bd.MLA_ERR_INVALID_ARG
+    assert call(max_ctx=5) == bd.MLA_ERR_INVALID_ARG                    # fewer cached rows than queries
+    assert call(q_nope=None) == bd.MLA_ERR_INVALID_ARG
+    assert call(out=None) == bd.MLA_ERR_INVALID_ARG
+    assert call(ws=None) == bd.MLA_ERR_INVALID_ARG
+    assert call(ws_bytes=ws_bytes - 1) == bd.MLA_ERR_INVALID_ARG         # workspace too small
+    assert call(ws=ctypes.c_void_p(0x10008)) == bd.MLA_ERR_INVALID_ARG   # not 16-byte aligned
+    assert call(cache=None) == bd.MLA_ERR_INVALID_ARG
+    short = _cache(seq_stride=576 * 99)                                   # max_ctx rows do not fit
+    assert call(cache=ctypes.byref(short)) == bd.MLA_ERR_INVALID_ARG
+    paged = _cache(block_size=64, block_table=0x30000, max_blocks=4)
+    assert call(cache=ctypes.byref(paged)) == bd.MLA_ERR_UNSUPPORTED
+    fp8 = _cache(dtype=bd.FP8_E4M3, seq_stride=656 * 100)
+    assert call(cache=ctypes.byref(fp8)) == bd.MLA_ERR_UNSUPPORTED
+    small_cache = _cache(seq_stride=80 * 100)
+    small_ws = lib.mla_prefill_workspace_bytes(small, 2, 100)
+    assert call(dims=small, cache=ctypes.byref(small_cache), ws_bytes=small_ws) == bd.MLA_ERR_UNSUPPORTED
+    # past the 32-bit buffer offsets of the workspace rows
+    big = 1 << 20
+    huge = _cache(seq_stride=576 * big)
+    assert call(max_ctx=big, cache=ctypes.byref(huge), ws_bytes=lib.mla_prefill_workspace_bytes(d, 2, big)) \
+        == bd.MLA_ERR_UNSUPPORTED
+    assert lib.mla_prefill_weights(d, None, FAKE, FAKE, None) == bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_prefill_weights(small, FAKE, FAKE, FAKE, None) == bd.MLA_ERR_UNSUPPORTED
