@@ -862,8 +862,9 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
     // Stored straight from the registers, an instruction would touch 32 rows
     // with 32 bytes each (one L2 request per run).  Instead, per head block hb,
     // each wave puts its 32 rows x 128 latents (16 KiB: row r at 512 r,
-    // 16-byte chunk c at c ^ r) in the ring's memory and stores them back as
-    // 2 rows of 512 contiguous bytes per instruction.
+    // 16-byte chunk c at c ^ r) in the stage memory (the ring; the two bf16
+    // stages over an fp8 cache) and stores them back as 2 rows of 512
+    // contiguous bytes per instruction.
     lds_barrier();   // every wave is done with the ring
     // (lane offsets from an opaque copy of the lane index: the compiler cannot
     // hoist them out of the segment, where they would stay live through the
