@@ -337,6 +337,49 @@ def session_bench(args):
 PREFILL_WORKLOADS = {"prompt4k": (1, 4096, 4096), "chunk1k": (4, 8192, 1024)}   # B, ctx, n_q
 
 
+def prefill_cpu_baseline(w, ctx, n_q, min_seconds=10.0, q_sample=256, head_group=16):
+    """The fp64 oracle on a bounded sample of a prefill workload: sequence 0,
+    its last ``q_sample`` query tokens (each sees ~ctx cached tokens, the
+    costliest rows), heads in groups of ``head_group`` until the oracle has run
+    for ``min_seconds``.  The oracle rebuilds K and V of the heads it runs
+    (ctx tokens) and attends; the sample's FLOPs follow the GPU line's
+    definition (reconstruction of those heads' ctx tokens + attention of the
+    sampled rows), so TFLOP/s is comparable.  Queries are seeded normal draws
+    (timing only)."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    rng = np.random.default_rng(73)
+    nq = min(q_sample, n_q)
+    q_nope = rng.standard_normal((nq, w.n_h, w.d_nope))
+    q_rope = rng.standard_normal((nq, w.n_h, w.d_rope))
+    pos = np.arange(ctx - nq, ctx)
+    wt = W.weights(w)
+    rows = W.cache_rows(w, 0, 0, ctx)
+    spent, heads_done, flops = 0.0, 0, 0.0
+    for h0 in range(0, w.n_h, head_group):
+        heads = list(range(h0, min(h0 + head_group, w.n_h)))
+        t0 = time.perf_counter()
+        oracle.decode_sequence(q_nope, q_rope, pos, rows["c_kv"], rows["k_rope_raw"], wt["w_uk"], wt["w_uv"],
+                               w.sm_scale, w.rope_base, heads=heads)
+        spent += time.perf_counter() - t0
+        heads_done += len(heads)
+        flops += len(heads) * (ctx * 2 * w.d_c * (w.d_nope + w.d_v)
+                               + int((pos + 1).sum()) * 2 * (w.d_nope + w.d_rope + w.d_v))
+        if spent >= min_seconds:
+            break
+    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"sequence 0 of {w.name} (ctx {ctx}), its last {nq} query tokens, {heads_done} of {w.n_h} "
+                      f"heads in groups of {head_group}; fp64 rebuild of those heads' K/V then causal attention; "
+                      f"FLOPs as in the GPU line",
+            "seconds": round(spent, 3)}
+
+
 def prefill_bench(args):
     """mla_prefill at V3 shapes: the cache holds ctx rows per sequence, the last
     n_q of them are queries (positions ctx - n_q .. ctx - 1).  Cache rows come
@@ -396,7 +439,8 @@ def prefill_bench(args):
         "roofline": {"kernel": "mla_prefill (reconstruct_gemm_kernel + prefill_attn_kernel)", "bound": "mfma",
                      "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_BF16_PEAK_TFS, 4), "traffic": None},
-        "cpu_baseline": None}), flush=True)
+        "cpu_baseline": None if args.no_cpu_baseline else prefill_cpu_baseline(w, ctx, n_q, args.cpu_seconds)}),
+        flush=True)
 
 
 def main():
