@@ -167,3 +167,31 @@ def test_late_large_score_prefill_and_decode():
         torch.cuda.synchronize()
         dec = step.out.float().cpu().numpy().astype(np.float64)
         _check(w, st, {"o": dec}, spikes=spikes, keys=("o",))
+
+
+@pytest.mark.parametrize("batch,ctx,n_q", [(1, 4096, 4096), (4, 8192, 1024)], ids=["prompt4k", "chunk1k"])
+def test_prefill_full_size_sampled(batch, ctx, n_q):
+    """The two benchmark shapes (a 4096-token prompt; 1024-token chunks after
+    7168 cached tokens, 4 sequences) through the same entry point the bench
+    times, checked against the oracle on sampled query rows (the first and last
+    of the chunk, both sides of a 128-row block boundary, the middle) and
+    heads; the oracle rebuilds K/V of those heads over the whole context."""
+    _need_gpu()
+    from workloads.device import stage
+    w = W.custom(name=f"pf_full_{ctx}_{n_q}", seed=81, batch=batch, n_q=n_q, ctx=ctx)
+    st = stage(w)
+    got = _prefill(st)
+    wt, q = W.weights(w), W.queries(w)
+    rows_q = sorted({0, 127, 128, n_q // 2, n_q - 1})
+    heads = [0, 77, 127]
+    for b in range(batch):
+        rows = W.cache_rows(w, b, 0, ctx)
+        ref = oracle.decode_sequence(q["q_nope"][b][rows_q], q["q_rope"][b][rows_q],
+                                     st["positions_host"][b][rows_q], rows["c_kv"], rows["k_rope_raw"],
+                                     wt["w_uk"], wt["w_uv"], w.sm_scale, w.rope_base, heads=heads)
+        o = got["o"][b][rows_q][:, heads]
+        lse = got["lse"][b][rows_q][:, heads]
+        errs = {"o": vec_rel_err(o, ref["o"]), "lse": scalar_err(lse, ref["lse"])}
+        print(f"  seq {b} ctx {ctx} rows {rows_q}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+        for k, v in errs.items():
+            assert v <= 1e-2, (b, k, v)
