@@ -2,7 +2,9 @@
 launch configuration bench.py times (default split count), on outputs the
 oracle computes one by one: sampled sequences (shortest and longest of the
 ragged batch included) and sampled heads of each, through both the separate
-merge + up-projection and the fused one.  Tolerance 1e-2 (bf16)."""
+merge + up-projection and the fused one.  The same over an fp8 cache for
+the contiguous and paged shapes (the oracle quantises the latents as the
+cache holds them).  Tolerance 1e-2 (bf16 operands)."""
 import numpy as np
 import pytest
 
@@ -19,13 +21,16 @@ CASES = {
 }
 
 
-@pytest.mark.parametrize("name", list(CASES))
-def test_full_size_sampled(name):
+@pytest.mark.parametrize("name,fp8", [(n, False) for n in CASES] + [("v3_b64", True), ("v3_paged", True)],
+                         ids=[n for n in CASES] + ["v3_b64-fp8", "v3_paged-fp8"])
+def test_full_size_sampled(name, fp8):
     _need_gpu()
     from mla_latent_kv_02_amd.plan import default_num_splits
     from mla_latent_kv_02_amd.step import DecodeStep
     from workloads.device import stage
     w = W.get(name)
+    if fp8:
+        w = W.with_fp8_cache(w)
     st = stage(w)
     ctx = st["ctx_host"]
     ns = default_num_splits(int(ctx.sum()), w.n_q, w.n_h)
@@ -44,5 +49,5 @@ def test_full_size_sampled(name):
     for k in ("o", "lse", "o_fused", "lse_fused"):
         assert np.isfinite(got[k]).all(), k
     seqs, heads = CASES[name]
-    print(f"{name}: num_splits={ns}, total tokens {int(ctx.sum())}", flush=True)
+    print(f"{w.name}: num_splits={ns}, total tokens {int(ctx.sum())}", flush=True)
     _check(w, st, got, seqs=seqs(ctx), heads=heads)
