@@ -1,6 +1,6 @@
 """Benchmark of one MLA decode step (weight absorption, latent cache) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3_b64]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3_paged]
 
 A step is the whole hot path over one batch: append the step's own latents to
 the cache and absorb the query through W_UK (+ query RoPE) in one launch
@@ -10,10 +10,16 @@ the partials, and the W_UV up-projection (the last two as one pass over the
 partials, mla_combine_out_proj, unless --separate-tail).  Inputs are seeded synthetic
 DeepSeek-V3-shaped tensors already resident in HBM when timing starts.
 
-Prints one JSON line: algorithmic GB/s of the step (value), decode tokens/s,
-the roofline of the dominant kernel (mla_decode) measured with HIP events on
-the launch stream, and the fp64 CPU oracle timed on a bounded sample of the
-same workload on the host cores.
+Timing: every timed rep (a step, or in a second pass a step with events
+around mla_decode) runs right after an untimed flush that reads and writes
+1 GiB, so no rep finds the cache, weights or queries in L2 or the 256 MB
+memory-side cache, and the GPU stays busy between reps (the clock cannot
+idle-recover).  Each rep has its own HIP event pair on the launch stream.
+
+Prints one JSON line: algorithmic GB/s of the step (value, from the mean
+step time), decode tokens/s, median and minimum step and kernel times, the
+roofline of the dominant kernel (mla_decode), and the fp64 CPU oracle timed
+on a bounded sample of the same workload on the host cores.
 """
 from __future__ import annotations
 
@@ -34,10 +40,19 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=40,
-                    help="untimed steps first; the clock settles within ~10 ms of load")
-    ap.add_argument("--workload", default="v3_b64")
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="untimed steps first (at least --warmup-seconds of them)")
+    ap.add_argument("--warmup-seconds", type=float, default=0.5,
+                    help="time floor of the warm-up: steps continue until both --warmup steps and this many "
+                         "seconds have run")
+    ap.add_argument("--kernel-reps", type=int, default=20,
+                    help="minimum number of mla_decode launches timed for the roofline (at least --steps)")
+    ap.add_argument("--flush-mib", type=int, default=1024,
+                    help="MiB read and written by the untimed flush before every timed rep (0 = no flush)")
+    ap.add_argument("--workload", default="v3_paged",
+                    help="v3_paged (default: the largest single-GPU workload, B=128 ragged contexts, paged), "
+                         "v3_b64, v3_split, v3_b1, tiny_fp32")
     ap.add_argument("--prefill", choices=("prompt4k", "chunk1k"), default=None,
                     help="time mla_prefill instead of the decode step: a 4096-token prompt (B=1), or 1024-token "
                          "chunks after 7168 cached tokens (B=4)")
@@ -88,6 +103,35 @@ def decode_flops(w, ctx, pos):
     return int(visible) * w.n_h * 2 * (2 * w.d_c + w.d_rope)
 
 
+def host_cpu():
+    """Threads the oracle uses and what they run on: the cores this process may
+    run on (sched_getaffinity), capped by OMP_NUM_THREADS when the host sets a
+    CPU share that way, and the model name from /proc/cpuinfo."""
+    affinity = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    threads = min(affinity, int(cap)) if cap.isdigit() and int(cap) > 0 else affinity
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return threads, affinity, model
+
+
+def blas_threads(n):
+    """Context manager that runs the BLAS / OpenMP pools with n threads."""
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=n)
+    except Exception:   # threadpoolctl missing: the pools keep their defaults
+        import contextlib
+        return contextlib.nullcontext()
+
+
 def cpu_baseline(w, min_seconds=10.0, head_group=16):
     """The fp64 oracle timed on a bounded sample of the same workload.
 
@@ -101,11 +145,15 @@ def cpu_baseline(w, min_seconds=10.0, head_group=16):
     import numpy as np
     import oracle
     import workloads as W
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        cores = 1
+    cores, affinity, model = host_cpu()
+    with blas_threads(cores):
+        return _cpu_baseline(w, min_seconds, head_group, cores, affinity, model)
+
+
+def _cpu_baseline(w, min_seconds, head_group, cores, affinity, model):
+    import numpy as np
+    import oracle
+    import workloads as W
     ctx = W.context_lengths(w)
     order = [int(np.argmin(ctx)), int(np.argmax(ctx))] + list(range(w.batch))
     order = list(dict.fromkeys(order))
@@ -136,6 +184,7 @@ def cpu_baseline(w, min_seconds=10.0, head_group=16):
         if spent >= min_seconds:
             break
     return {"value": round(sample_bytes / spent / 1e9, 6), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "affinity_cores": int(affinity), "cpu_model": model,
             "sample": f"sequences {', '.join(done)} of {w.name}, all {w.n_q} query token(s), heads in groups of "
                       f"{head_group}; {'fp8 quantise + dequantise, ' if fp8 else ''}fp64 reconstruct-then-attend; "
                       f"GB/s = attended cache bytes x heads done/"
@@ -187,6 +236,17 @@ def copy_probe(mib):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
     log(f"copy probe: 5 x {mib} MiB read + {mib} MiB written")
+
+
+def make_flush(mib):
+    """An untimed flush of the GPU caches: one elementwise kernel that reads and
+    writes ``mib`` MiB (4x the 256 MB memory-side cache for the default 1 GiB),
+    so a rep after it finds nothing of its inputs in L2 or that cache."""
+    import torch
+    if mib <= 0:
+        return lambda: None
+    buf = torch.zeros(mib * (1 << 20) // 4, dtype=torch.float32, device="cuda")
+    return lambda: buf.add_(1.0)
 
 
 def folds_bench(args):
@@ -346,14 +406,17 @@ def prefill_cpu_baseline(w, ctx, n_q, min_seconds=10.0, q_sample=256, head_group
     definition (reconstruction of those heads' ctx tokens + attention of the
     sampled rows), so TFLOP/s is comparable.  Queries are seeded normal draws
     (timing only)."""
+    cores, affinity, model = host_cpu()
+    with blas_threads(cores):
+        r = _prefill_cpu_baseline(w, ctx, n_q, min_seconds, q_sample, head_group)
+    r.update({"cores": int(cores), "affinity_cores": int(affinity), "cpu_model": model})
+    return r
+
+
+def _prefill_cpu_baseline(w, ctx, n_q, min_seconds, q_sample, head_group):
     import numpy as np
     import oracle
     import workloads as W
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        cores = 1
     rng = np.random.default_rng(73)
     nq = min(q_sample, n_q)
     q_nope = rng.standard_normal((nq, w.n_h, w.d_nope))
@@ -373,7 +436,7 @@ def prefill_cpu_baseline(w, ctx, n_q, min_seconds=10.0, q_sample=256, head_group
                                + int((pos + 1).sum()) * 2 * (w.d_nope + w.d_rope + w.d_v))
         if spent >= min_seconds:
             break
-    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "kind": "oracle",
             "sample": f"sequence 0 of {w.name} (ctx {ctx}), its last {nq} query tokens, {heads_done} of {w.n_h} "
                       f"heads in groups of {head_group}; fp64 rebuild of those heads' K/V then causal attention; "
                       f"FLOPs as in the GPU line",
@@ -521,12 +584,17 @@ def main():
             mla.mla_combine(d, st["cache"].ctx_lens, num_splits, step.u_part, step.lse_part, step.u, step.lse)
             mla.mla_out_proj(d, step.u, st["w_uv"], step.out)
 
-    log(f"num_splits={num_splits}; warmup {args.warmup} steps")
-    for _ in range(args.warmup):
+    flush = make_flush(args.flush_mib)
+    log(f"num_splits={num_splits}; warmup >= {args.warmup} steps and >= {args.warmup_seconds} s")
+    warm_steps, warm_t0 = 0, time.perf_counter()
+    while warm_steps < args.warmup or time.perf_counter() - warm_t0 < args.warmup_seconds:
+        flush()
         run_step()
+        warm_steps += 1
+        if warm_steps % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
-    # (1) the step itself: K steps back to back, no event inside the steps
-    # (optionally replayed from a HIP graph captured once)
+    warm_s = time.perf_counter() - warm_t0
     graph = None
     if args.graph:
         graph = torch.cuda.CUDAGraph()
@@ -536,41 +604,39 @@ def main():
         for _ in range(args.warmup):
             graph.replay()
         torch.cuda.synchronize()
+    # (1) the step: K reps, each right after an untimed flush, each with its own
+    # event pair on the launch stream
     log(f"timing {args.steps} steps" + (" (graph replays)" if graph is not None else ""))
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    step_ms = []
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
+    for e0, e1 in evs:
+        flush()
+        e0.record(stream)
         if graph is not None:
             graph.replay()
         else:
             run_step()
-    end.record(stream)
+        e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    ms_step = start.elapsed_time(end) / args.steps
-    # (2) the dominant kernel: the same K steps again, with HIP events recorded on
-    # the launch stream right before and after mla_decode in every 5th step.  An
-    # event pair adds a few microseconds of idle time to its step; on every step
-    # that idle time would let the clock rise and flatter the kernel, so only a
-    # sample of the steps carries one.
-    every = 5
-    evs = {}
-    for k in range(args.steps):
-        ev = None
-        if k % every == every - 1:
-            ev = evs[k] = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    step_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    ms_step = sum(step_ms) / len(step_ms)
+    # (2) the dominant kernel: max(K, --kernel-reps) more reps, each after a flush,
+    # with an event pair right around mla_decode
+    n_dec = max(args.steps, args.kernel_reps)
+    dec_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_dec)]
+    for ev in dec_evs:
+        flush()
         run_step(ev)
     torch.cuda.synchronize()
-    if not evs:   # fewer steps than the sampling period: time the last one
-        ev = evs[0] = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-        run_step(ev)
-        torch.cuda.synchronize()
-    dec_ms = [a.elapsed_time(b) for a, b in evs.values()]
+    dec_ms = [a.elapsed_time(b) for a, b in dec_evs]
     dec_avg = sum(dec_ms) / len(dec_ms)
-    log(f"step {ms_step * 1e3:.1f} us (wall {wall / args.steps * 1e6:.1f} us); decode kernel avg "
-        f"{dec_avg * 1e3:.1f} us (min {min(dec_ms) * 1e3:.1f})")
+    med = lambda v: sorted(v)[len(v) // 2] if len(v) % 2 else 0.5 * (sorted(v)[len(v) // 2 - 1] + sorted(v)[len(v) // 2])
+    log(f"step mean {ms_step * 1e3:.1f} us, median {med(step_ms) * 1e3:.1f}, min {min(step_ms) * 1e3:.1f} "
+        f"(wall incl. flushes {wall / args.steps * 1e6:.1f} us); decode kernel mean {dec_avg * 1e3:.1f} us, median "
+        f"{med(dec_ms) * 1e3:.1f}, min {min(dec_ms) * 1e3:.1f} over {n_dec} launches")
 
     nbytes = algorithmic_bytes(w, ctx)
     flops = decode_flops(w, ctx, pos)
@@ -593,6 +659,14 @@ def main():
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic (seeded Philox N(0,1) latents/queries, "
         "N(0,1/d_c) weights)",
+        "timing": {"step_us": {"mean": round(ms_step * 1e3, 2), "median": round(med(step_ms) * 1e3, 2),
+                               "min": round(min(step_ms) * 1e3, 2), "reps": len(step_ms)},
+                   "decode_us": {"mean": round(dec_avg * 1e3, 2), "median": round(med(dec_ms) * 1e3, 2),
+                                 "min": round(min(dec_ms) * 1e3, 2), "reps": len(dec_ms)},
+                   "flush_mib_per_rep": args.flush_mib, "warmup_steps_run": warm_steps,
+                   "warmup_seconds_run": round(warm_s, 3),
+                   "note": "one HIP event pair per rep on the launch stream; an untimed read+write flush of "
+                           "flush_mib_per_rep MiB before every rep; value and ms_per_step use the mean"},
         "config": {"workload": w.name, "description": w.description, "fused_tail": fused_tail,
                    "fused_append": not args.separate_append,
                    "step_launch": "graph" if graph is not None else "eager", "batch": w.batch, "n_q": w.n_q,
@@ -605,6 +679,7 @@ def main():
         "roofline": {"kernel": "mla_decode (decode_mfma_kernel)", **roof,
                      "traffic": measured_traffic(w.name), "bytes_per_launch": nbytes["decode"],
                      "flops_per_launch": flops, "avg_launch_us": round(dec_avg * 1e3, 3),
+                     "median_launch_us": round(med(dec_ms) * 1e3, 3), "min_launch_us": round(min(dec_ms) * 1e3, 3),
                      "launches_timed": len(dec_ms)},
         "cpu_baseline": None,
     }
