@@ -50,6 +50,9 @@ def parse():
                     help="minimum number of mla_decode launches timed for the roofline (at least --steps)")
     ap.add_argument("--flush-mib", type=int, default=1024,
                     help="MiB read and written by the untimed flush before every timed rep (0 = no flush)")
+    ap.add_argument("--flush-kind", choices=("rw+read", "rw"), default="rw+read",
+                    help="rw+read: write the flush buffer, then read another one so the caches end clean; rw: only "
+                         "the read-write pass (its dirty lines are written back inside the next rep)")
     ap.add_argument("--workload", default="v3_paged",
                     help="v3_paged (default: the largest single-GPU workload, B=128 ragged contexts, paged), "
                          "v3_b64, v3_split, v3_b1, tiny_fp32")
@@ -238,15 +241,29 @@ def copy_probe(mib):
     log(f"copy probe: 5 x {mib} MiB read + {mib} MiB written")
 
 
-def make_flush(mib):
-    """An untimed flush of the GPU caches: one elementwise kernel that reads and
-    writes ``mib`` MiB (4x the 256 MB memory-side cache for the default 1 GiB),
-    so a rep after it finds nothing of its inputs in L2 or that cache."""
+def make_flush(mib, kind="rw+read"):
+    """An untimed flush of the GPU caches before a timed rep.
+
+    "rw": one elementwise kernel that reads and writes ``mib`` MiB (4x the
+    256 MB memory-side cache for the default 1 GiB): afterwards L2 and that
+    cache hold nothing of the rep's inputs, but they hold dirty lines whose
+    write-back then lands inside the timed rep.  "rw+read" (default): the
+    same, then a reduction that only reads another ``mib`` MiB, which writes
+    the dirty lines back before the rep and leaves the caches clean."""
     import torch
     if mib <= 0:
         return lambda: None
-    buf = torch.zeros(mib * (1 << 20) // 4, dtype=torch.float32, device="cuda")
-    return lambda: buf.add_(1.0)
+    n = mib * (1 << 20) // 4
+    buf = torch.zeros(n, dtype=torch.float32, device="cuda")
+    if kind == "rw":
+        return lambda: buf.add_(1.0)
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    acc = torch.zeros((), dtype=torch.float32, device="cuda")
+
+    def flush():
+        buf.add_(1.0)
+        torch.sum(src, (0,), out=acc)
+    return flush
 
 
 def folds_bench(args):
@@ -584,7 +601,7 @@ def main():
             mla.mla_combine(d, st["cache"].ctx_lens, num_splits, step.u_part, step.lse_part, step.u, step.lse)
             mla.mla_out_proj(d, step.u, st["w_uv"], step.out)
 
-    flush = make_flush(args.flush_mib)
+    flush = make_flush(args.flush_mib, args.flush_kind)
     log(f"num_splits={num_splits}; warmup >= {args.warmup} steps and >= {args.warmup_seconds} s")
     warm_steps, warm_t0 = 0, time.perf_counter()
     while warm_steps < args.warmup or time.perf_counter() - warm_t0 < args.warmup_seconds:
@@ -663,10 +680,12 @@ def main():
                                "min": round(min(step_ms) * 1e3, 2), "reps": len(step_ms)},
                    "decode_us": {"mean": round(dec_avg * 1e3, 2), "median": round(med(dec_ms) * 1e3, 2),
                                  "min": round(min(dec_ms) * 1e3, 2), "reps": len(dec_ms)},
-                   "flush_mib_per_rep": args.flush_mib, "warmup_steps_run": warm_steps,
+                   "flush_mib_per_rep": args.flush_mib, "flush_kind": args.flush_kind,
+                   "warmup_steps_run": warm_steps,
                    "warmup_seconds_run": round(warm_s, 3),
-                   "note": "one HIP event pair per rep on the launch stream; an untimed read+write flush of "
-                           "flush_mib_per_rep MiB before every rep; value and ms_per_step use the mean"},
+                   "note": "one HIP event pair per rep on the launch stream; before every rep an untimed flush: "
+                           "read+write flush_mib_per_rep MiB, then (rw+read) read another flush_mib_per_rep MiB "
+                           "so no dirty line is left; value and ms_per_step use the mean"},
         "config": {"workload": w.name, "description": w.description, "fused_tail": fused_tail,
                    "fused_append": not args.separate_append,
                    "step_launch": "graph" if graph is not None else "eager", "batch": w.batch, "n_q": w.n_q,

@@ -12,7 +12,9 @@ import os
 from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmla.so")
+# The in-tree build; MLA_LIBRARY names another build of the same ABI (for
+# comparing kernel variants).  Either way the HIP library is required.
+LIB_PATH = os.environ.get("MLA_LIBRARY") or os.path.join(HERE, "libmla.so")
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP, MLA_ERR_OUT_OF_BLOCKS = 0, 1, 2, 3, 4
 F32, BF16, FP8_E4M3 = 0, 1, 2

@@ -76,6 +76,11 @@ constexpr int NRAW = 3;               // fp8: stages of raw rows in flight per w
 // 8w .. 8w+7 (1 load), the tile's scale of every token (1 load of 4 B per lane).
 constexpr int RAW_CODES = 0, RAW_ROPE = 4096, RAW_SCALE = 5120, RAW_WAVE_BYTES = 5376;
 constexpr int FP8_LOADS_PER_STAGE = 6;
+// s_waitcnt immediates (GFX9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
+// vmcnt[5:4] << 14) that wait on vector memory only.  Issued through the
+// builtin so that the compiler's own wait insertion sees them.
+constexpr int kWaitVm0 = 0x0F70, kWaitVm9 = 0x0F79, kWaitVm18 = 0x4F72;
+constexpr int kWaitVm6 = 0x0F76, kWaitVm12 = 0x0F7C;   // fp8: 6 loads per stage
 // Word 3 of a raw buffer resource on gfx9-class chips (32-bit data format, no
 // swizzle, offsets in bytes); words 0-2 carry the base and the byte range.
 constexpr int kBufferWord3 = 0x00020000;
@@ -124,8 +129,10 @@ enum Layout : int {
 // stage meets at most two blocks, k0 from row r0 on, then k1).  Stages come in
 // order, T tokens apart, so (k0, r0) follows from the previous stage without a
 // division (a restart recomputes it).  The block ids come from a window of 64
-// ids, one per lane (`ids`), reloaded (one vector load; its wait also covers
-// the stage loads in flight) when a stage leaves it.  locate() gives the byte
+// ids, one per lane (`ids`), reloaded when a stage leaves it (one vector load,
+// waited for right there: a wait placed by the compiler at the uses of `ids`
+// would sit on every stage's path and drain the stage loads in flight each
+// time; this one runs once per 64 blocks).  locate() gives the byte
 // offsets, from the resource base at block blk_lo, of the stage's rows: row
 // t < span + 1 of the stage is at off(t), rows past the segment end repeat its
 // last row (uint32 arithmetic, exact modulo 2^32).
@@ -164,6 +171,7 @@ struct PagedCursor {
       kbase = k0;
       const int k = k0 + lane;
       ids = k <= (tok_end - 1) / bs ? c.block_table[(int64_t)b * c.max_blocks + k] : 0;
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
     }
     const int blk0 = __builtin_amdgcn_readlane(ids, k0 - kbase);
     const int blk1 = __builtin_amdgcn_readlane(ids, k1 - kbase);
@@ -440,11 +448,6 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// s_waitcnt immediates (GFX9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
-// vmcnt[5:4] << 14) that wait on vector memory only.  Issued through the
-// builtin so that the compiler's own wait insertion sees them.
-constexpr int kWaitVm0 = 0x0F70, kWaitVm9 = 0x0F79, kWaitVm18 = 0x4F72;
-constexpr int kWaitVm6 = 0x0F76, kWaitVm12 = 0x0F7C;   // fp8: 6 loads per stage
 static_assert(FP8_LOADS_PER_STAGE == 6 && NRAW == 3, "fp8 wait counts assume 6 loads per stage, 3 raw stages");
 
 // O += A . B for one 32x32 block of the PV product, with the accumulator pinned
@@ -543,9 +546,13 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
       const int qpos = a.positions[(int64_t)b * a.n_q + jq];
       limit = qpos + 1 < t1 ? qpos + 1 : t1;
     }
-    // The query loads are not waited for here: the first stages' loads are
-    // issued behind them, and the wait for stage 0 (vector-memory counter,
-    // completed in order) covers them too.
+    // Wait for the query rows before the first stage loads go out.  The
+    // stage loop reads these registers in every iteration; without a wait
+    // that covers them on every path, the compiler puts vector-memory waits
+    // in front of their uses inside the loop, and such a wait also waits for
+    // the stage loads issued just before it (the counter completes in order),
+    // which drains the prefetch pipeline once per stage.
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     std::conditional_t<FP8, Fp8Loader<SL>, StageLoader<SL>> ld;
     ld.init(a.cache, b, t1, wave, lane, blk_lo);
     // bf16 stage s (ring of NSTAGE, or two buffers for fp8); this wave's part of raw stage s
