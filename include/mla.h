@@ -29,12 +29,24 @@
  *     (a hipStream_t passed as void*, NULL = default stream) and returns.
  *   - Argument errors are found on the host before anything is enqueued and
  *     return MLA_ERR_INVALID_ARG; a shape the compiled kernels do not cover
- *     returns MLA_ERR_UNSUPPORTED; a failed launch returns MLA_ERR_HIP.
+ *     returns MLA_ERR_UNSUPPORTED; a failed launch returns MLA_ERR_HIP, and
+ *     mla_last_hip_error() then gives the hipError_t behind it.
+ *   - Arrays the kernels move in 16-byte vectors must be 16-byte aligned
+ *     (each entry point names them; MLA_ERR_INVALID_ARG otherwise).  Buffers
+ *     from a device allocator are; an offset view may not be.
  *   - Device-side contents (context lengths, positions, block ids) are the
- *     caller's contract and are not checked: ctx_lens[b] >= 0, positions in
- *     [0, ctx_lens[b]), block ids in [0, number of blocks).
- *   - The library keeps no mutable global state; concurrent calls on
- *     different streams are safe when their output buffers do not overlap.
+ *     caller's contract and are not checked on the host: ctx_lens[b] >= n_q,
+ *     positions[b][j] = ctx_lens[b] - n_q + j for decode, block ids in
+ *     [0, number of blocks), ctx_lens[b] <= max_blocks * block_size (paged)
+ *     or ctx_lens[b] * row <= seq_stride (contiguous).  The kernels keep
+ *     memory safety where they can see a breach: decode treats a segment
+ *     whose block ids include a negative one, or whose tokens run past
+ *     max_blocks * block_size, as empty (its partial is u = 0, lse = -inf);
+ *     an append skips a row whose block is missing (negative id) or lies
+ *     past max_blocks.
+ *   - The only mutable state is the per-thread record behind
+ *     mla_last_hip_error(); concurrent calls on different streams are safe
+ *     when their output buffers do not overlap.
  */
 #ifndef MLA_H
 #define MLA_H
@@ -76,7 +88,8 @@ typedef struct {
  *     token t of sequence b is row (t % block_size) of block
  *     block_table[b * max_blocks + t / block_size].
  * ctx_lens [B]: number of cached tokens of each sequence (the query tokens'
- * own rows included).  `data` must be 16-byte aligned.
+ * own rows included).  `data` must be 16-byte aligned.  A contiguous cache
+ * needs seq_stride >= one row (d_c + d_rope elements; the fp8 row's bytes).
  *
  * fp8 cache (dtype MLA_FP8_E4M3; [Huny], serving checklist, fp8 KV-cache item
  * and [Paldyn], KV-cache quantisation: per-block scales rather than one
@@ -143,7 +156,11 @@ int64_t mla_num_partials(int32_t B, int32_t num_splits);
  *                                     t <= positions[b][j]
  *   u_part    [mla_num_partials(B, num_splits)][n_q][n_h][d_c]  fp32, out
  *   lse_part  [mla_num_partials(B, num_splits)][n_q][n_h][2]    fp32, out
- * Requires 1 <= num_splits. */
+ * Requires 1 <= num_splits; q_lat, q_pe and u_part 16-byte aligned, lse_part
+ * 8-byte aligned.  The merge is always needed, also for num_splits = 1: a
+ * sequence that shares a work unit with another still gets its own partial,
+ * and a partial is unnormalised (mla_combine or mla_combine_out_proj turns
+ * it into u). */
 mla_status_t mla_decode(const mla_dims_t *dims, int32_t B, int32_t n_q, const void *q_lat,
                         const void *q_pe, const mla_cache_t *cache, const int32_t *positions,
                         int32_t num_splits, float *u_part, float *lse_part, void *stream);
@@ -153,8 +170,10 @@ mla_status_t mla_decode(const mla_dims_t *dims, int32_t B, int32_t n_q, const vo
  *   u[b][j][i][:] = sum_k exp(r_k - L) u_part_k,   lse[b][j][i] = L,
  * i.e. the softmax over the union of the ranges ([Ikmyung] §1.4) written in
  * terms of per-range results; u = 0, lse = -inf when every partial is empty.
- * ctx_lens and num_splits must be those given to mla_decode.
- *   u   [B][n_q][n_h][d_c] fp32, out;  lse [B][n_q][n_h] fp32, out (may be NULL) */
+ * ctx_lens and num_splits must be those given to mla_decode (they fix the
+ * slot layout; ctx_lens is the cache's, as mla_decode read it).
+ *   u   [B][n_q][n_h][d_c] fp32, out;  lse [B][n_q][n_h] fp32, out (may be NULL)
+ * u_part and u 16-byte aligned, lse_part 8-byte aligned. */
 mla_status_t mla_combine(const mla_dims_t *dims, int32_t B, int32_t n_q, const int32_t *ctx_lens,
                          int32_t num_splits, const float *u_part, const float *lse_part,
                          float *u, float *lse, void *stream);
@@ -164,7 +183,8 @@ mla_status_t mla_combine(const mla_dims_t *dims, int32_t B, int32_t n_q, const i
  *   w_uv [n_h][d_c][d_v]      dtype w_dt
  *   out  [B][n_q][n_h][d_v]   fp32, out
  * With bf16 weights the fp32 u is split into a bf16 high part and a bf16
- * residual and both are multiplied (fp32 accumulation). */
+ * residual and both are multiplied (fp32 accumulation).  u and w_uv 16-byte
+ * aligned. */
 mla_status_t mla_out_proj(const mla_dims_t *dims, int32_t B, int32_t n_q, const float *u,
                           mla_dtype_t w_dt, const void *w_uv, float *out, void *stream);
 
@@ -173,7 +193,7 @@ mla_status_t mla_out_proj(const mla_dims_t *dims, int32_t B, int32_t n_q, const 
  *   out[b][j][i][:] = (sum_k exp(r_k - L) u_part_k) W_i^UV,   lse[b][j][i] = L,
  * L = log sum_k exp(lse_k) over the partials k of (b, j, i).  The merged u is
  * not stored.  Arguments as for mla_combine and mla_out_proj; lse may be
- * NULL.  Compiled for bf16 weights with d_c = 512 and d_v = 128; other shapes
+ * NULL; u_part and w_uv 16-byte aligned, lse_part 8-byte aligned.  Compiled for bf16 weights with d_c = 512 and d_v = 128; other shapes
  * return MLA_ERR_UNSUPPORTED (use mla_combine, then mla_out_proj). */
 mla_status_t mla_combine_out_proj(const mla_dims_t *dims, int32_t B, int32_t n_q, const int32_t *ctx_lens,
                                   int32_t num_splits, const float *u_part, const float *lse_part,
@@ -318,6 +338,15 @@ int32_t mla_block_pool_free_count(const void *pool);
 
 /* Static description of a status code. */
 const char *mla_status_string(mla_status_t status);
+
+/* The hipError_t (as an integer) behind the last MLA_ERR_HIP returned to the
+ * calling thread; 0 (hipSuccess) if there was none.  A later MLA_ERR_HIP
+ * overwrites it; other results leave it. */
+int32_t mla_last_hip_error(void);
+
+/* Static name of a hipError_t value (hipGetErrorName), e.g. for
+ * mla_last_hip_error(); needs no GPU. */
+const char *mla_hip_error_name(int32_t code);
 
 /* Library version string. */
 const char *mla_version(void);

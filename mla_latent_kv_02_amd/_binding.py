@@ -21,7 +21,7 @@ F32, BF16, FP8_E4M3 = 0, 1, 2
 
 EXPORTED = ("mla_absorb_q", "mla_decode", "mla_combine", "mla_out_proj", "mla_combine_out_proj",
             "mla_cache_append", "mla_append_absorb_q", "mla_num_partials", "mla_cache_row_bytes",
-            "mla_status_string", "mla_version",
+            "mla_status_string", "mla_version", "mla_last_hip_error", "mla_hip_error_name",
             "mla_block_pool_bytes", "mla_block_pool_init", "mla_block_pool_reserve", "mla_block_pool_reserve_all",
             "mla_block_pool_release", "mla_fold_out", "mla_out_proj_folded", "mla_o_proj", "mla_fold_q",
             "mla_absorb_q_folded", "mla_prefill_weights", "mla_prefill_workspace_bytes", "mla_prefill",
@@ -101,6 +101,9 @@ def load_library(path: str = LIB_PATH):
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_version.restype = ctypes.c_char_p
+    lib.mla_last_hip_error.restype = ctypes.c_int32
+    lib.mla_hip_error_name.argtypes = [ctypes.c_int32]
+    lib.mla_hip_error_name.restype = ctypes.c_char_p
     _LIB = lib
     return lib
 
@@ -212,7 +215,12 @@ def _stream(stream) -> Optional[int]:
 
 def _check(fn: str, status: int):
     if status != MLA_OK:
-        raise MlaError(fn, status, load_library().mla_status_string(status).decode())
+        lib = load_library()
+        msg = lib.mla_status_string(status).decode()
+        if status == MLA_ERR_HIP:   # name the HIP error behind it
+            code = lib.mla_last_hip_error()
+            msg += f": {lib.mla_hip_error_name(code).decode()} ({code})"
+        raise MlaError(fn, status, msg)
 
 
 def mla_num_partials(B: int, num_splits: int) -> int:

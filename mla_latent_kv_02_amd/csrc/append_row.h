@@ -33,12 +33,15 @@ __device__ __forceinline__ void rope_pair(int pos, int r, int d_rope, float base
 }
 
 // Element pair `pair` (elements 2 pair, 2 pair + 1) of new row k.  Requires
-// 2 * pair < d_c + d_rope.
+// 2 * pair < d_c + d_rope.  A row the descriptor cannot place (no block
+// reserved for it) is skipped.
 template <typename T>
 __device__ __forceinline__ void append_pair(const AppendParams& p, int k, int pair) {
   const int b = p.seq_ids[k];
   const int pos = p.positions[k];
-  T* dst = static_cast<T*>(p.cache_data) + cache_row_offset(p.cache, b, pos);
+  const int64_t off = cache_row_offset_checked(p.cache, b, pos);
+  if (off < 0) return;   // no block reserved for this row: nothing is written
+  T* dst = static_cast<T*>(p.cache_data) + off;
   const int e = 2 * pair;
   if (e < p.d_c) {
     const T* src = static_cast<const T*>(p.c_kv) + (int64_t)k * p.c_kv_stride + e;
@@ -65,7 +68,9 @@ __device__ __forceinline__ void append_pair(const AppendParams& p, int k, int pa
 __device__ __forceinline__ void append_row_fp8(const AppendParams& p, int k, int lane) {
   const int b = p.seq_ids[k];
   const int pos = p.positions[k];
-  unsigned char* dst = static_cast<unsigned char*>(p.cache_data) + cache_row_offset(p.cache, b, pos);
+  const int64_t off = cache_row_offset_checked(p.cache, b, pos);
+  if (off < 0) return;   // no block reserved for this row (the whole wave skips it)
+  unsigned char* dst = static_cast<unsigned char*>(p.cache_data) + off;
   const uint16_t* src = static_cast<const uint16_t*>(p.c_kv) + (int64_t)k * p.c_kv_stride;
   const int n_tiles = p.d_c / kFp8Tile;
   float* scales = reinterpret_cast<float*>(dst + p.d_c + 2 * p.d_rope);

@@ -90,7 +90,9 @@ __global__ __launch_bounds__(NT) void decode_generic_kernel(DecodeParams p) {
       q_s[e] = e < p.d_c ? Elem<Q>::load(q_lat, qrow * p.d_c + e)
                          : Elem<Q>::load(q_pe, qrow * p.d_rope + (e - p.d_c));
     const int qpos = p.positions[(int64_t)b * p.n_q + jq];
-    const int limit = qpos + 1 < t1 ? qpos + 1 : t1;
+    // a range whose rows the descriptor cannot place is taken as empty
+    const int t_end = segment_rows_placed(p.cache, b, t0, t1, tid & 63) ? t1 : t0;
+    const int limit = qpos + 1 < t_end ? qpos + 1 : t_end;
     __syncthreads();
     float acc[MAX_DC_PER_THREAD] = {0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;

@@ -97,6 +97,13 @@ struct DecodeArgs {
   float scale_log2;        // sm_scale * log2(e)
 };
 
+// Byte range of a buffer resource over the first n rows of rb bytes (the
+// resource's range is 32 bits; the launch keeps a sequence within 4 GiB).
+__device__ __forceinline__ int record_bytes(int n, int rb) {
+  const int64_t v = (int64_t)n * rb;
+  return (int)(uint32_t)(v < (int64_t)0xFFFFFFFF ? v : (int64_t)0xFFFFFFFF);
+}
+
 // s(t) of the stage layout: P[(t >> 1) & 7] with P packed in nibbles
 __device__ __forceinline__ int swz(int t) { return (0x73625140 >> (4 * ((t >> 1) & 7))) & 7; }
 
@@ -224,7 +231,7 @@ struct StageLoader {
     if (LAYOUT == kContiguous) {
       base += (int64_t)b * cache.seq_stride * 2;
       rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(base), (short)0,
-                                               tok_end * RB16, kBufferWord3);
+                                               record_bytes(tok_end, RB16), kBufferWord3);
       lane_off = tt * RB16 + chunk_off;
     } else if (LAYOUT == kPaged) {
       pc.init(cache.block_size, RB16);
@@ -307,8 +314,8 @@ struct Fp8Loader {
     base = static_cast<const unsigned char*>(cache.data);
     if (LAYOUT == kContiguous) {
       base += (int64_t)b * cache.seq_stride;    // bytes
-      rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(base), (short)0, tok_end * RB8,
-                                               kBufferWord3);
+      rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(base), (short)0,
+                                               record_bytes(tok_end, RB8), kBufferWord3);
 #pragma unroll
       for (int k = 0; k < 3; ++k) lc[k] = (uint32_t)token(k == 0 ? 0 : k + 3) * RB8 + byte(k == 0 ? 0 : k + 3);
     } else if (LAYOUT == kPaged) {
@@ -415,14 +422,17 @@ __device__ __forceinline__ void convert_fp8_stage(const unsigned char* rw, unsig
 }
 
 // Paged cache, tokens t0..t1-1 of sequence b: the lowest block id among their
-// blocks, and whether all of them lie within 4 GiB of it (so that 32-bit
-// buffer offsets from it reach every row).  Each wave reads the block table
-// entries itself and reduces them across its lanes; the result is the same in
-// every wave.
-__device__ __forceinline__ bool paged_span(const CacheView& c, int b, int t0, int t1, int lane, int row_bytes,
-                                           int* blk_lo) {
+// blocks, and whether all of them lie within 4 GiB of it (kSpanNear: 32-bit
+// buffer offsets from it reach every row) or not (kSpanFar); kSpanInvalid if
+// the descriptor cannot place them (a block past the table row, or a negative
+// id).  Each wave reads the block table entries itself and reduces them across
+// its lanes; the result is the same in every wave.
+enum SpanKind : int { kSpanNear = 0, kSpanFar = 1, kSpanInvalid = 2 };
+__device__ __forceinline__ int paged_span(const CacheView& c, int b, int t0, int t1, int lane, int row_bytes,
+                                          int* blk_lo) {
   const int bs = c.block_size;
   const int k0 = t0 / bs, k1 = (t1 - 1) / bs;
+  if (k1 >= c.max_blocks) return kSpanInvalid;
   int lo = INT_MAX, hi = INT_MIN;
   for (int k = k0 + lane; k <= k1; k += 64) {
     const int id = c.block_table[(int64_t)b * c.max_blocks + k];
@@ -436,8 +446,9 @@ __device__ __forceinline__ bool paged_span(const CacheView& c, int b, int t0, in
     hi = oh > hi ? oh : hi;
   }
   *blk_lo = __builtin_amdgcn_readfirstlane(lo);
+  if (*blk_lo < 0) return kSpanInvalid;
   const int64_t span = ((int64_t)__builtin_amdgcn_readfirstlane(hi) - *blk_lo + 1) * bs * row_bytes;
-  return span <= (int64_t)0xFFFFFFFF;
+  return span <= (int64_t)0xFFFFFFFF ? kSpanNear : kSpanFar;
 }
 
 // Workgroup barrier that waits only for this wave's LDS operations (a
@@ -914,14 +925,19 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
   using Paged = std::integral_constant<int, kPaged>;
   using Any = std::integral_constant<int, kAnyLayout>;
   for_each_segment<NT>(a.ctx_lens, a.B, a.num_splits, w, &sm->plan, [&](int b, int t0, int t1, int slot) {
+    // (a range the descriptor cannot place is taken as empty: its partial is
+    // u = 0, lse = -inf, and no row of it is read)
     if constexpr (LAYOUT == kContiguous) {
       segment(Contig{}, b, t0, t1, slot, 0);
     } else if constexpr (LAYOUT == kPaged) {
-      int blk_lo;
-      if (paged_span(a.cache, b, t0, t1, lane, FP8 ? RB8 : RB16, &blk_lo)) segment(Paged{}, b, t0, t1, slot, blk_lo);
-      else segment(Any{}, b, t0, t1, slot, 0);    // blocks 4 GiB or more apart
+      int blk_lo = 0;
+      const int span = paged_span(a.cache, b, t0, t1, lane, FP8 ? RB8 : RB16, &blk_lo);
+      if (span == kSpanNear) segment(Paged{}, b, t0, t1, slot, blk_lo);
+      else if (span == kSpanFar) segment(Any{}, b, t0, t1, slot, 0);    // blocks 4 GiB or more apart
+      else segment(Any{}, b, t0, t0, slot, 0);
     } else {
-      segment(Any{}, b, t0, t1, slot, 0);
+      const bool placed = segment_rows_placed(a.cache, b, t0, t1, lane);
+      segment(Any{}, b, t0, placed ? t1 : t0, slot, 0);
     }
   });
 }

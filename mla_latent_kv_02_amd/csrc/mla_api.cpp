@@ -34,11 +34,15 @@ float base_of(const mla_dims_t* d) { return d->rope_base > 0.f ? d->rope_base : 
 
 bool cache_ok(const mla_cache_t* c, const mla_dims_t* d) {
   if (!c || !c->data || !c->ctx_lens || !cache_dtype_ok(c->dtype)) return false;
-  if (row_bytes(d, c->dtype) < 0) return false;
+  const int64_t rb = row_bytes(d, c->dtype);
+  if (rb < 0) return false;
   if (reinterpret_cast<uintptr_t>(c->data) % 16) return false;
   if (c->block_size < 0) return false;
   if (c->block_size > 0) return c->block_table && c->max_blocks >= 1;
-  return c->seq_stride >= 0;
+  // contiguous: a sequence holds at least one row (seq_stride counts elements,
+  // bytes for fp8 rows)
+  const int64_t row_units = c->dtype == MLA_FP8_E4M3 ? rb : d->d_c + d->d_rope;
+  return c->seq_stride >= row_units;
 }
 
 mla::CacheView view_of(const mla_cache_t* c, const mla_dims_t* d) {
@@ -53,8 +57,16 @@ mla::CacheView view_of(const mla_cache_t* c, const mla_dims_t* d) {
   return v;
 }
 
-mla_status_t from_hip(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+// The HIP error behind the last MLA_ERR_HIP this thread got (hipSuccess if none).
+thread_local hipError_t t_last_hip_error = hipSuccess;
+
+mla_status_t from_hip(hipError_t e) {
+  if (e == hipSuccess) return MLA_OK;
+  t_last_hip_error = e;
+  return MLA_ERR_HIP;
+}
 bool al16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+bool al8(const void* p) { return reinterpret_cast<uintptr_t>(p) % 8 == 0; }
 
 // Checks the arguments of mla_absorb_q and fills *p (p->B == 0: nothing to do).
 mla_status_t absorb_args(const mla_dims_t* dims, int32_t B, int32_t n_q, mla_dtype_t dt, const void* q_nope,
@@ -112,7 +124,11 @@ const char* mla_status_string(mla_status_t s) {
   return "unknown status";
 }
 
-const char* mla_version(void) { return "mla-mi355x 0.1.0 (gfx950)"; }
+const char* mla_version(void) { return "mla-mi355x 0.2.0 (gfx950)"; }
+
+int32_t mla_last_hip_error(void) { return (int32_t)t_last_hip_error; }
+
+const char* mla_hip_error_name(int32_t code) { return hipGetErrorName((hipError_t)code); }
 
 int64_t mla_cache_row_bytes(const mla_dims_t* dims, mla_dtype_t dtype) {
   if (!dims_ok(dims) || !cache_dtype_ok(dtype)) return -1;
@@ -141,6 +157,8 @@ mla_status_t mla_decode(const mla_dims_t* dims, int32_t B, int32_t n_q, const vo
   if (B == 0) return MLA_OK;
   if (!q_lat || !q_pe || !positions || !u_part || !lse_part || !cache_ok(cache, dims))
     return MLA_ERR_INVALID_ARG;
+  // the kernels move q_lat, q_pe and u_part in 16-byte vectors, lse_part in pairs
+  if (!al16(q_lat) || !al16(q_pe) || !al16(u_part) || !al8(lse_part)) return MLA_ERR_INVALID_ARG;
   if ((int64_t)n_q * dims->n_h > 65535) return MLA_ERR_UNSUPPORTED;
   mla::DecodeParams p;
   p.q_lat = q_lat; p.q_pe = q_pe; p.cache = view_of(cache, dims); p.ctx_lens = cache->ctx_lens;
@@ -161,6 +179,7 @@ mla_status_t mla_combine(const mla_dims_t* dims, int32_t B, int32_t n_q, const i
     return MLA_ERR_INVALID_ARG;
   if (B == 0) return MLA_OK;
   if (!ctx_lens || !u_part || !lse_part || !u) return MLA_ERR_INVALID_ARG;
+  if (!al16(u_part) || !al8(lse_part) || !al16(u)) return MLA_ERR_INVALID_ARG;
   if ((int64_t)n_q * dims->n_h > 65535 * 4) return MLA_ERR_UNSUPPORTED;
   mla::CombineParams p;
   p.ctx_lens = ctx_lens; p.u_part = u_part; p.lse_part = lse_part; p.u = u; p.lse = lse;
@@ -173,6 +192,7 @@ mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t B, int32_t n_q, const 
   if (!dims_ok(dims) || B < 0 || n_q < 1 || !dtype_ok(w_dt)) return MLA_ERR_INVALID_ARG;
   if (B == 0) return MLA_OK;
   if (!u || !w_uv || !out) return MLA_ERR_INVALID_ARG;
+  if (!al16(u) || !al16(w_uv)) return MLA_ERR_INVALID_ARG;
   if ((size_t)16 * dims->d_c * sizeof(float) > 64 * 1024) return MLA_ERR_UNSUPPORTED;
   mla::OutProjParams p;
   p.u = u; p.w_uv = w_uv; p.out = out;
@@ -195,6 +215,7 @@ mla_status_t mla_combine_out_proj(const mla_dims_t* dims, int32_t B, int32_t n_q
     return MLA_ERR_INVALID_ARG;
   if (B == 0) return MLA_OK;
   if (!ctx_lens || !u_part || !lse_part || !w_uv || !out) return MLA_ERR_INVALID_ARG;
+  if (!al16(u_part) || !al8(lse_part) || !al16(w_uv)) return MLA_ERR_INVALID_ARG;
   if (!mla::tail_mfma_ok(dims->d_c, dims->d_v, w_dt == MLA_BF16)) return MLA_ERR_UNSUPPORTED;
   mla::TailParams p{};
   p.ctx_lens = ctx_lens; p.u_part = u_part; p.lse_part = lse_part; p.w_uv = w_uv; p.out = out; p.lse = lse;

@@ -71,6 +71,33 @@ __device__ __forceinline__ int64_t cache_row_offset(const CacheView& c, int b, i
   return ((int64_t)blk * c.block_size + (t % c.block_size)) * (int64_t)c.row;
 }
 
+// As cache_row_offset, or -1 where the descriptor cannot place the row: a
+// negative position, or (paged) a block past the table row or a negative
+// block id (a block the caller has not reserved).
+__device__ __forceinline__ int64_t cache_row_offset_checked(const CacheView& c, int b, int t) {
+  if (t < 0) return -1;
+  if (c.block_size == 0) return (int64_t)b * c.seq_stride + (int64_t)t * c.row;
+  const int k = t / c.block_size;
+  if (k >= c.max_blocks) return -1;
+  const int blk = c.block_table[(int64_t)b * c.max_blocks + k];
+  if (blk < 0) return -1;
+  return ((int64_t)blk * c.block_size + (t % c.block_size)) * (int64_t)c.row;
+}
+
+// Whether every row of tokens t0..t1-1 (t0 < t1) of sequence b is placed by a
+// paged descriptor: the range's blocks lie within the table row and none of
+// their ids is negative.  The lanes of the calling wave read the table row
+// together; the result is the same in every lane (and in every wave that
+// asks).  Contiguous caches: true.
+__device__ __forceinline__ bool segment_rows_placed(const CacheView& c, int b, int t0, int t1, int lane) {
+  if (c.block_size == 0) return true;
+  const int k0 = t0 / c.block_size, k1 = (t1 - 1) / c.block_size;
+  if (k1 >= c.max_blocks) return false;
+  int bad = 0;
+  for (int k = k0 + lane; k <= k1; k += 64) bad |= c.block_table[(int64_t)b * c.max_blocks + k] < 0;
+  return __builtin_amdgcn_ballot_w64(bad != 0) == 0;
+}
+
 // ------------------------------------------------------ split-KV work plan
 // The tokens of all sequences, in order, are cut into ranges of Q tokens
 // (Q = ceil(total / num_splits)); range w is work unit w.  Sequence b (prefix

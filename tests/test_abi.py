@@ -225,3 +225,62 @@ def test_prefill_argument_checks(lib):
         == bd.MLA_ERR_UNSUPPORTED
     assert lib.mla_prefill_weights(d, None, FAKE, FAKE, None) == bd.MLA_ERR_INVALID_ARG
     assert lib.mla_prefill_weights(small, FAKE, FAKE, FAKE, None) == bd.MLA_ERR_UNSUPPORTED
+
+
+def test_hip_error_detail_without_a_launch(lib):
+    # no call on this thread has failed a launch yet
+    assert lib.mla_last_hip_error() == 0
+    assert lib.mla_hip_error_name(0) == b"hipSuccess"
+    assert lib.mla_hip_error_name(100) == b"hipErrorNoDevice"
+    assert lib.mla_hip_error_name(98) == b"hipErrorInvalidDeviceFunction"
+    # an argument error is not a HIP error and leaves the record alone
+    assert lib.mla_decode(None, 2, 1, FAKE, FAKE, None, FAKE, 4, FAKE, FAKE, None) == bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_last_hip_error() == 0
+
+
+def test_binding_names_the_hip_error(monkeypatch):
+    # the binding turns MLA_ERR_HIP into a message that names the HIP error
+    class FakeLib:
+        def mla_status_string(self, s):
+            return b"HIP launch error"
+
+        def mla_last_hip_error(self):
+            return 98
+
+        def mla_hip_error_name(self, c):
+            return b"hipErrorInvalidDeviceFunction"
+    monkeypatch.setattr(bd, "load_library", lambda *a, **k: FakeLib())
+    with pytest.raises(bd.MlaError, match=r"hipErrorInvalidDeviceFunction \(98\)"):
+        bd._check("mla_decode", bd.MLA_ERR_HIP)
+
+
+def test_misaligned_vector_buffers_are_rejected(lib):
+    c = _cache()
+    d = ctypes.byref(V3)
+    odd16, odd8 = ctypes.c_void_p(0x10008), ctypes.c_void_p(0x10004)
+    base = [d, 2, 1, FAKE, FAKE, ctypes.byref(c), FAKE, 4, FAKE, FAKE, None]
+    for idx, bad in ((3, odd16), (4, odd16), (8, odd16), (9, odd8)):
+        args = list(base)
+        args[idx] = bad
+        assert lib.mla_decode(*args) == bd.MLA_ERR_INVALID_ARG, idx
+    # combine: u_part, u 16 bytes, lse_part 8 bytes
+    assert lib.mla_combine(d, 2, 1, FAKE, 4, odd16, FAKE, FAKE, None, None) == bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_combine(d, 2, 1, FAKE, 4, FAKE, odd8, FAKE, None, None) == bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_combine(d, 2, 1, FAKE, 4, FAKE, FAKE, odd16, None, None) == bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_out_proj(d, 2, 1, odd16, 1, FAKE, FAKE, None) == bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_out_proj(d, 2, 1, FAKE, 1, odd16, FAKE, None) == bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_combine_out_proj(d, 2, 1, FAKE, 4, odd16, FAKE, 1, FAKE, FAKE, None, None) == \
+        bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_combine_out_proj(d, 2, 1, FAKE, 4, FAKE, odd8, 1, FAKE, FAKE, None, None) == \
+        bd.MLA_ERR_INVALID_ARG
+
+
+def test_contiguous_stride_below_one_row_is_rejected(lib):
+    d = ctypes.byref(V3)
+    for stride in (0, 575, -1):
+        c = _cache(seq_stride=stride)
+        assert lib.mla_decode(d, 1, 1, FAKE, FAKE, ctypes.byref(c), FAKE, 4, FAKE, FAKE, None) == \
+            bd.MLA_ERR_INVALID_ARG, stride
+    # fp8 rows: the stride counts bytes, one row is 656 bytes at V3 dims
+    c = _cache(dtype=2, seq_stride=655)
+    assert lib.mla_decode(d, 1, 1, FAKE, FAKE, ctypes.byref(c), FAKE, 4, FAKE, FAKE, None) == bd.MLA_ERR_INVALID_ARG

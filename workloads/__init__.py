@@ -335,6 +335,8 @@ def _synth_lib():
             ctypes.c_uint32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p]
+        lib.synth_error_name.restype = ctypes.c_char_p
+        lib.synth_error_name.argtypes = [ctypes.c_int]
         _SYNTH_LIB = lib
     return _SYNTH_LIB
 
@@ -353,5 +355,8 @@ def fill_cache_rows_device(w: Workload, seq_ids_dev: int, tok_dev: int, n_tokens
         ctypes.c_uint32(w.seed), ctypes.c_int32(STREAM_CACHE), ctypes.c_int32(w.row),
         ctypes.c_int32(n_tokens), ctypes.c_void_p(seq_ids_dev), ctypes.c_void_p(tok_dev),
         ctypes.c_void_p(table_dev), ctypes.c_void_p(out_dev), ctypes.c_void_p(stream))
+    if rc == -1:
+        raise ValueError("synth_fill_cache_rows: invalid argument")
     if rc != 0:
-        raise RuntimeError(f"synth_fill_cache_rows failed with status {rc}")
+        name = _synth_lib().synth_error_name(rc).decode()
+        raise RuntimeError(f"synth_fill_cache_rows: launch failed with {name} ({rc})")

@@ -44,13 +44,17 @@ __global__ __launch_bounds__(64) void fill_rows_kernel(uint32_t seed, uint32_t s
 
 }  // namespace
 
+// Returns 0, -1 for an invalid argument, or the hipError_t of a failed launch
+// (synth_error_name gives its name).
 extern "C" int synth_fill_cache_rows(uint32_t seed, int32_t stream_id, int32_t row, int32_t n_tokens,
                                      const int32_t* seq_ids, const int32_t* tok, const uint16_t* table,
                                      uint16_t* out, void* stream) {
-  if (n_tokens < 0 || row <= 0 || !seq_ids || !tok || !table || !out) return 1;
+  if (n_tokens < 0 || row <= 0 || !seq_ids || !tok || !table || !out) return -1;
   if (n_tokens == 0) return 0;
   dim3 grid(n_tokens, (row / 8 + 63) / 64 + 1);
   hipLaunchKernelGGL(fill_rows_kernel, grid, dim3(64), 0, (hipStream_t)stream, seed, (uint32_t)stream_id,
                      row, n_tokens, seq_ids, tok, table, out);
-  return hipGetLastError() == hipSuccess ? 0 : 3;
+  return (int)hipGetLastError();
 }
+
+extern "C" const char* synth_error_name(int code) { return hipGetErrorName((hipError_t)code); }
