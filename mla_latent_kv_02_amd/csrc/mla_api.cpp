@@ -109,6 +109,38 @@ mla_status_t launch_absorb_any(const mla::AbsorbParams& p, hipStream_t stream) {
   return from_hip(mla::launch_absorb(p, stream));
 }
 
+// Checks the arguments of mla_decode other than the partials and fills *p
+// (p->B == 0: nothing to do; u_part and lse_part are left for the caller).
+mla_status_t decode_args(const mla_dims_t* dims, int32_t B, int32_t n_q, const void* q_lat, const void* q_pe,
+                         const mla_cache_t* cache, const int32_t* positions, int32_t num_splits,
+                         mla::DecodeParams* p) {
+  if (!dims_ok(dims) || B < 0 || n_q < 1 || num_splits < 1 || num_splits > kMaxSplits)
+    return MLA_ERR_INVALID_ARG;
+  p->B = 0;
+  if (B == 0) return MLA_OK;
+  if (!q_lat || !q_pe || !positions || !cache_ok(cache, dims)) return MLA_ERR_INVALID_ARG;
+  // the kernels read q_lat and q_pe in 16-byte vectors
+  if (!al16(q_lat) || !al16(q_pe)) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)n_q * dims->n_h > 65535) return MLA_ERR_UNSUPPORTED;
+  p->q_lat = q_lat; p->q_pe = q_pe; p->cache = view_of(cache, dims); p->ctx_lens = cache->ctx_lens;
+  p->positions = positions; p->u_part = nullptr; p->lse_part = nullptr;
+  p->B = B; p->n_q = n_q; p->n_h = dims->n_h; p->d_c = dims->d_c; p->d_rope = dims->d_rope;
+  p->num_splits = num_splits; p->bf16 = cache->dtype == MLA_BF16; p->fp8 = cache->dtype == MLA_FP8_E4M3;
+  p->sm_scale = scale_of(dims);
+  if (!((p->bf16 || p->fp8) && p->d_c == 512 && p->d_rope == 64 && p->n_h % 32 == 0) &&
+      (p->d_c + p->d_rope > 2048 || p->d_c > 1024))
+    return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+// The decode kernel for the shapes of p: the MFMA kernel for the V3 row (bf16
+// or fp8 cache), the generic one otherwise.
+mla_status_t launch_decode_any(const mla::DecodeParams& p, hipStream_t stream) {
+  const bool fast = (p.bf16 || p.fp8) && p.d_c == 512 && p.d_rope == 64 && p.n_h % 32 == 0;
+  if (fast) return from_hip(mla::launch_decode_mfma(p, stream));
+  return from_hip(mla::launch_decode_generic(p, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -152,24 +184,15 @@ mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t B, int32_t n_q, mla_dt
 mla_status_t mla_decode(const mla_dims_t* dims, int32_t B, int32_t n_q, const void* q_lat,
                         const void* q_pe, const mla_cache_t* cache, const int32_t* positions,
                         int32_t num_splits, float* u_part, float* lse_part, void* stream) {
-  if (!dims_ok(dims) || B < 0 || n_q < 1 || num_splits < 1 || num_splits > kMaxSplits)
-    return MLA_ERR_INVALID_ARG;
-  if (B == 0) return MLA_OK;
-  if (!q_lat || !q_pe || !positions || !u_part || !lse_part || !cache_ok(cache, dims))
-    return MLA_ERR_INVALID_ARG;
-  // the kernels move q_lat, q_pe and u_part in 16-byte vectors, lse_part in pairs
-  if (!al16(q_lat) || !al16(q_pe) || !al16(u_part) || !al8(lse_part)) return MLA_ERR_INVALID_ARG;
-  if ((int64_t)n_q * dims->n_h > 65535) return MLA_ERR_UNSUPPORTED;
   mla::DecodeParams p;
-  p.q_lat = q_lat; p.q_pe = q_pe; p.cache = view_of(cache, dims); p.ctx_lens = cache->ctx_lens;
-  p.positions = positions; p.u_part = u_part; p.lse_part = lse_part;
-  p.B = B; p.n_q = n_q; p.n_h = dims->n_h; p.d_c = dims->d_c; p.d_rope = dims->d_rope;
-  p.num_splits = num_splits; p.bf16 = cache->dtype == MLA_BF16; p.fp8 = cache->dtype == MLA_FP8_E4M3;
-  p.sm_scale = scale_of(dims);
-  const bool fast = (p.bf16 || p.fp8) && p.d_c == 512 && p.d_rope == 64 && p.n_h % 32 == 0;
-  if (fast) return from_hip(mla::launch_decode_mfma(p, (hipStream_t)stream));
-  if (p.d_c + p.d_rope > 2048 || p.d_c > 1024) return MLA_ERR_UNSUPPORTED;
-  return from_hip(mla::launch_decode_generic(p, (hipStream_t)stream));
+  const mla_status_t st = decode_args(dims, B, n_q, q_lat, q_pe, cache, positions, num_splits, &p);
+  if (st != MLA_OK || p.B == 0) return st;
+  if (!u_part || !lse_part) return MLA_ERR_INVALID_ARG;
+  // the kernels store u_part in 16-byte vectors, lse_part in pairs
+  if (!al16(u_part) || !al8(lse_part)) return MLA_ERR_INVALID_ARG;
+  p.u_part = u_part;
+  p.lse_part = lse_part;
+  return launch_decode_any(p, (hipStream_t)stream);
 }
 
 mla_status_t mla_combine(const mla_dims_t* dims, int32_t B, int32_t n_q, const int32_t* ctx_lens,
