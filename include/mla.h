@@ -44,9 +44,10 @@
  *     max_blocks * block_size, as empty (its partial is u = 0, lse = -inf);
  *     an append skips a row whose block is missing (negative id) or lies
  *     past max_blocks.
- *   - The only mutable state is the per-thread record behind
- *     mla_last_hip_error(); concurrent calls on different streams are safe
- *     when their output buffers do not overlap.
+ *   - Mutable state: the per-thread record behind mla_last_hip_error(), and
+ *     the per-GPU scratch of mla_decode_out_noalloc (see there); other
+ *     concurrent calls on different streams are safe when their output
+ *     buffers do not overlap.
  */
 #ifndef MLA_H
 #define MLA_H
@@ -62,7 +63,8 @@ typedef enum {
   MLA_ERR_INVALID_ARG = 1,
   MLA_ERR_UNSUPPORTED = 2,
   MLA_ERR_HIP = 3,
-  MLA_ERR_OUT_OF_BLOCKS = 4    /* block pool: not enough free blocks */
+  MLA_ERR_OUT_OF_BLOCKS = 4,   /* block pool: not enough free blocks */
+  MLA_ERR_TOO_LARGE = 5         /* mla_decode_out_noalloc: the input needs more than its fixed scratch */
 } mla_status_t;
 
 /* MLA_FP8_E4M3 is a cache dtype only (see mla_cache_t); queries, weights and
@@ -335,6 +337,32 @@ mla_status_t mla_block_pool_release(void *pool, int32_t b);
 const int32_t *mla_block_pool_table(const void *pool);
 /* Number of free blocks (-1 if pool is not one). */
 int32_t mla_block_pool_free_count(const void *pool);
+
+/* ---- The decode step for callers that cannot allocate (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same work and results as mla_decode followed by mla_combine_out_proj, with
+ * the split-KV partials in device memory the library holds instead of
+ * caller-provided u_part / lse_part.  It calls no allocator.
+ *   - Arguments as for mla_decode (q_lat, q_pe, cache, positions, num_splits)
+ *     and mla_combine_out_proj (w_dt, w_uv, out, lse; lse may be NULL).
+ *     Compiled for what mla_combine_out_proj covers (bf16 weights, d_c = 512,
+ *     d_v = 128); other shapes return MLA_ERR_UNSUPPORTED.
+ *   - With rows = (num_splits + B - 1) * n_q * n_h partial rows, the
+ *     partials take 4 d_c * rows bytes rounded up to a multiple of 256, plus
+ *     8 * rows; more than MLA_NOALLOC_SCRATCH_BYTES (128 MiB) returns
+ *     MLA_ERR_TOO_LARGE before anything is enqueued.  At V3 shapes that is
+ *     510 partial slots for n_q * n_h = 128 (num_splits 256 with B up to 255),
+ *     255 for n_q * n_h = 256.
+ *   - One scratch per GPU, shared by every call on that GPU and kept until the
+ *     process ends (the first call on a device looks up its address there).
+ *     It keeps the last call's contents, and nothing in it needs to start at
+ *     zero.  Calls that overlap on one GPU (different streams, or host
+ *     threads without ordering) race on it: order them. */
+#define MLA_NOALLOC_SCRATCH_BYTES (128LL << 20)
+mla_status_t mla_decode_out_noalloc(const mla_dims_t *dims, int32_t B, int32_t n_q, const void *q_lat,
+                                    const void *q_pe, const mla_cache_t *cache, const int32_t *positions,
+                                    int32_t num_splits, mla_dtype_t w_dt, const void *w_uv, float *out,
+                                    float *lse, void *stream);
 
 /* Static description of a status code. */
 const char *mla_status_string(mla_status_t status);

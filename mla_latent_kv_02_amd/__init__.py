@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     mla_num_partials,
     mla_out_proj,
     mla_combine_out_proj,
+    mla_decode_out_noalloc,
     mla_fold_out,
     mla_out_proj_folded,
     mla_o_proj,

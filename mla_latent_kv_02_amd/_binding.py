@@ -16,12 +16,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # comparing kernel variants).  Either way the HIP library is required.
 LIB_PATH = os.environ.get("MLA_LIBRARY") or os.path.join(HERE, "libmla.so")
 
-MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP, MLA_ERR_OUT_OF_BLOCKS = 0, 1, 2, 3, 4
+MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP, MLA_ERR_OUT_OF_BLOCKS, MLA_ERR_TOO_LARGE = 0, 1, 2, 3, 4, 5
+NOALLOC_SCRATCH_BYTES = 128 << 20     # MLA_NOALLOC_SCRATCH_BYTES
 F32, BF16, FP8_E4M3 = 0, 1, 2
 
 EXPORTED = ("mla_absorb_q", "mla_decode", "mla_combine", "mla_out_proj", "mla_combine_out_proj",
             "mla_cache_append", "mla_append_absorb_q", "mla_num_partials", "mla_cache_row_bytes",
             "mla_status_string", "mla_version", "mla_last_hip_error", "mla_hip_error_name",
+            "mla_decode_out_noalloc",
             "mla_block_pool_bytes", "mla_block_pool_init", "mla_block_pool_reserve", "mla_block_pool_reserve_all",
             "mla_block_pool_release", "mla_fold_out", "mla_out_proj_folded", "mla_o_proj", "mla_fold_q",
             "mla_absorb_q_folded", "mla_prefill_weights", "mla_prefill_workspace_bytes", "mla_prefill",
@@ -66,6 +68,7 @@ def load_library(path: str = LIB_PATH):
         "mla_combine": [DP, I32, I32, P, I32, P, P, P, P, V],
         "mla_out_proj": [DP, I32, I32, P, ctypes.c_int, P, P, V],
         "mla_combine_out_proj": [DP, I32, I32, P, I32, P, P, ctypes.c_int, P, P, P, V],
+        "mla_decode_out_noalloc": [DP, I32, I32, P, P, CP, P, I32, ctypes.c_int, P, P, P, V],
         "mla_cache_append": [DP, CP, I32, P, P, P, I64, P, I64, V],
         "mla_append_absorb_q": [DP, CP, I32, P, P, P, I64, P, I64, I32, I32, ctypes.c_int, P, P, P, P, P, P, V],
         "mla_fold_out": [DP, I32, P, P, P, V],
@@ -331,6 +334,37 @@ def mla_combine_out_proj(dims: Dims, ctx_lens, num_splits: int, u_part, lse_part
     _check("mla_combine_out_proj", load_library().mla_combine_out_proj(
         ctypes.byref(d), B, n_q, ctx_lens.data_ptr(), num_splits, u_part.data_ptr(), lse_part.data_ptr(),
         _dtype(w_uv), w_uv.data_ptr(), out.data_ptr(), None if lse is None else lse.data_ptr(), _stream(stream)))
+
+
+def mla_decode_out_noalloc(dims: Dims, q_lat, q_pe, cache: LatentCache, positions, num_splits: int, w_uv, out,
+                           lse=None, stream=None) -> None:
+    """mla_decode then mla_combine_out_proj with the partials in the
+    library's own per-GPU scratch (no buffer of the caller's, no allocation)."""
+    B, n_q = q_lat.shape[0], q_lat.shape[1]
+    torch = _torch()
+    _dev(q_lat, "q_lat", cache.query_dtype)
+    _dev(q_pe, "q_pe", cache.query_dtype)
+    _dev(positions, "positions", torch.int32)
+    _dev(out, "out", torch.float32)
+    _dev(w_uv, "w_uv")
+    _shape(q_lat, "q_lat", (B, n_q, dims.n_h, dims.d_c))
+    _shape(q_pe, "q_pe", (B, n_q, dims.n_h, dims.d_rope))
+    _shape(positions, "positions", (B, n_q))
+    _shape(cache.ctx_lens, "cache.ctx_lens", (B,))
+    _shape(w_uv, "w_uv", (dims.n_h, dims.d_c, dims.d_v))
+    _shape(out, "out", (B, n_q, dims.n_h, dims.d_v))
+    if cache.data.shape[-1] != cache.row_width(dims):
+        raise ValueError(f"cache rows must be {cache.row_width(dims)} wide")
+    if cache.block_size == 0 and cache.data.shape[0] < B:
+        raise ValueError("contiguous cache holds fewer sequences than B")
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+        _shape(lse, "lse", (B, n_q, dims.n_h))
+    d, c = dims._c(), cache._c()
+    _check("mla_decode_out_noalloc", load_library().mla_decode_out_noalloc(
+        ctypes.byref(d), B, n_q, q_lat.data_ptr(), q_pe.data_ptr(), ctypes.byref(c), positions.data_ptr(),
+        num_splits, _dtype(w_uv), w_uv.data_ptr(), out.data_ptr(), None if lse is None else lse.data_ptr(),
+        _stream(stream)))
 
 
 def mla_cache_append(dims: Dims, cache: LatentCache, seq_ids, positions, c_kv_new, k_rope_new,

@@ -3,7 +3,9 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <atomic>
 #include <climits>
+#include <mutex>
 
 #include "../../include/mla.h"
 #include "launch.h"
@@ -152,6 +154,7 @@ const char* mla_status_string(mla_status_t s) {
     case MLA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case MLA_ERR_HIP: return "HIP launch error";
     case MLA_ERR_OUT_OF_BLOCKS: return "block pool has too few free blocks";
+    case MLA_ERR_TOO_LARGE: return "input needs more than the fixed scratch of the no-allocation entry point";
   }
   return "unknown status";
 }
@@ -412,6 +415,73 @@ mla_status_t mla_absorb_q_folded(const mla_dims_t* dims, int32_t d_q, int32_t B,
   p.B = B; p.n_q = n_q; p.n_h = n_h; p.d_c = d_c; p.d_rope = dims->d_rope; p.d_nope = dims->d_nope;
   p.bf16 = true; p.rope_base = base_of(dims);
   return from_hip(mla::launch_rope_q(p, (hipStream_t)stream));
+}
+
+// ---- the decode step without allocation (mla_decode_out_noalloc)
+namespace {
+// The split-KV partials of mla_decode_out_noalloc: u_part, then lse_part at
+// the next 256-byte boundary.  One copy per GPU, in device memory that the
+// library's code object holds until the process ends.  In host code the name
+// `scratch` is a host-side stand-in, not a device address: what the kernels
+// get is the address hipGetSymbolAddress returns on the current device.
+constexpr size_t kScratchBytes = (size_t)MLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];   // per device, set once
+std::mutex g_scratch_mutex;
+
+// The device address of `scratch` on the current device, looked up (with that
+// device current) on the first call there.
+hipError_t scratch_on_current_device(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
+}
+}  // namespace
+
+mla_status_t mla_decode_out_noalloc(const mla_dims_t* dims, int32_t B, int32_t n_q, const void* q_lat,
+                                    const void* q_pe, const mla_cache_t* cache, const int32_t* positions,
+                                    int32_t num_splits, mla_dtype_t w_dt, const void* w_uv, float* out,
+                                    float* lse, void* stream) {
+  mla::DecodeParams p;
+  mla_status_t st = decode_args(dims, B, n_q, q_lat, q_pe, cache, positions, num_splits, &p);
+  if (st != MLA_OK || p.B == 0) return st;
+  if (!dtype_ok(w_dt) || !w_uv || !out || !al16(w_uv)) return MLA_ERR_INVALID_ARG;
+  if (!mla::tail_mfma_ok(dims->d_c, dims->d_v, w_dt == MLA_BF16)) return MLA_ERR_UNSUPPORTED;
+  // partial rows of the plan; u_part rows of d_c fp32, lse_part rows of 2 fp32
+  const int64_t rows = ((int64_t)num_splits + B - 1) * n_q * dims->n_h;
+  const int64_t u_bytes = (rows * dims->d_c * 4 + 255) / 256 * 256;
+  if (u_bytes + rows * 2 * 4 > (int64_t)kScratchBytes) return MLA_ERR_TOO_LARGE;
+  void* base = nullptr;
+  st = from_hip(scratch_on_current_device(&base));
+  if (st != MLA_OK) return st;
+  p.u_part = static_cast<float*>(base);
+  p.lse_part = reinterpret_cast<float*>(static_cast<unsigned char*>(base) + u_bytes);
+  const hipStream_t s = (hipStream_t)stream;
+  st = launch_decode_any(p, s);
+  if (st != MLA_OK) return st;
+  // every partial the merge reads was written by the decode above: nothing in
+  // the scratch has to start at zero
+  mla::TailParams t{};
+  t.ctx_lens = cache->ctx_lens; t.u_part = p.u_part; t.lse_part = p.lse_part; t.w_uv = w_uv; t.out = out;
+  t.lse = lse; t.B = B; t.n_q = n_q; t.n_h = dims->n_h; t.d_c = dims->d_c; t.d_v = dims->d_v;
+  t.num_splits = num_splits;
+  return from_hip(mla::launch_tail_mfma(t, true, s));
 }
 
 }  // extern "C"

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    for code in range(5):
+    for code in range(6):
         assert lib.mla_status_string(code)
     assert b"unknown" in lib.mla_status_string(99)
     assert b"gfx950" in lib.mla_version()
@@ -284,3 +284,22 @@ def test_contiguous_stride_below_one_row_is_rejected(lib):
     # fp8 rows: the stride counts bytes, one row is 656 bytes at V3 dims
     c = _cache(dtype=2, seq_stride=655)
     assert lib.mla_decode(d, 1, 1, FAKE, FAKE, ctypes.byref(c), FAKE, 4, FAKE, FAKE, None) == bd.MLA_ERR_INVALID_ARG
+
+
+def test_noalloc_rejects_inputs_beyond_its_scratch(lib):
+    # host-side size check, before any HIP call: (num_splits + B - 1) partial
+    # slots of n_q * n_h rows beyond MLA_NOALLOC_SCRATCH_BYTES
+    c = _cache()
+    d = ctypes.byref(V3)
+    args = lambda B, ns: (d, B, 1, FAKE, FAKE, ctypes.byref(c), FAKE, ns, 1, FAKE, FAKE, None, None)
+    assert lib.mla_decode_out_noalloc(*args(2, 1 << 20)) == bd.MLA_ERR_TOO_LARGE
+    assert lib.mla_decode_out_noalloc(*args(2, 510)) == bd.MLA_ERR_TOO_LARGE     # 511 slots of 128 rows
+    assert lib.mla_status_string(bd.MLA_ERR_TOO_LARGE).startswith(b"input needs more")
+    # argument errors come first, as for mla_decode / mla_combine_out_proj
+    assert lib.mla_decode_out_noalloc(d, 2, 1, FAKE, FAKE, ctypes.byref(c), FAKE, 4, 1, None, FAKE, None, None) == \
+        bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_out_noalloc(d, 2, 1, FAKE, FAKE, ctypes.byref(c), FAKE, 4, 1, FAKE, None, None, None) == \
+        bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_out_noalloc(d, 2, 1, FAKE, FAKE, ctypes.byref(c), FAKE, 0, 1, FAKE, FAKE, None, None) == \
+        bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_out_noalloc(d, 0, 1, None, None, ctypes.byref(c), None, 4, 1, None, None, None, None) == 0
