@@ -54,21 +54,27 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False, jobs: int = 4) -> None:
+def build(verbose: bool = False, jobs: int = 4, lib_path: str = LIB, host_flags=(), synth: bool = True) -> None:
+    """Compile libmla.so (to ``lib_path``) and, with ``synth``, libmla_synth.so.
+    ``host_flags`` go to the host side of every compile and the link (each one
+    behind -Xarch_host, e.g. sanitizers for a host-checking build)."""
     hipcc = _hipcc()
+    host = [x for f in host_flags for x in ("-Xarch_host", f)]
     with tempfile.TemporaryDirectory(prefix="mla_build_") as tmp:
         def compile_one(src):
             obj = os.path.join(tmp, os.path.basename(src) + ".o")
             lang = ["-x", "hip"] if src.endswith(".cpp") else []
-            _run([hipcc, *DEVICE_FLAGS, *EXTRA_FLAGS.get(src, []), *lang, "-I", CSRC,
+            _run([hipcc, *DEVICE_FLAGS, *EXTRA_FLAGS.get(src, []), *host, *lang, "-I", CSRC,
                   "-I", os.path.join(ROOT, "include"),
                   "-c", os.path.join(CSRC, src), "-o", obj])
             return obj
         with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
             objs = list(ex.map(compile_one, SOURCES))
-        tmp_lib = LIB + ".tmp"
-        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_lib, *objs])
-        os.replace(tmp_lib, LIB)
+        tmp_lib = lib_path + ".tmp"
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *host, "-o", tmp_lib, *objs])
+        os.replace(tmp_lib, lib_path)
+        if not synth:
+            return
         synth_obj = os.path.join(tmp, "synth.o")
         _run([hipcc, *DEVICE_FLAGS, "-c", SYNTH_SRC, "-o", synth_obj])
         tmp_synth = SYNTH_LIB + ".tmp"

@@ -5,6 +5,7 @@
 #include <stdint.h>
 #include <atomic>
 #include <climits>
+#include <cstring>
 #include <mutex>
 
 #include "../../include/mla.h"
@@ -20,10 +21,22 @@ bool dims_ok(const mla_dims_t* d) {
          d->d_rope <= (1 << 16) && d->d_nope <= (1 << 16) && d->d_v <= (1 << 16) &&
          isfinite(d->sm_scale) && d->sm_scale >= 0.f && isfinite(d->rope_base) && d->rope_base >= 0.f;
 }
-bool dtype_ok(mla_dtype_t t) { return t == MLA_F32 || t == MLA_BF16; }
-bool cache_dtype_ok(mla_dtype_t t) { return dtype_ok(t) || t == MLA_FP8_E4M3; }
+// The value of an enum argument as the integer the caller passed: a C caller
+// may pass any int, and reading one outside the enumerators' range as the
+// enum type is undefined in C++, so enums from the ABI are only compared as
+// integers.
+template <typename E>
+int32_t as_int(const E& e) {
+  static_assert(sizeof(E) == sizeof(int32_t), "ABI enums are 32-bit");
+  int32_t v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+
+bool dtype_ok(int32_t t) { return t == MLA_F32 || t == MLA_BF16; }
+bool cache_dtype_ok(int32_t t) { return dtype_ok(t) || t == MLA_FP8_E4M3; }
 // bytes of one cache row; -1 if the dtype does not fit the dims
-int64_t row_bytes(const mla_dims_t* d, mla_dtype_t t) {
+int64_t row_bytes(const mla_dims_t* d, int32_t t) {
   if (t == MLA_FP8_E4M3) return d->d_c % 128 ? -1 : (int64_t)d->d_c + 2 * d->d_rope + 4 * (d->d_c / 128);
   if (t == MLA_BF16) return 2 * (int64_t)(d->d_c + d->d_rope);
   if (t == MLA_F32) return 4 * (int64_t)(d->d_c + d->d_rope);
@@ -35,15 +48,15 @@ float scale_of(const mla_dims_t* d) {
 float base_of(const mla_dims_t* d) { return d->rope_base > 0.f ? d->rope_base : 10000.0f; }
 
 bool cache_ok(const mla_cache_t* c, const mla_dims_t* d) {
-  if (!c || !c->data || !c->ctx_lens || !cache_dtype_ok(c->dtype)) return false;
-  const int64_t rb = row_bytes(d, c->dtype);
+  if (!c || !c->data || !c->ctx_lens || !cache_dtype_ok(as_int(c->dtype))) return false;
+  const int64_t rb = row_bytes(d, as_int(c->dtype));
   if (rb < 0) return false;
   if (reinterpret_cast<uintptr_t>(c->data) % 16) return false;
   if (c->block_size < 0) return false;
   if (c->block_size > 0) return c->block_table && c->max_blocks >= 1;
   // contiguous: a sequence holds at least one row (seq_stride counts elements,
   // bytes for fp8 rows)
-  const int64_t row_units = c->dtype == MLA_FP8_E4M3 ? rb : d->d_c + d->d_rope;
+  const int64_t row_units = as_int(c->dtype) == MLA_FP8_E4M3 ? rb : d->d_c + d->d_rope;
   return c->seq_stride >= row_units;
 }
 
@@ -55,7 +68,7 @@ mla::CacheView view_of(const mla_cache_t* c, const mla_dims_t* d) {
   v.block_size = c->block_size;
   v.max_blocks = c->max_blocks;
   // elements per row; for fp8 rows (mixed element types) the unit is the byte
-  v.row = c->dtype == MLA_FP8_E4M3 ? (int32_t)row_bytes(d, c->dtype) : d->d_c + d->d_rope;
+  v.row = as_int(c->dtype) == MLA_FP8_E4M3 ? (int32_t)row_bytes(d, MLA_FP8_E4M3) : d->d_c + d->d_rope;
   return v;
 }
 
@@ -71,7 +84,7 @@ bool al16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 bool al8(const void* p) { return reinterpret_cast<uintptr_t>(p) % 8 == 0; }
 
 // Checks the arguments of mla_absorb_q and fills *p (p->B == 0: nothing to do).
-mla_status_t absorb_args(const mla_dims_t* dims, int32_t B, int32_t n_q, mla_dtype_t dt, const void* q_nope,
+mla_status_t absorb_args(const mla_dims_t* dims, int32_t B, int32_t n_q, int32_t dt, const void* q_nope,
                          const void* q_rope, const int32_t* positions, const void* w_uk, void* q_lat, void* q_pe,
                          mla::AbsorbParams* p) {
   if (!dims_ok(dims) || B < 0 || n_q < 1 || !dtype_ok(dt)) return MLA_ERR_INVALID_ARG;
@@ -100,8 +113,8 @@ mla_status_t append_args(const mla_dims_t* dims, const mla_cache_t* cache, int32
   p->cache_data = cache->data;
   p->n = n; p->seq_ids = seq_ids; p->positions = positions;
   p->c_kv = c_kv_new; p->c_kv_stride = c_kv_stride; p->k_rope = k_rope_new; p->k_rope_stride = k_rope_stride;
-  p->d_c = dims->d_c; p->d_rope = dims->d_rope; p->bf16 = cache->dtype == MLA_BF16;
-  p->fp8 = cache->dtype == MLA_FP8_E4M3;
+  p->d_c = dims->d_c; p->d_rope = dims->d_rope; p->bf16 = as_int(cache->dtype) == MLA_BF16;
+  p->fp8 = as_int(cache->dtype) == MLA_FP8_E4M3;
   p->rope_base = base_of(dims);
   return MLA_OK;
 }
@@ -127,7 +140,8 @@ mla_status_t decode_args(const mla_dims_t* dims, int32_t B, int32_t n_q, const v
   p->q_lat = q_lat; p->q_pe = q_pe; p->cache = view_of(cache, dims); p->ctx_lens = cache->ctx_lens;
   p->positions = positions; p->u_part = nullptr; p->lse_part = nullptr;
   p->B = B; p->n_q = n_q; p->n_h = dims->n_h; p->d_c = dims->d_c; p->d_rope = dims->d_rope;
-  p->num_splits = num_splits; p->bf16 = cache->dtype == MLA_BF16; p->fp8 = cache->dtype == MLA_FP8_E4M3;
+  p->num_splits = num_splits; p->bf16 = as_int(cache->dtype) == MLA_BF16;
+  p->fp8 = as_int(cache->dtype) == MLA_FP8_E4M3;
   p->sm_scale = scale_of(dims);
   if (!((p->bf16 || p->fp8) && p->d_c == 512 && p->d_rope == 64 && p->n_h % 32 == 0) &&
       (p->d_c + p->d_rope > 2048 || p->d_c > 1024))
@@ -148,7 +162,7 @@ mla_status_t launch_decode_any(const mla::DecodeParams& p, hipStream_t stream) {
 extern "C" {
 
 const char* mla_status_string(mla_status_t s) {
-  switch (s) {
+  switch (as_int(s)) {
     case MLA_OK: return "ok";
     case MLA_ERR_INVALID_ARG: return "invalid argument";
     case MLA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
@@ -163,11 +177,16 @@ const char* mla_version(void) { return "mla-mi355x 0.2.0 (gfx950)"; }
 
 int32_t mla_last_hip_error(void) { return (int32_t)t_last_hip_error; }
 
-const char* mla_hip_error_name(int32_t code) { return hipGetErrorName((hipError_t)code); }
+const char* mla_hip_error_name(int32_t code) {
+  // hipError_t's enumerators span 0 .. 1054, so its values are 0 .. 2047; an
+  // integer outside that is no hipError_t at all
+  if (code < 0 || code > 2047) return "not a HIP error code";
+  return hipGetErrorName(static_cast<hipError_t>(code));
+}
 
 int64_t mla_cache_row_bytes(const mla_dims_t* dims, mla_dtype_t dtype) {
-  if (!dims_ok(dims) || !cache_dtype_ok(dtype)) return -1;
-  return row_bytes(dims, dtype);
+  if (!dims_ok(dims) || !cache_dtype_ok(as_int(dtype))) return -1;
+  return row_bytes(dims, as_int(dtype));
 }
 
 int64_t mla_num_partials(int32_t B, int32_t num_splits) {
@@ -179,7 +198,7 @@ mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t B, int32_t n_q, mla_dt
                           const void* q_nope, const void* q_rope, const int32_t* positions,
                           const void* w_uk, void* q_lat, void* q_pe, void* stream) {
   mla::AbsorbParams p;
-  const mla_status_t st = absorb_args(dims, B, n_q, dt, q_nope, q_rope, positions, w_uk, q_lat, q_pe, &p);
+  const mla_status_t st = absorb_args(dims, B, n_q, as_int(dt), q_nope, q_rope, positions, w_uk, q_lat, q_pe, &p);
   if (st != MLA_OK || p.B == 0) return st;
   return launch_absorb_any(p, (hipStream_t)stream);
 }
@@ -215,7 +234,7 @@ mla_status_t mla_combine(const mla_dims_t* dims, int32_t B, int32_t n_q, const i
 
 mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t B, int32_t n_q, const float* u,
                           mla_dtype_t w_dt, const void* w_uv, float* out, void* stream) {
-  if (!dims_ok(dims) || B < 0 || n_q < 1 || !dtype_ok(w_dt)) return MLA_ERR_INVALID_ARG;
+  if (!dims_ok(dims) || B < 0 || n_q < 1 || !dtype_ok(as_int(w_dt))) return MLA_ERR_INVALID_ARG;
   if (B == 0) return MLA_OK;
   if (!u || !w_uv || !out) return MLA_ERR_INVALID_ARG;
   if (!al16(u) || !al16(w_uv)) return MLA_ERR_INVALID_ARG;
@@ -223,7 +242,7 @@ mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t B, int32_t n_q, const 
   mla::OutProjParams p;
   p.u = u; p.w_uv = w_uv; p.out = out;
   p.B = B; p.n_q = n_q; p.n_h = dims->n_h; p.d_c = dims->d_c; p.d_v = dims->d_v;
-  p.bf16 = w_dt == MLA_BF16;
+  p.bf16 = as_int(w_dt) == MLA_BF16;
   if (mla::tail_mfma_ok(p.d_c, p.d_v, p.bf16)) {
     mla::TailParams t{};
     t.u = u; t.w_uv = w_uv; t.out = out;
@@ -237,12 +256,12 @@ mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t B, int32_t n_q, const 
 mla_status_t mla_combine_out_proj(const mla_dims_t* dims, int32_t B, int32_t n_q, const int32_t* ctx_lens,
                                   int32_t num_splits, const float* u_part, const float* lse_part,
                                   mla_dtype_t w_dt, const void* w_uv, float* out, float* lse, void* stream) {
-  if (!dims_ok(dims) || B < 0 || n_q < 1 || num_splits < 1 || num_splits > kMaxSplits || !dtype_ok(w_dt))
+  if (!dims_ok(dims) || B < 0 || n_q < 1 || num_splits < 1 || num_splits > kMaxSplits || !dtype_ok(as_int(w_dt)))
     return MLA_ERR_INVALID_ARG;
   if (B == 0) return MLA_OK;
   if (!ctx_lens || !u_part || !lse_part || !w_uv || !out) return MLA_ERR_INVALID_ARG;
   if (!al16(u_part) || !al8(lse_part) || !al16(w_uv)) return MLA_ERR_INVALID_ARG;
-  if (!mla::tail_mfma_ok(dims->d_c, dims->d_v, w_dt == MLA_BF16)) return MLA_ERR_UNSUPPORTED;
+  if (!mla::tail_mfma_ok(dims->d_c, dims->d_v, as_int(w_dt) == MLA_BF16)) return MLA_ERR_UNSUPPORTED;
   mla::TailParams p{};
   p.ctx_lens = ctx_lens; p.u_part = u_part; p.lse_part = lse_part; p.w_uv = w_uv; p.out = out; p.lse = lse;
   p.B = B; p.n_q = n_q; p.n_h = dims->n_h; p.d_c = dims->d_c; p.d_v = dims->d_v; p.num_splits = num_splits;
@@ -271,7 +290,7 @@ mla_status_t mla_append_absorb_q(const mla_dims_t* dims, const mla_cache_t* cach
   mla_status_t st = append_args(dims, cache, n, seq_ids, new_positions, c_kv_new, c_kv_stride, k_rope_new,
                                 k_rope_stride, &ap);
   if (st != MLA_OK) return st;
-  st = absorb_args(dims, B, n_q, dt, q_nope, q_rope, positions, w_uk, q_lat, q_pe, &p);
+  st = absorb_args(dims, B, n_q, as_int(dt), q_nope, q_rope, positions, w_uk, q_lat, q_pe, &p);
   if (st != MLA_OK) return st;
   const hipStream_t s = (hipStream_t)stream;
   if (p.B > 0 && mla::absorb_mfma_ok(p)) return from_hip(mla::launch_append_absorb_mfma(p, &ap, s));
@@ -312,7 +331,7 @@ mla_status_t mla_prefill(const mla_dims_t* dims, int32_t B, int32_t n_q, int32_t
     return MLA_ERR_INVALID_ARG;
   if (workspace_bytes < mla_prefill_workspace_bytes(dims, B, max_ctx) || !al16(workspace))
     return MLA_ERR_INVALID_ARG;
-  if (!prefill_dims_ok(dims) || cache->dtype != MLA_BF16 || cache->block_size != 0) return MLA_ERR_UNSUPPORTED;
+  if (!prefill_dims_ok(dims) || as_int(cache->dtype) != MLA_BF16 || cache->block_size != 0) return MLA_ERR_UNSUPPORTED;
   if (cache->seq_stride < (int64_t)max_ctx * (dims->d_c + dims->d_rope)) return MLA_ERR_INVALID_ARG;
   const int64_t kv_tok = (int64_t)dims->n_h * (dims->d_nope + dims->d_v) * 2;
   if ((int64_t)(max_ctx + 64) * kv_tok >= (1LL << 32) || (int64_t)(max_ctx + 64) * (dims->d_c + dims->d_rope) * 2 >=
@@ -461,8 +480,8 @@ mla_status_t mla_decode_out_noalloc(const mla_dims_t* dims, int32_t B, int32_t n
   mla::DecodeParams p;
   mla_status_t st = decode_args(dims, B, n_q, q_lat, q_pe, cache, positions, num_splits, &p);
   if (st != MLA_OK || p.B == 0) return st;
-  if (!dtype_ok(w_dt) || !w_uv || !out || !al16(w_uv)) return MLA_ERR_INVALID_ARG;
-  if (!mla::tail_mfma_ok(dims->d_c, dims->d_v, w_dt == MLA_BF16)) return MLA_ERR_UNSUPPORTED;
+  if (!dtype_ok(as_int(w_dt)) || !w_uv || !out || !al16(w_uv)) return MLA_ERR_INVALID_ARG;
+  if (!mla::tail_mfma_ok(dims->d_c, dims->d_v, as_int(w_dt) == MLA_BF16)) return MLA_ERR_UNSUPPORTED;
   // partial rows of the plan; u_part rows of d_c fp32, lse_part rows of 2 fp32
   const int64_t rows = ((int64_t)num_splits + B - 1) * n_q * dims->n_h;
   const int64_t u_bytes = (rows * dims->d_c * 4 + 255) / 256 * 256;
