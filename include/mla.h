@@ -35,10 +35,14 @@
  *     (each entry point names them; MLA_ERR_INVALID_ARG otherwise).  Buffers
  *     from a device allocator are; an offset view may not be.
  *   - Device-side contents (context lengths, positions, block ids) are the
- *     caller's contract and are not checked on the host: ctx_lens[b] >= n_q,
- *     positions[b][j] = ctx_lens[b] - n_q + j for decode, block ids in
- *     [0, number of blocks), ctx_lens[b] <= max_blocks * block_size (paged)
- *     or ctx_lens[b] * row <= seq_stride (contiguous).  The kernels keep
+ *     caller's contract and are not checked on the host: 0 <= ctx_lens[b] <=
+ *     max_blocks * block_size (paged) or ctx_lens[b] * row <= seq_stride
+ *     (contiguous); the id of every block holding one of a sequence's first
+ *     ctx_lens[b] tokens in [0, number of blocks); for a decode step,
+ *     positions[b][j] = ctx_lens[b] - n_q + j (the queries are the last n_q
+ *     tokens; a negative position sees no token); append targets reserved
+ *     and distinct.  The Python binding checks all of this on the host
+ *     before each call when MLA_CHECK_CONTRACT=1.  The kernels keep
  *     memory safety where they can see a breach: decode treats a segment
  *     whose block ids include a negative one, or whose tokens run past
  *     max_blocks * block_size, as empty (its partial is u = 0, lse = -inf);

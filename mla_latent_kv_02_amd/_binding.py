@@ -216,6 +216,19 @@ def _stream(stream) -> Optional[int]:
     return stream if isinstance(stream, int) else stream.cuda_stream
 
 
+def _contract(check: str, *args, fn: str) -> None:
+    """With MLA_CHECK_CONTRACT=1, copy the device-side arguments the library
+    trusts (context lengths, positions, block ids, append targets) to the host
+    and check them before the call (contract.py); off by default."""
+    if os.environ.get("MLA_CHECK_CONTRACT") != "1":
+        return
+    cuda = _torch().cuda
+    if cuda.is_initialized() and cuda.is_current_stream_capturing():
+        return      # no host copy inside a graph capture; the eager calls before it are checked
+    from . import contract
+    getattr(contract, check)(*args, fn=fn)
+
+
 def _check(fn: str, status: int):
     if status != MLA_OK:
         lib = load_library()
@@ -274,6 +287,7 @@ def mla_decode(dims: Dims, q_lat, q_pe, cache: LatentCache, positions, num_split
     _shape(u_part, "u_part", (slots, n_q, dims.n_h, dims.d_c))
     _shape(lse_part, "lse_part", (slots, n_q, dims.n_h, 2))
     d, c = dims._c(), cache._c()
+    _contract("check_decode", cache, positions, fn="mla_decode")
     _check("mla_decode", load_library().mla_decode(
         ctypes.byref(d), B, n_q, q_lat.data_ptr(), q_pe.data_ptr(), ctypes.byref(c),
         positions.data_ptr(), num_splits, u_part.data_ptr(), lse_part.data_ptr(), _stream(stream)))
@@ -294,6 +308,7 @@ def mla_combine(dims: Dims, ctx_lens, num_splits: int, u_part, lse_part, u, lse=
         _dev(lse, "lse", torch.float32)
         _shape(lse, "lse", (B, n_q, dims.n_h))
     d = dims._c()
+    _contract("check_ctx_lens", ctx_lens, fn="mla_combine")
     _check("mla_combine", load_library().mla_combine(
         ctypes.byref(d), B, n_q, ctx_lens.data_ptr(), num_splits, u_part.data_ptr(), lse_part.data_ptr(),
         u.data_ptr(), None if lse is None else lse.data_ptr(), _stream(stream)))
@@ -331,6 +346,7 @@ def mla_combine_out_proj(dims: Dims, ctx_lens, num_splits: int, u_part, lse_part
         _dev(lse, "lse", torch.float32)
         _shape(lse, "lse", (B, n_q, dims.n_h))
     d = dims._c()
+    _contract("check_ctx_lens", ctx_lens, fn="mla_combine_out_proj")
     _check("mla_combine_out_proj", load_library().mla_combine_out_proj(
         ctypes.byref(d), B, n_q, ctx_lens.data_ptr(), num_splits, u_part.data_ptr(), lse_part.data_ptr(),
         _dtype(w_uv), w_uv.data_ptr(), out.data_ptr(), None if lse is None else lse.data_ptr(), _stream(stream)))
@@ -361,6 +377,7 @@ def mla_decode_out_noalloc(dims: Dims, q_lat, q_pe, cache: LatentCache, position
         _dev(lse, "lse", torch.float32)
         _shape(lse, "lse", (B, n_q, dims.n_h))
     d, c = dims._c(), cache._c()
+    _contract("check_decode", cache, positions, fn="mla_decode_out_noalloc")
     _check("mla_decode_out_noalloc", load_library().mla_decode_out_noalloc(
         ctypes.byref(d), B, n_q, q_lat.data_ptr(), q_pe.data_ptr(), ctypes.byref(c), positions.data_ptr(),
         num_splits, _dtype(w_uv), w_uv.data_ptr(), out.data_ptr(), None if lse is None else lse.data_ptr(),
@@ -373,6 +390,7 @@ def mla_cache_append(dims: Dims, cache: LatentCache, seq_ids, positions, c_kv_ne
     the tensors, so both may be column slices of one [n][d_c + d_rope] array)."""
     n = _append_checks(dims, cache, seq_ids, positions, c_kv_new, k_rope_new)
     d, c = dims._c(), cache._c()
+    _contract("check_cache_append", cache, seq_ids, positions, fn="mla_cache_append")
     _check("mla_cache_append", load_library().mla_cache_append(
         ctypes.byref(d), ctypes.byref(c), n, seq_ids.data_ptr(), positions.data_ptr(),
         c_kv_new.data_ptr(), c_kv_new.stride(0), k_rope_new.data_ptr(), k_rope_new.stride(0),
@@ -387,6 +405,7 @@ def mla_append_absorb_q(dims: Dims, cache: LatentCache, seq_ids, new_positions, 
     n = _append_checks(dims, cache, seq_ids, new_positions, c_kv_new, k_rope_new)
     B, n_q = _absorb_checks(dims, q_nope, q_rope, positions, w_uk, q_lat, q_pe)
     d, c = dims._c(), cache._c()
+    _contract("check_cache_append", cache, seq_ids, new_positions, fn="mla_append_absorb_q")
     _check("mla_append_absorb_q", load_library().mla_append_absorb_q(
         ctypes.byref(d), ctypes.byref(c), n, seq_ids.data_ptr(), new_positions.data_ptr(),
         c_kv_new.data_ptr(), c_kv_new.stride(0), k_rope_new.data_ptr(), k_rope_new.stride(0),

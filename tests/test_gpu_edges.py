@@ -193,9 +193,10 @@ def test_late_spike_redo_path(layout, num_splits):
 
 
 @pytest.mark.parametrize("bs", [16, 64])
-def test_append_without_a_block_writes_nothing(bs):
+def test_append_without_a_block_writes_nothing(bs, monkeypatch):
     _need_gpu()
     import mla_latent_kv_02_amd as mla
+    from mla_latent_kv_02_amd.contract import ContractError
     from workloads.device import stage
     w = W.custom(name=f"noblock{bs}", seed=95, batch=2, n_q=1, ctx=None, ctx_range=(1, 1), block_size=bs)
     ctx = np.array([3 * bs - 5, bs + 3], np.int32)      # table rows of 3 blocks; sequence 1 holds 2
@@ -208,6 +209,14 @@ def test_append_without_a_block_writes_nothing(bs):
     sid = torch.tensor([1, 0, 0], dtype=torch.int32, device="cuda")
     pos = torch.tensor([2 * bs + 1, 3 * bs, -1], dtype=torch.int32, device="cuda")
     raw = torch.randn((3, w.row), device="cuda").bfloat16()
+    # the host-side contract check names the first breach (and launches nothing)
+    monkeypatch.setenv("MLA_CHECK_CONTRACT", "1")
+    with pytest.raises(ContractError, match="block id -1"):
+        mla.mla_cache_append(st["dims"], st["cache"], sid, pos, raw[:, :w.d_c], raw[:, w.d_c:])
+    torch.cuda.synchronize()
+    assert torch.equal(st["cache"].data.view(torch.int16), before)
+    # without it, the kernel's own guards keep the breach from writing
+    monkeypatch.setenv("MLA_CHECK_CONTRACT", "0")
     mla.mla_cache_append(st["dims"], st["cache"], sid, pos, raw[:, :w.d_c], raw[:, w.d_c:])
     torch.cuda.synchronize()
     assert torch.equal(st["cache"].data.view(torch.int16), before)
@@ -219,8 +228,9 @@ def test_append_without_a_block_writes_nothing(bs):
 
 
 @pytest.mark.parametrize("bs", [16, 64])
-def test_decode_range_the_descriptor_cannot_place_is_empty(bs):
+def test_decode_range_the_descriptor_cannot_place_is_empty(bs, monkeypatch):
     _need_gpu()
+    from mla_latent_kv_02_amd.contract import ContractError
     from workloads.device import stage
     w = W.custom(name=f"badtable{bs}", seed=96, batch=3, n_q=1, ctx=None, ctx_range=(1, 1), block_size=bs)
     ctx = np.array([4 * bs - 7, 3 * bs + 2, 2 * bs + 9], np.int32)
@@ -233,6 +243,14 @@ def test_decode_range_the_descriptor_cannot_place_is_empty(bs):
     st["cache"].ctx_lens[2] = long_ctx
     st["positions"][2, 0] = long_ctx - 1
     torch.cuda.synchronize()
+    monkeypatch.setenv("MLA_CHECK_CONTRACT", "1")
+    with pytest.raises(ContractError, match=f"ctx_lens\\[2\\] = {long_ctx} outside"):
+        _decode(st, num_splits=1)
+    st["cache"].ctx_lens[2] = int(ctx[2])
+    with pytest.raises(ContractError, match="sequence 1: block 1 .* has id -1"):
+        _decode(st, num_splits=1)
+    st["cache"].ctx_lens[2] = long_ctx
+    monkeypatch.setenv("MLA_CHECK_CONTRACT", "0")
     got = _decode(st, num_splits=1)
     _assert_close(got, _ref(w, 0, int(ctx[0]), st["positions_host"][0]), 0, "valid sequence")
     _assert_empty(got, 1, "negative block id")
