@@ -349,7 +349,16 @@ struct Fp8Loader {
         vo = (int)lc[i < 4 ? 0 : i - 3];
         so = (int)(sbase + (i < 4 ? 8u * i * RB8 : 0u));
       } else {
-        vo = (int)pc.row(token(i), byte(i));
+        // the per-lane parts of the six loads' offsets are formed here, from
+        // an opaque copy of the lane index, so the compiler cannot hoist them
+        // out of the stage loop (twelve more live registers there spill)
+        int ln = lane_;
+        asm volatile("" : "+v"(ln));
+        const int q = ln >> 3, p = ln & 7;
+        const int t = i < 4 ? 8 * i + q : (i == 4 ? 8 * wave_ + q : (ln & 31));
+        const uint32_t by = i < 4 ? 128 * wave_ + 16 * p
+                                  : (i == 4 ? F8_ROPE + 16 * (p ^ swz(8 * wave_ + q)) : F8_SCALE + 4 * wave_);
+        vo = (int)pc.row(t, by);
         so = 0;
       }
       if (i < 5) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, d, 16, vo, so, 0, 0);
@@ -932,9 +941,10 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
     } else if constexpr (LAYOUT == kPaged) {
       int blk_lo = 0;
       const int span = paged_span(a.cache, b, t0, t1, lane, FP8 ? RB8 : RB16, &blk_lo);
+      // one call site per layout: a second inlined copy of the segment body
+      // costs the whole kernel registers (spills in the stage loop)
       if (span == kSpanNear) segment(Paged{}, b, t0, t1, slot, blk_lo);
-      else if (span == kSpanFar) segment(Any{}, b, t0, t1, slot, 0);    // blocks 4 GiB or more apart
-      else segment(Any{}, b, t0, t0, slot, 0);
+      else segment(Any{}, b, t0, span == kSpanFar ? t1 : t0, slot, 0);   // blocks 4 GiB or more apart
     } else {
       const bool placed = segment_rows_placed(a.cache, b, t0, t1, lane);
       segment(Any{}, b, t0, placed ? t1 : t0, slot, 0);
