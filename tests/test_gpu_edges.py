@@ -211,7 +211,9 @@ def test_append_without_a_block_writes_nothing(bs, monkeypatch):
     raw = torch.randn((3, w.row), device="cuda").bfloat16()
     # the host-side contract check names the first breach (and launches nothing)
     monkeypatch.setenv("MLA_CHECK_CONTRACT", "1")
-    with pytest.raises(ContractError, match="block id -1"):
+    with pytest.raises(ContractError, match="goes to block id -1"):
+        mla.mla_cache_append(st["dims"], st["cache"], sid[:1], pos[:1], raw[:1, :w.d_c], raw[:1, w.d_c:])
+    with pytest.raises(ContractError, match=f"positions\\[1\\] = {3 * bs} outside"):
         mla.mla_cache_append(st["dims"], st["cache"], sid, pos, raw[:, :w.d_c], raw[:, w.d_c:])
     torch.cuda.synchronize()
     assert torch.equal(st["cache"].data.view(torch.int16), before)
