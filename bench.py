@@ -73,6 +73,10 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain fp32 copy kernel (dst = -src) over this many MiB, 5 times: the "
                          "calibration run for the HBM byte counters")
+    ap.add_argument("--stream-probe-mib", type=int, default=0,
+                    help="only measure plain HBM streaming over buffers of this many MiB: torch's sum (read only) "
+                         "and neg (read + write), 20 reps each with HIP events, after the same flush as the bench; "
+                         "the practical ceiling the decode rates are set against")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time in the CPU sample")
     ap.add_argument("--folds", action="store_true",
                     help="instead of the step bench: the weight folds' per-step products (layer output through "
@@ -239,6 +243,36 @@ def copy_probe(mib):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
     log(f"copy probe: 5 x {mib} MiB read + {mib} MiB written")
+
+
+def stream_probe(mib, flush_mib, reps=20):
+    """Plain HBM streaming rates: torch.sum over `mib` MiB (reads only) and
+    torch.neg into a second buffer (reads + writes), each rep timed with its
+    own events after the bench's flush.  Prints one JSON line."""
+    import numpy as np
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    acc = torch.zeros((), dtype=torch.float32, device="cuda")
+    flush = make_flush(flush_mib)
+    out = {"probe": "hbm_stream", "mib": mib, "reps": reps, "flush_mib_per_rep": flush_mib}
+    for name, fn, nbytes in (("read", lambda: torch.sum(src, (0,), out=acc), n * 4),
+                             ("copy", lambda: torch.neg(src, out=dst), n * 8)):
+        ts = []
+        for r in range(reps + 3):
+            flush()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if r >= 3:
+                ts.append(e0.elapsed_time(e1) * 1e-3)
+        rates = np.array([nbytes / t / 1e9 for t in ts])
+        out[name + "_gbs"] = {"median": round(float(np.median(rates)), 1), "min": round(float(rates.min()), 1),
+                              "max": round(float(rates.max()), 1), "bytes_per_rep": nbytes}
+    print(json.dumps(out), flush=True)
 
 
 def make_flush(mib, kind="rw+read"):
@@ -531,6 +565,9 @@ def main():
         sys.exit(2)
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
+        return
+    if args.stream_probe_mib:
+        stream_probe(args.stream_probe_mib, args.flush_mib)
         return
     if args.session:
         session_bench(args)
