@@ -191,9 +191,6 @@ __global__ __launch_bounds__(256) void absorb_rope_kernel(AbsorbParams p, Append
   const int g = lane >> 4, l16 = lane & 15;
   const int M = p.B * p.n_q;
   const int half = p.d_rope / 2;
-  // turns per position of plane k: base^(-2k/d_rope) / (2 pi)
-  if (threadIdx.x < half) theta[threadIdx.x] = pow((double)p.rope_base, -2.0 * threadIdx.x / p.d_rope) * kInv2Pi;
-  __syncthreads();
   // ---- query RoPE of head i, rows m = h2, h2 + nslices, ...: the loads of
   // the first AR_ROPE items of this thread are issued before the GEMM loads,
   // so the rotation only waits for them
@@ -240,6 +237,10 @@ __global__ __launch_bounds__(256) void absorb_rope_kernel(AbsorbParams p, Append
   };
   u16x8 bq[4][4];
   load_b(0, bq);
+  // turns per position of plane k: base^(-2k/d_rope) / (2 pi), formed while
+  // the loads above are in flight (the barrier waits for LDS only)
+  if (threadIdx.x < half) theta[threadIdx.x] = pow((double)p.rope_base, -2.0 * threadIdx.x / p.d_rope) * kInv2Pi;
+  lds_sync();
   auto rotate = [&](int idx, uint32_t x, int pos) {
     int m, k;
     const int64_t off = rope_off(idx, m, k);

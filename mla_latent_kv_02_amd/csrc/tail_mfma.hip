@@ -5,7 +5,8 @@
 // over the partials k of a query row -- the softmax over the union of the
 // partials' token ranges ([Ikmyung] §1.4).  The merged u is never written.
 //
-// Workgroup = (head i, block of 32 query rows), all d_v = 128 value columns.
+// Workgroup = (head i, block of up to 32 query rows; fewer when the batch is
+// small, so that the workgroups cover the CUs), all d_v = 128 value columns.
 // Wave w owns the contraction slice d_c*w/4 .. d_c*(w+1)/4 (<= 128 latents):
 //   1. its W_i^UV rows are staged in LDS (global->LDS loads, 16-byte chunks
 //      xor-swizzled by row so that transposed reads hit distinct banks);
@@ -24,7 +25,7 @@ namespace mla {
 namespace {
 
 constexpr int NT = 256;
-constexpr int TR = 32;            // query rows per workgroup (MFMA M)
+constexpr int TR = 32;            // query rows of the MFMA tile (M), and the most a workgroup takes
 constexpr int TDV = 128;          // value columns (4 MFMA column blocks of 32)
 constexpr int TKW = 128;          // contraction rows per wave (d_c / 4)
 constexpr int TKS = TKW / 16;     // MFMA k-steps per wave
@@ -45,18 +46,19 @@ struct __attribute__((aligned(16))) TailSmem {
 __device__ __forceinline__ int wswz(int r) { return 4 * (r & 3); }
 
 template <bool PARTIALS>
-__global__ __launch_bounds__(NT, 1) void tail_kernel(TailParams p, int items_pad) {
+__global__ __launch_bounds__(NT, 1) void tail_kernel(TailParams p, int items_pad, int rows_per_block) {
   __shared__ TailSmem sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int M = p.B * p.n_q;
-  const int rblocks = (M + TR - 1) / TR;
+  const int R = rows_per_block;              // a power of two <= TR
+  const int rblocks = (M + R - 1) / R;
   // block -> (head, row block); consecutive items on one XCD (block b runs on
   // XCD b % 8), so the row blocks of a head share its weights in L2
   const int item = (blockIdx.x & 7) * (items_pad / 8) + (blockIdx.x >> 3);
   if (item >= p.n_h * rblocks) return;
   const int ih = item / rblocks;
-  const int m0 = (item % rblocks) * TR;
+  const int m0 = (item % rblocks) * R;
   const int k0 = wave * TKW;                 // first latent of this wave's slice
   // the sequence lengths for the plan, loaded ahead of the weights
   const int len_tid = PARTIALS && (int)threadIdx.x < p.B ? p.ctx_lens[threadIdx.x] : 0;
@@ -79,7 +81,7 @@ __global__ __launch_bounds__(NT, 1) void tail_kernel(TailParams p, int items_pad
   // two): replica j of a row takes the partials k = j, j+rep, ... and the
   // replicas are summed with lane exchanges before the MFMAs (rows past the
   // block end carry copies that are never stored).
-  const int rows_here = (M - m0) < TR ? (M - m0) : TR;
+  const int rows_here = (M - m0) < R ? (M - m0) : R;
   int prow2 = 1;
   while (prow2 < rows_here) prow2 <<= 1;
   const int rep = PARTIALS ? TR / prow2 : 1;
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(NT, 1) void tail_kernel(TailParams p, int items_pad
   int slot0 = 0, np = 1;
   const int b_lo = m0 / p.n_q;
   if (PARTIALS) {
-    const int b_hi = ((M < m0 + TR ? M : m0 + TR) - 1) / p.n_q;
+    const int b_hi = ((M < m0 + R ? M : m0 + R) - 1) / p.n_q;
     plan_slot_range<NT>(p.ctx_lens, p.B, p.num_splits, b_lo, b_hi - b_lo + 1, len_tid, &sm.plan, sm.slot0,
                         sm.nparts);
   }
@@ -248,12 +250,17 @@ bool tail_mfma_ok(int d_c, int d_v, bool bf16_weights) {
 
 hipError_t launch_tail_mfma(const TailParams& p, bool from_partials, hipStream_t stream) {
   const int M = p.B * p.n_q;
-  const int items = p.n_h * ((M + TR - 1) / TR);
+  // Blocks of fewer rows when the batch is small, so that the workgroups
+  // cover the 256 CUs (the spare lanes of a block take shares of its rows'
+  // partials, as replicas).
+  int R = TR;
+  while (R > 1 && (int64_t)p.n_h * ((M + R - 1) / R) < 256) R >>= 1;
+  const int items = p.n_h * ((M + R - 1) / R);
   const int items_pad = (items + 7) / 8 * 8;
   if (from_partials)
-    hipLaunchKernelGGL(tail_kernel<true>, dim3(items_pad), dim3(NT), 0, stream, p, items_pad);
+    hipLaunchKernelGGL(tail_kernel<true>, dim3(items_pad), dim3(NT), 0, stream, p, items_pad, R);
   else
-    hipLaunchKernelGGL(tail_kernel<false>, dim3(items_pad), dim3(NT), 0, stream, p, items_pad);
+    hipLaunchKernelGGL(tail_kernel<false>, dim3(items_pad), dim3(NT), 0, stream, p, items_pad, R);
   return hipGetLastError();
 }
 
