@@ -200,8 +200,10 @@ def _cpu_baseline(w, min_seconds, head_group, cores, affinity, model):
             "head_rows_per_s": round(head_rows / spent, 3)}
 
 
-DECODE_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "mla_latent_kv_02_amd", "csrc",
-                             "decode_mfma.hip")
+# the decode kernel and the device header with its work plan (which sets the
+# partials it writes)
+DECODE_SOURCES = tuple(os.path.join(os.path.dirname(os.path.abspath(__file__)), "mla_latent_kv_02_amd", "csrc", f)
+                       for f in ("decode_mfma.hip", "mla_device.h"))
 PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
 
 
@@ -209,14 +211,18 @@ def measured_traffic(workload):
     """HBM bytes per decode launch from the committed counter summaries.
 
     A summary under profiles/ carries a line ``traffic-record: {json}`` with the
-    workload, the sha256 of the decode kernel's source when the counters were
-    taken, and the calibrated FETCH_SIZE + WRITE_SIZE bytes per launch.  The
-    figure is returned only while the source is unchanged; otherwise None.
+    workload, the sha256 of the decode kernel's sources (DECODE_SOURCES, in
+    that order, concatenated) when the counters were taken, and the calibrated
+    FETCH_SIZE + WRITE_SIZE bytes per launch.  The figure is returned only
+    while the sources are unchanged; otherwise None.
     """
     import hashlib
     try:
-        with open(DECODE_SOURCE, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        h = hashlib.sha256()
+        for path in DECODE_SOURCES:
+            with open(path, "rb") as f:
+                h.update(f.read())
+        sha = h.hexdigest()
         names = sorted(os.listdir(PROFILES))
     except OSError:
         return None

@@ -138,13 +138,20 @@ mla_status_t mla_absorb_q(const mla_dims_t *dims, int32_t B, int32_t n_q, mla_dt
                           const void *w_uk, void *q_lat, void *q_pe, void *stream);
 
 /* Number of partial slots mla_decode may write for a batch of B sequences
- * split into num_splits token-balanced work units: num_splits + B - 1. */
+ * split into num_splits work units: num_splits + B - 1. */
 int64_t mla_num_partials(int32_t B, int32_t num_splits);
 
 /* Decode attention over the latent cache, split-KV ([Huny] §2.2, §3.1, §3.2).
  * The tokens of all sequences, taken in order (sequence 0 first), are cut
- * into num_splits consecutive ranges of ceil(sum ctx / num_splits) tokens;
- * each range is one work unit.  Every (sequence, work unit) pair that shares
+ * into num_splits consecutive ranges of about equal cost; each range is one
+ * work unit.  Cost: with T = sum ctx, U = num_splits and q0 = ceil(T / U),
+ * a sequence whose token prefix P_b is not a multiple of q0 starts inside a
+ * unit (the unit then runs a second segment) and is preceded by 288 cost
+ * positions; its tokens sit at cost positions C_b .. C_b + ctx_b - 1, C_b =
+ * P_b + 288 * (such starts among sequences 0..b).  Unit w covers cost
+ * positions [w Q, (w + 1) Q), Q = ceil((T + 288 E) / U), E = all such
+ * starts; when every sequence starts on a multiple of q0 this is the plain
+ * split into ranges of q0 tokens.  Every (sequence, work unit) pair that shares
  * tokens produces one partial over those tokens T_p: with a reference r_p
  * (any real number the kernel picks; it keeps the weights in range),
  *   u_part[p][j][i][:]   = sum_{t in T_p} exp(s_t - r_p) c_t     (not normalised)

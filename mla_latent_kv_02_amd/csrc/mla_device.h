@@ -99,11 +99,23 @@ __device__ __forceinline__ bool segment_rows_placed(const CacheView& c, int b, i
 }
 
 // ------------------------------------------------------ split-KV work plan
-// The tokens of all sequences, in order, are cut into ranges of Q tokens
-// (Q = ceil(total / num_splits)); range w is work unit w.  Sequence b (prefix
-// P_b, length L_b > 0) meets work units P_b / Q .. (P_b + L_b - 1) / Q and owns
-// that many consecutive partial slots starting at slot_base(b), the sum of the
-// counts of the sequences before it.
+// Work units are equal ranges of a cost line on which the tokens of all
+// sequences lie in order (U = num_splits, T = the sum of the lengths):
+//   - the token cut q0 = ceil(T / U) marks where a plain token split would
+//     cut; sequence b (token prefix P_b, length L_b > 0) starts inside a unit
+//     when P_b is not a multiple of q0 (f_b = 1);
+//   - such a start costs the unit that meets it a second segment (query rows,
+//     pipeline start, one more partial written), counted as kSegmentCost
+//     tokens placed in front of the sequence's tokens: b's tokens occupy cost
+//     positions C_b .. C_b + L_b - 1, C_b = P_b + kSegmentCost * sum_{b' <= b} f_b';
+//   - unit w covers cost positions [w Q, (w + 1) Q), Q = ceil((T + kSegmentCost E) / U)
+//     with E = sum_b f_b.
+// Sequence b meets units C_b / Q .. (C_b + L_b - 1) / Q and owns that many
+// consecutive partial slots starting at the sum of the counts of the
+// sequences before it.  When every sequence starts on a multiple of q0, E = 0
+// and this is the plain token split.
+constexpr int64_t kSegmentCost = 288;
+
 __device__ __forceinline__ int64_t plan_chunk(int64_t total, int num_splits) {
   int64_t q = (total + num_splits - 1) / num_splits;
   return q > 0 ? q : 1;
@@ -158,6 +170,69 @@ struct PlanScratch {
   int32_t first, last;
 };
 
+// Positions of one chunk of NT sequences on the cost line (this thread's
+// sequence has length len; run and frun are the token count and the number
+// of inside starts of the sequences before the chunk): *p = P_b, *cp = C_b;
+// *tot_len and *tot_f receive the chunk's sums.
+template <int NT>
+__device__ __forceinline__ void plan_positions(int64_t len, int64_t run, int64_t frun, int64_t q0, int64_t* scan,
+                                               int64_t* p, int64_t* cp, int64_t* tot_len, int64_t* tot_f) {
+  *p = run + block_scan_incl<NT>(len, scan, tot_len) - len;
+  const int64_t f = len > 0 && *p % q0 != 0 ? 1 : 0;
+  *cp = *p + kSegmentCost * (frun + block_scan_incl<NT>(f, scan, tot_f));
+}
+
+// The plan's token cut q0, unit width Q and cost-line length, and the
+// positions of the first chunk of NT sequences (this thread's C_b and the
+// chunk's sums), which the walks below reuse.  len0 is ctx_lens[threadIdx.x]
+// (0 past B), loaded by the caller.  All NT threads must call this together.
+struct PlanGeometry {
+  int64_t q0, Q, cost_total;
+  int64_t cp0, tot_len0, tot_f0;
+};
+template <int NT>
+__device__ void plan_geometry(const int32_t* __restrict__ ctx_lens, int B, int num_splits, int len0,
+                              PlanScratch<NT>* sc, PlanGeometry* g) {
+  const int tid = threadIdx.x;
+  const int64_t p0 = block_scan_incl<NT>((int64_t)len0, sc->scan, &g->tot_len0) - len0;
+  int64_t total = g->tot_len0;
+  if (B > NT) {   // the token total needs the other chunks too
+    int64_t part = 0, rest;
+    for (int b = tid + NT; b < B; b += NT) part += ctx_lens[b];
+    block_scan_incl<NT>(part, sc->scan, &rest);
+    total += rest;
+  }
+  g->q0 = plan_chunk(total, num_splits);
+  const int64_t f0 = len0 > 0 && p0 % g->q0 != 0 ? 1 : 0;
+  g->cp0 = p0 + kSegmentCost * block_scan_incl<NT>(f0, sc->scan, &g->tot_f0);
+  int64_t run = g->tot_len0, frun = g->tot_f0;
+  for (int c0 = NT; c0 < B; c0 += NT) {
+    const int b = c0 + tid;
+    const int64_t len = b < B ? ctx_lens[b] : 0;
+    int64_t p, cp, tot_len, tot_f;
+    plan_positions<NT>(len, run, frun, g->q0, sc->scan, &p, &cp, &tot_len, &tot_f);
+    run += tot_len;
+    frun += tot_f;
+  }
+  g->cost_total = total + kSegmentCost * frun;
+  g->Q = plan_chunk(g->cost_total, num_splits);
+}
+
+// C_b of this thread's sequence in the chunk starting at c0, and the chunk's sums.
+template <int NT>
+__device__ __forceinline__ void plan_chunk_positions(const PlanGeometry& g, int c0, int64_t len, int64_t run,
+                                                     int64_t frun, int64_t* scan, int64_t* cp, int64_t* tot_len,
+                                                     int64_t* tot_f) {
+  if (c0 == 0) {
+    *cp = g.cp0;
+    *tot_len = g.tot_len0;
+    *tot_f = g.tot_f0;
+  } else {
+    int64_t p;
+    plan_positions<NT>(len, run, frun, g.q0, scan, &p, cp, tot_len, tot_f);
+  }
+}
+
 // Calls f(b, t0, t1, slot) for every segment of work unit w: the tokens
 // t0..t1-1 of sequence b that fall into the unit, and the partial slot they
 // own.  Segments come in sequence order.  All NT threads of the workgroup
@@ -166,28 +241,27 @@ template <int NT, typename F>
 __device__ void for_each_segment(const int32_t* __restrict__ ctx_lens, int B, int num_splits, int w,
                                  PlanScratch<NT>* sc, F&& f) {
   const int tid = threadIdx.x;
-  int64_t part = 0;
-  for (int b = tid; b < B; b += NT) part += ctx_lens[b];
-  int64_t total;
-  block_scan_incl<NT>(part, sc->scan, &total);
-  const int64_t q = plan_chunk(total, num_splits);
+  const int len0 = tid < B ? ctx_lens[tid] : 0;
+  PlanGeometry g;
+  plan_geometry<NT>(ctx_lens, B, num_splits, len0, sc, &g);
+  const int64_t q = g.Q;
   const int64_t a = (int64_t)w * q;
-  const int64_t e = a + q < total ? a + q : total;
+  const int64_t e = a + q < g.cost_total ? a + q : g.cost_total;
   if (a >= e) return;
-  int64_t run = 0, slot_run = 0;
+  int64_t run = 0, frun = 0, slot_run = 0;
   for (int c0 = 0; c0 < B; c0 += NT) {
     const int b = c0 + tid;
-    const int64_t len = b < B ? ctx_lens[b] : 0;
-    int64_t tot_len, tot_np;
-    const int64_t p = run + block_scan_incl<NT>(len, sc->scan, &tot_len) - len;
-    const int64_t np = plan_parts(p, len, q);
+    const int64_t len = c0 == 0 ? len0 : (b < B ? ctx_lens[b] : 0);
+    int64_t cp, tot_len, tot_f, tot_np;
+    plan_chunk_positions<NT>(g, c0, len, run, frun, sc->scan, &cp, &tot_len, &tot_f);
+    const int64_t np = plan_parts(cp, len, q);
     const int64_t sb = slot_run + block_scan_incl<NT>(np, sc->scan, &tot_np) - np;
     if (tid == 0) { sc->first = NT; sc->last = -1; }
     __syncthreads();
-    const bool hit = len > 0 && p < e && p + len > a;
-    sc->prefix[tid] = p;
+    const bool hit = len > 0 && cp < e && cp + len > a;
+    sc->prefix[tid] = cp;
     sc->len[tid] = (int32_t)len;
-    sc->slot[tid] = (int32_t)(sb + (w - p / q));
+    sc->slot[tid] = (int32_t)(sb + (w - cp / q));
     if (hit) { atomicMin(&sc->first, tid); atomicMax(&sc->last, tid); }
     __syncthreads();
     // the segment values are the same in every lane: keep them in scalar
@@ -208,8 +282,9 @@ __device__ void for_each_segment(const int32_t* __restrict__ ctx_lens, int B, in
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
     run += tot_len;
+    frun += tot_f;
     slot_run += tot_np;
-    if (run >= e) break;
+    if (run + kSegmentCost * frun >= e) break;   // later sequences start at or past the unit's end
   }
 }
 
@@ -222,21 +297,19 @@ template <int NT>
 __device__ void plan_slot_range(const int32_t* __restrict__ ctx_lens, int B, int num_splits, int b_lo, int n,
                                 int len_tid, PlanScratch<NT>* sc, int* slot0, int* nparts) {
   const int tid = threadIdx.x;
-  int64_t part = len_tid;
-  for (int k = tid + NT; k < B; k += NT) part += ctx_lens[k];
-  int64_t total;
-  block_scan_incl<NT>(part, sc->scan, &total);
-  const int64_t q = plan_chunk(total, num_splits);
-  int64_t run = 0, slot_run = 0;
+  PlanGeometry g;
+  plan_geometry<NT>(ctx_lens, B, num_splits, len_tid, sc, &g);
+  int64_t run = 0, frun = 0, slot_run = 0;
   for (int c0 = 0; c0 < b_lo + n; c0 += NT) {
     const int k = c0 + tid;
     const int64_t len = c0 == 0 ? len_tid : (k < B ? ctx_lens[k] : 0);
-    int64_t tot_len, tot_np;
-    const int64_t p = run + block_scan_incl<NT>(len, sc->scan, &tot_len) - len;
-    const int64_t np = plan_parts(p, len, q);
+    int64_t cp, tot_len, tot_f, tot_np;
+    plan_chunk_positions<NT>(g, c0, len, run, frun, sc->scan, &cp, &tot_len, &tot_f);
+    const int64_t np = plan_parts(cp, len, g.Q);
     const int64_t sb = slot_run + block_scan_incl<NT>(np, sc->scan, &tot_np) - np;
     if (k >= b_lo && k < b_lo + n) { slot0[k - b_lo] = (int32_t)sb; nparts[k - b_lo] = (int32_t)np; }
     run += tot_len;
+    frun += tot_f;
     slot_run += tot_np;
   }
   lds_sync();
@@ -247,21 +320,20 @@ template <int NT>
 __device__ void plan_lookup(const int32_t* __restrict__ ctx_lens, int B, int num_splits, int b,
                             PlanScratch<NT>* sc, int* slot_base, int* n_parts) {
   const int tid = threadIdx.x;
-  int64_t part = 0;
-  for (int k = tid; k < B; k += NT) part += ctx_lens[k];
-  int64_t total;
-  block_scan_incl<NT>(part, sc->scan, &total);
-  const int64_t q = plan_chunk(total, num_splits);
-  int64_t run = 0, slot_run = 0;
+  const int len0 = tid < B ? ctx_lens[tid] : 0;
+  PlanGeometry g;
+  plan_geometry<NT>(ctx_lens, B, num_splits, len0, sc, &g);
+  int64_t run = 0, frun = 0, slot_run = 0;
   for (int c0 = 0; c0 <= b; c0 += NT) {
     const int k = c0 + tid;
-    const int64_t len = k < B ? ctx_lens[k] : 0;
-    int64_t tot_len, tot_np;
-    const int64_t p = run + block_scan_incl<NT>(len, sc->scan, &tot_len) - len;
-    const int64_t np = plan_parts(p, len, q);
+    const int64_t len = c0 == 0 ? len0 : (k < B ? ctx_lens[k] : 0);
+    int64_t cp, tot_len, tot_f, tot_np;
+    plan_chunk_positions<NT>(g, c0, len, run, frun, sc->scan, &cp, &tot_len, &tot_f);
+    const int64_t np = plan_parts(cp, len, g.Q);
     const int64_t sb = slot_run + block_scan_incl<NT>(np, sc->scan, &tot_np) - np;
     if (k == b) { sc->slot[0] = (int32_t)sb; sc->len[0] = (int32_t)np; }
     run += tot_len;
+    frun += tot_f;
     slot_run += tot_np;
   }
   __syncthreads();

@@ -3,9 +3,9 @@ and the cache descriptor, against the fp64 oracle (tolerance 1e-2, bf16
 operands):
 
 - a batch of 300 sequences: the plan walk takes sequences in chunks of 256,
-  so work-unit boundaries and partial slots fall in both chunks; short ragged
-  contexts, some of them empty (a query that sees no token gives u = 0,
-  o = 0, lse = -inf);
+  so work-unit boundaries and partial slots fall in both chunks (or a unit
+  runs across the chunk boundary); short ragged contexts, two of 1500 tokens,
+  some empty (a query that sees no token gives u = 0, o = 0, lse = -inf);
 - one late token whose latent row is 2048 e_j: its scores pass many rows'
   reference by far more than the kernel's headroom, so those segments are
   computed again with the true maximum.  Over paged caches whose segment
@@ -24,6 +24,7 @@ import pytest
 import oracle
 import workloads as W
 from tests._metrics import scalar_err, vec_rel_err
+from tests.plan_ref import Plan
 from tests.test_gpu_parity import _need_gpu, torch
 
 pytestmark = pytest.mark.gpu
@@ -107,12 +108,14 @@ def test_batch_over_one_plan_chunk(num_splits):
     ctx = W.context_lengths(w).copy()
     ctx[[5, 200, 255, 256, 299]] = 0
     ctx[[1, 257]] = 1
+    ctx[[40, 270]] = 1500   # longer than a unit at 64 and 256 splits
     st = stage(w, ctx=ctx)
     total = int(ctx.sum())
-    q = -(-total // num_splits)
-    prefix = np.concatenate([[0], np.cumsum(ctx)])
-    straddle = [b for b in range(w.batch) if ctx[b] > 0 and prefix[b] // q != (prefix[b] + ctx[b] - 1) // q]
-    assert any(b < 256 for b in straddle) and any(b >= 256 for b in straddle)
+    # the plan cuts sequences of both chunks, or runs a unit across the chunk boundary
+    plan = Plan(ctx, num_splits)
+    straddle = [b for b in range(w.batch) if plan.parts[b] > 1]
+    spanning = [u for u in range(num_splits) if {b < 256 for b, *_ in plan.segments(u)} == {True, False}]
+    assert any(b < 256 for b in straddle) and (any(b >= 256 for b in straddle) or spanning)
     got = _decode(st, num_splits)
     worst = 0.0
     for b in range(w.batch):

@@ -17,6 +17,7 @@ import numpy as np
 import pytest
 
 import workloads as W
+from tests.plan_ref import Plan
 from tests.test_gpu_parity import _check, _need_gpu, torch
 
 pytestmark = pytest.mark.gpu
@@ -24,17 +25,13 @@ pytestmark = pytest.mark.gpu
 def _cut_sequences(ctx, num_splits, k):
     """The k sequences whose tokens a work-unit boundary splits most unevenly:
     ranked by the shorter of the pieces on either side of a boundary inside
-    the sequence (the plan cuts the concatenated tokens every ceil(total /
-    num_splits))."""
-    total = int(ctx.sum())
-    q = -(-total // num_splits)
-    prefix = np.concatenate([[0], np.cumsum(ctx.astype(np.int64))])
+    the sequence (boundaries of the documented plan)."""
+    plan = Plan(ctx, num_splits)
     cut = []
     for b in range(len(ctx)):
-        p0, p1 = int(prefix[b]), int(prefix[b] + ctx[b])
-        bounds = [m * q for m in range(p0 // q + 1, (p1 - 1) // q + 1)]
+        bounds = plan.cuts(b)
         if bounds:
-            cut.append((min(min(x - p0, p1 - x) for x in bounds), b))
+            cut.append((min(min(x, int(ctx[b]) - x) for x in bounds), b))
     return [b for _, b in sorted(cut)[:k]]
 
 

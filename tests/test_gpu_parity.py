@@ -14,6 +14,7 @@ import pytest
 import oracle
 import workloads as W
 from tests._metrics import scalar_err, vec_rel_err
+from tests.plan_ref import Plan
 
 pytestmark = pytest.mark.gpu
 
@@ -254,7 +255,7 @@ def test_combine_alone_against_oracle():
     import mla_latent_kv_02_amd as mla
     rng = np.random.default_rng(5)
     dims = mla.Dims(8, 64, 16, 32, 32)
-    ctx = np.array([10, 1, 35, 7], np.int32)
+    ctx = np.array([1000, 1, 3500, 700], np.int32)   # the third sequence meets five units
     num_splits = 6
     slots = mla.mla_num_partials(len(ctx), num_splits)
     u_norm = rng.standard_normal((slots, 1, 8, 64))
@@ -271,12 +272,11 @@ def test_combine_alone_against_oracle():
                     torch.from_numpy(rl).cuda(), u, lse_out)
     torch.cuda.synchronize()
     # slots of each sequence under the documented plan
-    total = int(ctx.sum())
-    q = -(-total // num_splits)
-    prefix = np.concatenate([[0], np.cumsum(ctx)])
+    plan = Plan(ctx, num_splits)
     base = 0
     for b in range(4):
-        n = (prefix[b] + ctx[b] - 1) // q - prefix[b] // q + 1
+        n = plan.parts[b]
+        assert plan.slot0[b] == base
         ref_u, ref_l = oracle.merge_partials(u_norm[base:base + n], lse[base:base + n])
         assert vec_rel_err(u[b].cpu().numpy(), ref_u) < 1e-5
         assert scalar_err(lse_out[b].cpu().numpy(), ref_l) < 1e-6
@@ -294,7 +294,7 @@ def test_combine_out_proj_against_oracle(num_splits):
     rng = np.random.default_rng(31 + num_splits)
     n_h, d_c, d_v, n_q = 16, 512, 128, 2
     dims = mla.Dims(n_h, d_c, 64, 128, d_v)
-    ctx = rng.integers(1, 400, size=40).astype(np.int32)
+    ctx = rng.integers(1, 4000, size=40).astype(np.int32)   # one to four partials a sequence
     ctx[3] = 1
     B = len(ctx)
     slots = mla.mla_num_partials(B, num_splits)
@@ -313,12 +313,11 @@ def test_combine_out_proj_against_oracle(num_splits):
                              torch.from_numpy(rl).cuda(), torch.from_numpy(wuv).cuda().bfloat16(), out, lse_out)
     torch.cuda.synchronize()
     out, lse_out = out.cpu().numpy(), lse_out.cpu().numpy()
-    total = int(ctx.sum())
-    q = -(-total // num_splits)
-    prefix = np.concatenate([[0], np.cumsum(ctx)])
+    plan = Plan(ctx, num_splits)
     base = 0
     for b in range(B):
-        n = (prefix[b] + ctx[b] - 1) // q - prefix[b] // q + 1
+        n = plan.parts[b]
+        assert plan.slot0[b] == base
         ref_u, ref_l = oracle.merge_partials(u_norm[base:base + n], lse[base:base + n])
         ref_o = oracle.value_up_projection(ref_u, wuv)
         assert vec_rel_err(out[b], ref_o) < 1e-4, b
