@@ -251,20 +251,51 @@ def copy_probe(mib):
     log(f"copy probe: 5 x {mib} MiB read + {mib} MiB written")
 
 
+PROBE_LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "workloads", "libmla_probe.so")
+
+
 def stream_probe(mib, flush_mib, reps=20):
-    """Plain HBM streaming rates: torch.sum over `mib` MiB (reads only) and
-    torch.neg into a second buffer (reads + writes), each rep timed with its
-    own events after the bench's flush.  Prints one JSON line."""
+    """Plain HBM streaming rates over `mib` MiB, each rep timed with its own
+    events after the bench's flush; prints one JSON line:
+      read, copy: torch.sum (reads only) and torch.neg into a second buffer
+        (reads + writes);
+      hip_read, hip_read_nt: 16-byte loads, 8 in flight per lane, over 256
+        workgroups of 4 waves, plain and non-temporal (workloads/stream_probe.hip);
+      rows_paged_nt: the decode kernel's stage loads (36 KiB stages of
+        1152-byte rows, 4-slot LDS ring, two barriers a stage) over 64-row
+        blocks in a seeded random order, non-temporal, with no work between."""
+    import ctypes
     import numpy as np
     import torch
     n = mib * (1 << 20) // 4
-    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (n,), dtype=torch.int32, device="cuda").view(torch.float32)
     dst = torch.empty_like(src)
     acc = torch.zeros((), dtype=torch.float32, device="cuda")
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
     flush = make_flush(flush_mib)
+    if not os.path.exists(PROBE_LIB):
+        raise RuntimeError(f"{PROBE_LIB} is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    lib.probe_stream_rows.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_void_p, ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    n_blocks = (n * 4 // 73728) // 128 * 128          # 64-row blocks of 1152 bytes, 2 stages each over 256 WGs
+    order = torch.from_numpy(np.random.default_rng(7).permutation(n_blocks).astype(np.int32)).cuda()
+
+    def call(status):
+        if status != 0:
+            raise RuntimeError(f"stream probe launch failed ({status})")
     out = {"probe": "hbm_stream", "mib": mib, "reps": reps, "flush_mib_per_rep": flush_mib}
-    for name, fn, nbytes in (("read", lambda: torch.sum(src, (0,), out=acc), n * 4),
-                             ("copy", lambda: torch.neg(src, out=dst), n * 8)):
+    for name, fn, nbytes in (
+            ("read", lambda: torch.sum(src, (0,), out=acc), n * 4),
+            ("copy", lambda: torch.neg(src, out=dst), n * 8),
+            ("hip_read", lambda: call(lib.probe_stream_read(src.data_ptr(), n * 4, 0, sink.data_ptr(), stream)), n * 4),
+            ("hip_read_nt", lambda: call(lib.probe_stream_read(src.data_ptr(), n * 4, 1, sink.data_ptr(), stream)),
+             n * 4),
+            ("rows_paged_nt", lambda: call(lib.probe_stream_rows(src.data_ptr(), order.data_ptr(), n_blocks, 1,
+                                                                 sink.data_ptr(), stream)), n_blocks * 73728)):
         ts = []
         for r in range(reps + 3):
             flush()

@@ -3,8 +3,9 @@
     python -m mla_latent_kv_02_amd.build
 
 produces mla_latent_kv_02_amd/libmla.so (the MLA decode library behind
-include/mla.h) and workloads/libmla_synth.so (the device side of the seeded
-input generator).  Every call recompiles.
+include/mla.h), workloads/libmla_synth.so (the device side of the seeded
+input generator) and workloads/libmla_probe.so (the bench's HBM streaming
+probes).  Every call recompiles.
 """
 from __future__ import annotations
 
@@ -21,6 +22,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla.so")
 SYNTH_SRC = os.path.join(ROOT, "workloads", "synth_fill.hip")
 SYNTH_LIB = os.path.join(ROOT, "workloads", "libmla_synth.so")
+PROBE_SRC = os.path.join(ROOT, "workloads", "stream_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "workloads", "libmla_probe.so")
 
 ARCH = "gfx950"
 # No packed-fp32 instructions anywhere.
@@ -55,7 +58,8 @@ def _run(cmd):
 
 
 def build(verbose: bool = False, jobs: int = 4, lib_path: str = LIB, host_flags=(), synth: bool = True) -> None:
-    """Compile libmla.so (to ``lib_path``) and, with ``synth``, libmla_synth.so.
+    """Compile libmla.so (to ``lib_path``) and, with ``synth``, libmla_synth.so
+    and libmla_probe.so.
     ``host_flags`` go to the host side of every compile and the link (each one
     behind -Xarch_host, e.g. sanitizers for a host-checking build)."""
     hipcc = _hipcc()
@@ -80,8 +84,13 @@ def build(verbose: bool = False, jobs: int = 4, lib_path: str = LIB, host_flags=
         tmp_synth = SYNTH_LIB + ".tmp"
         _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_synth, synth_obj])
         os.replace(tmp_synth, SYNTH_LIB)
+        probe_obj = os.path.join(tmp, "probe.o")
+        _run([hipcc, *DEVICE_FLAGS, "-c", PROBE_SRC, "-o", probe_obj])
+        tmp_probe = PROBE_LIB + ".tmp"
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_probe, probe_obj])
+        os.replace(tmp_probe, PROBE_LIB)
     if verbose:
-        print(f"built {LIB} and {SYNTH_LIB}")
+        print(f"built {LIB}, {SYNTH_LIB} and {PROBE_LIB}")
 
 
 if __name__ == "__main__":
