@@ -301,7 +301,10 @@ mla_status_t mla_fold_out(const mla_dims_t *dims, int32_t d_model, const void *w
                           void *w_comb, void *stream);
 /* Layer output through the fold: y[b][j][:] = sum_i u[b][j][i][:] W_i,comb.
  *   u [B][n_q][n_h][d_c] fp32 (split into bf16 high + residual, ~fp32 accuracy),
- *   y [B][n_q][d_model] fp32, out. */
+ *   y [B][n_q][d_model] fp32, out.
+ * For few rows the contraction is cut into slices added into y with atomic
+ * adds (y is cleared first), in no fixed order: y can differ in its last bits
+ * from call to call.  The same holds for mla_o_proj. */
 mla_status_t mla_out_proj_folded(const mla_dims_t *dims, int32_t d_model, int32_t B, int32_t n_q,
                                  const float *u, const void *w_comb, float *y, void *stream);
 /* The same layer output without the fold: y[b][j][:] = sum_i o[b][j][i][:] W_i^O,

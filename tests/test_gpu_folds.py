@@ -96,3 +96,48 @@ def test_query_fold_and_folded_absorption():
     e_kq = np.abs(got - want).max() / np.abs(want).max()
     print(f"  q_lat {e_lat:.2e}, q_pe {e_pe:.2e}, W_KQ samples {e_kq:.2e}", flush=True)
     assert e_lat <= 1e-2 and e_pe <= 1e-2 and e_kq <= 1e-2
+
+
+def test_products_over_ragged_tiles_and_k_slices():
+    """The per-step products at shapes that cut their tiles: 70 query rows (a
+    second, ragged 64-row tile), d_model 300 (a 256-column tile and a ragged
+    one in which three of the four waves hold no column), K = n_h d_v = 16384
+    and n_h d_c = 65536 cut into slices added into C (fp32 C), and the folded
+    absorption's 128 head products over 70 rows (bf16 C, one slice)."""
+    _need_gpu()
+    import mla_latent_kv_02_amd as mla
+    from workloads.device import dims_of
+    w = W.custom(name="fold_tiles", seed=54, batch=35, n_q=2, ctx=1)
+    dims = dims_of(w)
+    d_model, d_q = 300, 1536
+    rng = np.random.default_rng(55)
+    w_uv = W.weights(w)["w_uv"]
+    w_o = W.round_to_bf16((rng.standard_normal((w.n_h, w.d_v, d_model)) /
+                           np.sqrt(w.n_h * w.d_v)).astype(np.float32))
+    u = rng.standard_normal((w.batch, w.n_q, w.n_h, w.d_c)).astype(np.float32)
+    o = rng.standard_normal((w.batch, w.n_q, w.n_h, w.d_v)).astype(np.float32)
+    w_uv_d, w_o_d = _dev_bf16(w_uv), _dev_bf16(w_o.transpose(2, 0, 1))
+    y_o = torch.full((w.batch, w.n_q, d_model), float("nan"), device="cuda")
+    mla.mla_o_proj(dims, torch.from_numpy(o).cuda(), w_o_d, y_o)
+    w_comb = torch.empty((d_model, w.n_h, w.d_c), dtype=torch.bfloat16, device="cuda")
+    mla.mla_fold_out(dims, w_uv_d, w_o_d, w_comb)
+    y_f = torch.full((w.batch, w.n_q, d_model), float("nan"), device="cuda")
+    mla.mla_out_proj_folded(dims, torch.from_numpy(u).cuda(), w_comb, y_f)
+    w_uk = W.weights(w)["w_uk"]
+    w_uq = W.round_to_bf16((rng.standard_normal((w.n_h, d_q, w.d_nope)) / np.sqrt(d_q)).astype(np.float32))
+    c_q = W.round_to_bf16(rng.standard_normal((w.batch, w.n_q, d_q)).astype(np.float32))
+    q_rope = W.round_to_bf16(rng.standard_normal((w.batch, w.n_q, w.n_h, w.d_rope)).astype(np.float32))
+    pos = rng.integers(0, 100000, size=(w.batch, w.n_q)).astype(np.int32)
+    w_kq = torch.empty((w.n_h, w.d_c, d_q), dtype=torch.bfloat16, device="cuda")
+    mla.mla_fold_q(dims, _dev_bf16(w_uq.transpose(1, 0, 2)), _dev_bf16(w_uk), w_kq)
+    q_lat = torch.full((w.batch, w.n_q, w.n_h, w.d_c), float("nan"), dtype=torch.bfloat16, device="cuda")
+    q_pe = torch.empty((w.batch, w.n_q, w.n_h, w.d_rope), dtype=torch.bfloat16, device="cuda")
+    mla.mla_absorb_q_folded(dims, _dev_bf16(c_q), _dev_bf16(q_rope), torch.from_numpy(pos).cuda(), w_kq, q_lat, q_pe)
+    torch.cuda.synchronize()
+    e_o = vec_rel_err(y_o.cpu().numpy(), oracle.output_projection(o.astype(np.float64), w_o))
+    ref_f = oracle.output_projection(oracle.value_up_projection(u.astype(np.float64), w_uv), w_o)
+    e_f = vec_rel_err(y_f.cpu().numpy(), ref_f)
+    ref_lat = oracle.absorb_query(oracle.query_from_compressed(c_q.astype(np.float64), w_uq), w_uk)
+    e_lat = vec_rel_err(q_lat.float().cpu().numpy(), ref_lat)
+    print(f"  o W_O^T {e_o:.2e}, u W_comb^T {e_f:.2e}, c_q W_KQ^T {e_lat:.2e}", flush=True)
+    assert e_o <= 1e-2 and e_f <= 1e-2 and e_lat <= 1e-2
