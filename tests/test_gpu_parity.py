@@ -284,6 +284,49 @@ def test_combine_alone_against_oracle():
     assert base <= slots
 
 
+@pytest.mark.parametrize("num_splits", [7, 50])
+def test_decode_partials_follow_the_documented_plan(num_splits):
+    """mla_decode writes sequence b's partials to the slots the documented
+    plan gives it (tests/plan_ref.py) and to no other slot: with u_part and
+    lse_part poisoned with NaN, every slot past the plan's count stays NaN,
+    and each sequence's slots, normalised (u_part exp(r - lse)) and merged by
+    the oracle, give the oracle's u and lse for that sequence.  Ragged
+    contexts with empty ones, so that units start inside sequences and the
+    cost of the extra segments moves the cuts."""
+    _need_gpu()
+    from mla_latent_kv_02_amd.step import DecodeStep
+    from workloads.device import stage
+    w = W.custom(name="plan_slots", seed=61, batch=12, n_q=1, ctx=None, ctx_range=(1, 700))
+    ctx = W.context_lengths(w).copy()
+    ctx[[3, 8]] = 0
+    ctx[5] = 1
+    st = stage(w, ctx=ctx)
+    step = DecodeStep(st["dims"], w.batch, w.n_q, num_splits, torch.bfloat16)
+    step.u_part.fill_(float("nan"))
+    step.lse_part.fill_(float("nan"))
+    step.run(st["q_nope"], st["q_rope"], st["positions"], st["w_uk"], st["w_uv"], st["cache"])
+    torch.cuda.synchronize()
+    u_part = step.u_part.cpu().numpy().astype(np.float64)
+    rl = step.lse_part.cpu().numpy().astype(np.float64)
+    plan = Plan(ctx, num_splits)
+    used = sum(plan.parts)
+    assert plan.cost_total > int(ctx.sum())                      # some unit starts inside a sequence
+    assert np.isnan(rl[used:]).all() and np.isnan(u_part[used:]).all()
+    assert not np.isnan(rl[:used]).any() and not np.isnan(u_part[:used]).any()
+    for b in range(w.batch):
+        if ctx[b] == 0:
+            assert plan.parts[b] == 0
+            continue
+        sl = slice(plan.slot0[b], plan.slot0[b] + plan.parts[b])
+        r, lse = rl[sl, ..., 0], rl[sl, ..., 1]
+        fin = np.isfinite(lse)
+        u_norm = np.where(fin[..., None], u_part[sl] * np.exp(np.where(fin, r - lse, 0.0))[..., None], 0.0)
+        u_m, lse_m = oracle.merge_partials(u_norm, lse)
+        ref = _oracle(w, st, b)
+        assert vec_rel_err(u_m, ref["u"]) <= 1e-2, b
+        assert scalar_err(lse_m, ref["lse"]) <= 1e-2, b
+
+
 @pytest.mark.parametrize("num_splits", [1, 7, 50])
 def test_combine_out_proj_against_oracle(num_splits):
     """mla_combine_out_proj on partials in the documented format, 80 query rows
