@@ -184,6 +184,9 @@ __global__ __launch_bounds__(256) void absorb_rope_kernel(AbsorbParams p, Append
     return;
   }
   __shared__ double theta[64];
+  // per wave: a 64-row x 64-latent block of q_lat (bf16, 128 bytes a row,
+  // 16-byte chunk c of row r at c ^ (r % 8)) on its way to memory
+  __shared__ __attribute__((aligned(16))) unsigned char qout[4][64 * 128];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nslices = p.d_c / AR_LAT;
   const int i = blockIdx.x / nslices, h2 = blockIdx.x % nslices;
@@ -264,9 +267,15 @@ __global__ __launch_bounds__(256) void absorb_rope_kernel(AbsorbParams p, Append
     // the next block's query rows are in flight while this block is computed
     u16x8 bn[4][4];
     if (m0 + 64 < M) load_b(m0 + 64, bn);
+    // the block's results go through this wave's LDS block, so that each
+    // store writes 8 rows x 128 contiguous bytes (from the registers a store
+    // would carry 8 bytes of each of 64 rows)
+    typedef __attribute__((address_space(3))) u16x4 lds_u16x4;
+    typedef __attribute__((address_space(3))) const u32x4 lds_cu32x4;
+    unsigned char* qo = qout[wave];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const int m = m0 + 16 * mt + l16;
+      const int r = 16 * mt + l16;
       f32x4 acc[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -276,15 +285,25 @@ __global__ __launch_bounds__(256) void absorb_rope_kernel(AbsorbParams p, Append
           acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[t][ks]),
                                                            __builtin_bit_cast(bf16x8, bq[mt][ks]), acc[t], 0, 0, 0);
       }
-      if (m < M) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const u16x4 o4 = {f32_to_bf16(acc[t][0]), f32_to_bf16(acc[t][1]), f32_to_bf16(acc[t][2]),
-                            f32_to_bf16(acc[t][3])};
-          *reinterpret_cast<u16x4*>(out + ((int64_t)m * p.n_h + i) * p.d_c + c0 + 16 * t + 4 * g) = o4;
-        }
+      for (int t = 0; t < 4; ++t) {
+        // latents 16t + 4g .. +3 of row r: chunk 2t + g/2, bytes 8(g%2) of it
+        const u16x4 o4 = {f32_to_bf16(acc[t][0]), f32_to_bf16(acc[t][1]), f32_to_bf16(acc[t][2]),
+                          f32_to_bf16(acc[t][3])};
+        const int c = 2 * t + (g >> 1);
+        *(lds_u16x4*)((__attribute__((address_space(3))) unsigned char*)(qo + r * 128 + ((c ^ (r & 7)) << 4) +
+                                                                          8 * (g & 1))) = o4;
       }
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's block is in (only it reads it)
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int r = 8 * it + (lane >> 3), c = lane & 7;
+      const u32x4 v = *(lds_cu32x4*)((__attribute__((address_space(3))) unsigned char*)(qo + r * 128 +
+                                                                                        ((c ^ (r & 7)) << 4)));
+      if (m0 + r < M) *reinterpret_cast<u32x4*>(out + ((int64_t)(m0 + r) * p.n_h + i) * p.d_c + c0 + 8 * c) = v;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next block's writes
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
