@@ -312,6 +312,40 @@ def stream_probe(mib, flush_mib, reps=20):
     print(json.dumps(out), flush=True)
 
 
+def rows_stream_rate(flush, mib=2048, reps=10):
+    """The decode kernel's own load schedule at memory speed: median GB/s of
+    probe_stream_rows (36 KiB stages of 1152-byte rows over randomly ordered
+    64-row blocks, non-temporal, no work between) over `mib` MiB of random
+    data, each rep after the bench's flush.  The practical rate the decode's
+    counter traffic is set against."""
+    import ctypes
+    import numpy as np
+    import torch
+    if not os.path.exists(PROBE_LIB):
+        raise RuntimeError(f"{PROBE_LIB} is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.probe_stream_rows.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_void_p, ctypes.c_void_p]
+    n_blocks = (mib * (1 << 20) // 73728) // 128 * 128
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (n_blocks * 73728 // 4,), dtype=torch.int32, device="cuda")
+    order = torch.from_numpy(np.random.default_rng(7).permutation(n_blocks).astype(np.int32)).cuda()
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    rates = []
+    for r in range(reps + 2):
+        flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        if lib.probe_stream_rows(src.data_ptr(), order.data_ptr(), n_blocks, 1, sink.data_ptr(), stream) != 0:
+            raise RuntimeError("stream probe launch failed")
+        e1.record()
+        torch.cuda.synchronize()
+        if r >= 2:
+            rates.append(n_blocks * 73728 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del src
+    return float(np.median(rates))
+
+
 def make_flush(mib, kind="rw+read"):
     """An untimed flush of the GPU caches before a timed rep.
 
@@ -776,6 +810,16 @@ def main():
                      "launches_timed": len(dec_ms)},
         "cpu_baseline": None,
     }
+    # the chip's practical streaming rate for the decode's access pattern, measured here
+    rate = rows_stream_rate(flush)
+    traffic = result["roofline"]["traffic"]
+    result["roofline"]["practical"] = {
+        "probe": "the decode's stage loads over randomly ordered 64-row blocks of 1152-byte rows, non-temporal, "
+                 "no work between (workloads/stream_probe.hip), median GB/s after the flush",
+        "gbs": round(rate, 1),
+        "frac_algorithmic": round(achieved / rate, 4),
+        "frac_traffic": round(traffic / (dec_avg * 1e-3) / 1e9 / rate, 4) if traffic else None}
+    log(f"decode load schedule at memory speed: {rate:.0f} GB/s")
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a CPU sample")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
