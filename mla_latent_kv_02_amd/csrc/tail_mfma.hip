@@ -5,18 +5,28 @@
 // over the partials k of a query row -- the softmax over the union of the
 // partials' token ranges ([Ikmyung] §1.4).  The merged u is never written.
 //
-// Workgroup = (head i, block of up to 32 query rows; fewer when the batch is
-// small, so that the workgroups cover the CUs), all d_v = 128 value columns.
-// Wave w owns the contraction slice d_c*w/4 .. d_c*(w+1)/4 (<= 128 latents):
-//   1. its W_i^UV rows are staged in LDS (global->LDS loads, 16-byte chunks
-//      xor-swizzled by row so that transposed reads hit distinct banks);
+// Workgroup = (head i, NTEAM blocks of up to 32 query rows; fewer when the
+// batch is small, so that the workgroups cover the CUs), all d_v = 128 value
+// columns, NTEAM teams of 4 waves.  Team t takes row block t; wave w of a
+// team owns the contraction slice d_c*w/4 .. d_c*(w+1)/4 (<= 128 latents):
+//   1. W_i^UV is staged in LDS once for all teams (global->LDS loads, 16-byte
+//      chunks xor-swizzled by row so that transposed reads hit distinct
+//      banks), and the plan walk (the slots of the rows' partials) is done
+//      once for the workgroup's rows;
 //   2. each lane builds its row's slice of u in fp32 registers (64 values per
 //      lane: row lane%32, latents 16*ks + 8*(lane/32) + 0..7), reading every
 //      partial element once, all 16 loads of one partial in flight together;
 //   3. u is split into a bf16 high part and a bf16 residual (u = hi + lo to
 //      ~2^-16 relative) and both are multiplied with MFMA 32x32x16 against
 //      W^UV read transposed from LDS (ds_read_b64_tr_b16), fp32 accumulation;
-//   4. the four waves' partial products are summed through LDS.
+//   4. the four waves' partial products of a team are summed through LDS.
+// One team (4 waves, one per SIMD) keeps two partials in flight per lane.
+// Batches that would need more than one round of such workgroups over the
+// 256 CUs (more than 64 rows at 128 heads) take two teams: the W^UV staging
+// and the plan walk are shared by twice the rows, and the rounds halve; two
+// waves then share each SIMD, so a lane keeps one partial in flight (the
+// registers of a second do not fit), and the teams keep in step at the
+// workgroup barriers.
 
 #include "mla_device.h"
 #include "launch.h"
@@ -24,52 +34,59 @@
 namespace mla {
 namespace {
 
-constexpr int NT = 256;
-constexpr int TR = 32;            // query rows of the MFMA tile (M), and the most a workgroup takes
+constexpr int TR = 32;            // query rows of the MFMA tile (M), and the most a team takes
 constexpr int TDV = 128;          // value columns (4 MFMA column blocks of 32)
 constexpr int TKW = 128;          // contraction rows per wave (d_c / 4)
 constexpr int TKS = TKW / 16;     // MFMA k-steps per wave
 constexpr int TROWB = TDV * 2;    // bytes of one W^UV row
 
+template <int NTEAM>
 struct __attribute__((aligned(16))) TailSmem {
   union {
-    unsigned char w[4][TKW * TROWB];   // 4 x 32 KiB: each wave's W^UV rows
-    float red[4][4][16][64];           // 64 KiB: each wave's [col block][acc reg][lane]
+    unsigned char w[4][TKW * TROWB];   // 4 x 32 KiB: the W^UV rows of each contraction slice
+    float red[NTEAM][4][4][16][64];    // 64 KiB per team: each wave's [col block][acc reg][lane]
   };
-  int32_t slot0[TR];
-  int32_t nparts[TR];
-  PlanScratch<NT> plan;
+  int32_t slot0[NTEAM * TR];           // the workgroup's sequences (at most NTEAM * R of them)
+  int32_t nparts[NTEAM * TR];
+  PlanScratch<256 * NTEAM> plan;
 };
+static_assert(sizeof(TailSmem<2>) <= 160 * 1024, "LDS budget");
 
 // chunk xor of W^UV row r: a transposed read covers 4 consecutive rows x 4
 // chunks (one aligned group of 4); the xor by 4(r%4) gives each row its own group
 __device__ __forceinline__ int wswz(int r) { return 4 * (r & 3); }
 
-template <bool PARTIALS>
-__global__ __launch_bounds__(NT, 1) void tail_kernel(TailParams p, int items_pad, int rows_per_block) {
-  __shared__ TailSmem sm;
+template <bool PARTIALS, int NTEAM>
+__global__ __launch_bounds__(256 * NTEAM, 1) void tail_kernel(TailParams p, int items_pad, int rows_per_block) {
+  constexpr int NT = 256 * NTEAM;
+  __shared__ TailSmem<NTEAM> sm;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave8 = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int team = wave8 >> 2;               // row block of the workgroup
+  const int wave = wave8 & 3;                // contraction slice
   const int M = p.B * p.n_q;
-  const int R = rows_per_block;              // a power of two <= TR
-  const int rblocks = (M + R - 1) / R;
-  // block -> (head, row block); consecutive items on one XCD (block b runs on
-  // XCD b % 8), so the row blocks of a head share its weights in L2
+  const int R = rows_per_block;              // rows per team, a power of two <= TR
+  const int rblocks = (M + NTEAM * R - 1) / (NTEAM * R);
+  // block -> (head, pair of row blocks); consecutive items on one XCD (block b
+  // runs on XCD b % 8), so the row blocks of a head share its weights in L2
   const int item = (blockIdx.x & 7) * (items_pad / 8) + (blockIdx.x >> 3);
   if (item >= p.n_h * rblocks) return;
   const int ih = item / rblocks;
-  const int m0 = (item % rblocks) * R;
+  const int mw0 = (item % rblocks) * NTEAM * R;   // first row of the workgroup
+  const int m0 = mw0 + team * R;                  // first row of this team
   const int k0 = wave * TKW;                 // first latent of this wave's slice
   // the sequence lengths for the plan, loaded ahead of the weights
   const int len_tid = PARTIALS && (int)threadIdx.x < p.B ? p.ctx_lens[threadIdx.x] : 0;
 
-  // ---- 1. this wave's W^UV rows into LDS (4 rows of 256 B per instruction)
+  // ---- 1. W^UV rows of slice `wave` into LDS, 4 rows of 256 B per
+  // instruction: team t stages rows (128/NTEAM) t .. (128/NTEAM)(t+1) - 1 of the slice
   {
     const unsigned char* src = static_cast<const unsigned char*>(p.w_uv) + ((int64_t)ih * p.d_c + k0) * TROWB;
     unsigned char* dst = sm.w[wave];
     const int rr = lane >> 4, pos = lane & 15;
 #pragma unroll 4
-    for (int it = 0; it < TKW / 4; ++it) {
+    for (int i = 0; i < TKW / 4 / NTEAM; ++i) {
+      const int it = team * (TKW / 4 / NTEAM) + i;
       const int r = 4 * it + rr;
       __builtin_amdgcn_global_load_lds(src + r * TROWB + ((pos ^ wswz(r)) << 4), (lds_void*)(dst + it * 1024),
                                        16, 0, 0);
@@ -81,7 +98,7 @@ __global__ __launch_bounds__(NT, 1) void tail_kernel(TailParams p, int items_pad
   // two): replica j of a row takes the partials k = j, j+rep, ... and the
   // replicas are summed with lane exchanges before the MFMAs (rows past the
   // block end carry copies that are never stored).
-  const int rows_here = (M - m0) < R ? (M - m0) : R;
+  const int rows_here = (M - m0) < R ? (M - m0) : R;   // <= 0: a team past the batch end
   int prow2 = 1;
   while (prow2 < rows_here) prow2 <<= 1;
   const int rep = PARTIALS ? TR / prow2 : 1;
@@ -92,9 +109,9 @@ __global__ __launch_bounds__(NT, 1) void tail_kernel(TailParams p, int items_pad
   const bool mvalid = m < M;
   float L = 0.f;
   int slot0 = 0, np = 1;
-  const int b_lo = m0 / p.n_q;
+  const int b_lo = mw0 / p.n_q;            // the workgroup's first sequence
   if (PARTIALS) {
-    const int b_hi = ((M < m0 + R ? M : m0 + R) - 1) / p.n_q;
+    const int b_hi = ((M < mw0 + NTEAM * R ? M : mw0 + NTEAM * R) - 1) / p.n_q;
     plan_slot_range<NT>(p.ctx_lens, p.B, p.num_splits, b_lo, b_hi - b_lo + 1, len_tid, &sm.plan, sm.slot0,
                         sm.nparts);
   }
@@ -115,12 +132,14 @@ __global__ __launch_bounds__(NT, 1) void tail_kernel(TailParams p, int items_pad
     // rescaled whenever mx grows; then L = mx + log s and u = acc / s.  Every
     // r_k <= lse_k, so no weight exceeds 1.
     const float2* lp = reinterpret_cast<const float2*>(p.lse_part);
-    // this lane's partials: k = replica + j*rep, j = 0 .. nj-1.  Partial j is
-    // fetched into buffer j%2 while partial j-1 is merged, so two partials are
-    // in flight.  The loads of a fetch are unconditional (a lane past its last
-    // partial re-reads row 0 and ignores it), so every wait is for exactly the
-    // older buffer.
+    // this lane's partials: k = replica + j*rep, j = 0 .. nj-1, one in flight
+    // per lane (two waves share a SIMD, so a CU still has 8 waves' loads in
+    // flight); partial j+1 is fetched as soon as partial j is merged.
     const int nj = replica < np ? (np - replica + rep - 1) / rep : 0;
+    // (one team: partial j is fetched into buffer j%2 while partial j-1 is
+    // merged; the loads of a fetch are unconditional, a lane past its last
+    // partial re-reading row 0 and ignoring it, so every wait is for exactly
+    // the older buffer)
     auto fetch = [&](int j, f32x4* v, float2& rl) {
       const int64_t prow = j < nj ? (int64_t)(slot0 + replica + j * rep) * rows_per_slot + rowid : 0;
       rl = lp[prow];
@@ -132,33 +151,44 @@ __global__ __launch_bounds__(NT, 1) void tail_kernel(TailParams p, int items_pad
       }
     };
     float mx = -INFINITY, sum = 0.f;
+    // branch-free, so that u keeps its registers through the loop: a partial
+    // past the lane's last one, or with no visible token, gets weight 0 and
+    // leaves mx (and the scale 1) unchanged
     auto merge = [&](int j, const f32x4* v, float2 rl) {
-      if (j >= nj || rl.y == -INFINITY) return;    // past the lane's partials, or no visible token
-      if (rl.y > mx) {
-        const float sc = __expf(mx - rl.y);        // 0 while mx is -inf
-        sum *= sc;
+      const bool ok = j < nj && rl.y != -INFINITY;
+      const float nm = ok ? fmaxf(mx, rl.y) : mx;
+      const float sc = nm == mx ? 1.f : __expf(mx - nm);   // 0 while mx is -inf
+      const float wk = ok ? __expf(rl.x - nm) : 0.f;
+      sum = sum * sc + (ok ? __expf(rl.y - nm) : 0.f);
 #pragma unroll
-        for (int e = 0; e < 2 * TKS; ++e) u[e] *= sc;
-        mx = rl.y;
-      }
-      sum += __expf(rl.y - mx);
-      const float wk = __expf(rl.x - mx);
-#pragma unroll
-      for (int e = 0; e < 2 * TKS; ++e) u[e] += wk * v[e];
+      for (int e = 0; e < 2 * TKS; ++e) u[e] = u[e] * sc + wk * v[e];
+      mx = nm;
     };
-    f32x4 va[2 * TKS], vb[2 * TKS];
-    float2 ra, rb;
-    fetch(0, va, ra);
-    fetch(1, vb, rb);
-    int j = 0;
-    for (; j + 2 < nj; j += 2) {
+    if constexpr (NTEAM == 1) {
+      f32x4 va[2 * TKS], vb[2 * TKS];
+      float2 ra, rb;
+      fetch(0, va, ra);
+      fetch(1, vb, rb);
+      int j = 0;
+      for (; j + 2 < nj; j += 2) {
+        merge(j, va, ra);
+        fetch(j + 2, va, ra);
+        merge(j + 1, vb, rb);
+        fetch(j + 3, vb, rb);
+      }
       merge(j, va, ra);
-      fetch(j + 2, va, ra);
       merge(j + 1, vb, rb);
-      fetch(j + 3, vb, rb);
+    } else {
+      f32x4 va[2 * TKS];
+      float2 ra;
+      fetch(0, va, ra);
+      for (int j = 0; j < nj; ++j) {
+        merge(j, va, ra);
+        // (keeps the next loads behind the merge: one buffer's worth of registers)
+        __builtin_amdgcn_sched_barrier(0);
+        if (j + 1 < nj) fetch(j + 1, va, ra);
+      }
     }
-    merge(j, va, ra);
-    merge(j + 1, vb, rb);
     // merge the replicas of the row (lanes xor prow2, 2*prow2, ... within the half)
     for (int sh = prow2; sh < TR; sh <<= 1) {
       const float mo = __shfl_xor(mx, sh, 64);
@@ -189,6 +219,7 @@ __global__ __launch_bounds__(NT, 1) void tail_kernel(TailParams p, int items_pad
 
   // ---- 3. MFMA: acc[nb] (rows x value columns 32nb..32nb+31) += u_slice . W^UV_slice
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's staged W^UV rows have landed
+  if constexpr (NTEAM > 1) __syncthreads();   // and the other teams' parts of the slice
   const int g4 = lane >> 4, j = lane & 15;
   f32x16 acc[4];
 #pragma unroll
@@ -223,18 +254,20 @@ __global__ __launch_bounds__(NT, 1) void tail_kernel(TailParams p, int items_pad
     }
   }
 
-  // ---- 4. sum the four waves' products; acc[nb][i] = o[row 8(i/4) + 4(lane/32) + i%4][32nb + lane%32]
-  __syncthreads();   // every wave is done with its W^UV rows (the buffer is reused)
+  // ---- 4. sum the team's four products; acc[nb][i] = o[row 8(i/4) + 4(lane/32) + i%4][32nb + lane%32]
+  __syncthreads();   // every wave is done with the W^UV rows (the buffer is reused)
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sm.red[wave][nb][i][lane] = acc[nb][i];
+    for (int i = 0; i < 16; ++i) sm.red[team][wave][nb][i][lane] = acc[nb][i];
   __syncthreads();
+  const int ttid = tid & (NT / NTEAM - 1);   // thread within the team
+  const auto& red = sm.red[team];
 #pragma unroll 4
   for (int q = 0; q < 16; ++q) {
-    const int idx = q * NT + tid;
+    const int idx = q * (NT / NTEAM) + ttid;
     const int nb = idx >> 10, i = (idx >> 6) & 15, l = idx & 63;
-    const float v = sm.red[0][nb][i][l] + sm.red[1][nb][i][l] + sm.red[2][nb][i][l] + sm.red[3][nb][i][l];
+    const float v = red[0][nb][i][l] + red[1][nb][i][l] + red[2][nb][i][l] + red[3][nb][i][l];
     const int rr = 8 * (i >> 2) + 4 * (l >> 5) + (i & 3);   // MFMA row = the lane of the A operand
     const int mm = m0 + rr;
     if (rr < rows_here) p.out[((int64_t)mm * p.n_h + ih) * TDV + 32 * nb + (l & 31)] = v;
@@ -250,17 +283,24 @@ bool tail_mfma_ok(int d_c, int d_v, bool bf16_weights) {
 
 hipError_t launch_tail_mfma(const TailParams& p, bool from_partials, hipStream_t stream) {
   const int M = p.B * p.n_q;
-  // Blocks of fewer rows when the batch is small, so that the workgroups
-  // cover the 256 CUs (the spare lanes of a block take shares of its rows'
-  // partials, as replicas).
+  // Two teams when one-team workgroups of 32 rows would take more than one
+  // round over the 256 CUs.  Blocks of fewer rows when the batch is small, so
+  // that the workgroups cover the CUs (the spare lanes of a block take shares
+  // of its rows' partials, as replicas).  A workgroup takes nteam blocks of R rows.
+  const int nteam = (int64_t)p.n_h * ((M + TR - 1) / TR) > 256 ? 2 : 1;
   int R = TR;
-  while (R > 1 && (int64_t)p.n_h * ((M + R - 1) / R) < 256) R >>= 1;
-  const int items = p.n_h * ((M + R - 1) / R);
+  while (R > 1 && (int64_t)p.n_h * ((M + nteam * R - 1) / (nteam * R)) < 256) R >>= 1;
+  const int items = p.n_h * ((M + nteam * R - 1) / (nteam * R));
   const int items_pad = (items + 7) / 8 * 8;
-  if (from_partials)
-    hipLaunchKernelGGL(tail_kernel<true>, dim3(items_pad), dim3(NT), 0, stream, p, items_pad, R);
+  const dim3 grid(items_pad), block(256 * nteam);
+  if (from_partials && nteam == 2)
+    hipLaunchKernelGGL((tail_kernel<true, 2>), grid, block, 0, stream, p, items_pad, R);
+  else if (from_partials)
+    hipLaunchKernelGGL((tail_kernel<true, 1>), grid, block, 0, stream, p, items_pad, R);
+  else if (nteam == 2)
+    hipLaunchKernelGGL((tail_kernel<false, 2>), grid, block, 0, stream, p, items_pad, R);
   else
-    hipLaunchKernelGGL(tail_kernel<false>, dim3(items_pad), dim3(NT), 0, stream, p, items_pad, R);
+    hipLaunchKernelGGL((tail_kernel<false, 1>), grid, block, 0, stream, p, items_pad, R);
   return hipGetLastError();
 }
 

@@ -327,19 +327,27 @@ def test_decode_partials_follow_the_documented_plan(num_splits):
         assert scalar_err(lse_m, ref["lse"]) <= 1e-2, b
 
 
+# (heads, sequences), two query tokens each: 16 x 40 -> 80 query rows in blocks
+# of 4 with eight lanes per row, workgroups of one row block; the others take
+# workgroups of two row blocks (one-block workgroups of 32 rows would need more
+# than one round over 256 CUs):
+# 128 x 55 -> 110 rows, the second workgroup's second block ragged (14 rows);
+# 128 x 45 -> 90 rows, the second workgroup's second block past the batch end;
+# 96 x 50 -> 100 rows in blocks of 16 with two lanes per row, the last
+# workgroup's second block past the end.
+@pytest.mark.parametrize("n_h,B", [(16, 40), (128, 55), (128, 45), (96, 50)])
 @pytest.mark.parametrize("num_splits", [1, 7, 50])
-def test_combine_out_proj_against_oracle(num_splits):
-    """mla_combine_out_proj on partials in the documented format, 80 query rows
-    (three 32-row blocks, the last one ragged), one empty partial: against the
-    oracle's merge of the normalised partials followed by its W_UV product."""
+def test_combine_out_proj_against_oracle(num_splits, n_h, B):
+    """mla_combine_out_proj on partials in the documented format, two query
+    tokens a sequence, one empty partial: against the oracle's merge of the
+    normalised partials followed by its W_UV product."""
     _need_gpu()
     import mla_latent_kv_02_amd as mla
-    rng = np.random.default_rng(31 + num_splits)
-    n_h, d_c, d_v, n_q = 16, 512, 128, 2
+    rng = np.random.default_rng(31 + num_splits + n_h + B)
+    d_c, d_v, n_q = 512, 128, 2
     dims = mla.Dims(n_h, d_c, 64, 128, d_v)
-    ctx = rng.integers(1, 4000, size=40).astype(np.int32)   # one to four partials a sequence
+    ctx = rng.integers(1, 4000, size=B).astype(np.int32)   # one to four partials a sequence
     ctx[3] = 1
-    B = len(ctx)
     slots = mla.mla_num_partials(B, num_splits)
     u_norm = rng.standard_normal((slots, n_q, n_h, d_c))
     lse = rng.standard_normal((slots, n_q, n_h)) * 4
@@ -369,14 +377,17 @@ def test_combine_out_proj_against_oracle(num_splits):
     assert base <= slots
 
 
-def test_out_proj_alone_against_oracle():
+# 16 heads x 10 rows: workgroups of one row block; 128 heads x 90 rows:
+# workgroups of two, the last one's second block past the batch end
+@pytest.mark.parametrize("n_h,B", [(16, 5), (128, 45)])
+def test_out_proj_alone_against_oracle(n_h, B):
     _need_gpu()
     import mla_latent_kv_02_amd as mla
-    rng = np.random.default_rng(6)
-    dims = mla.Dims(16, 512, 64, 128, 128)
-    u = rng.standard_normal((5, 2, 16, 512)).astype(np.float32)
-    wuv = W.round_to_bf16((rng.standard_normal((16, 512, 128)) / np.sqrt(512)).astype(np.float32))
-    out = torch.empty((5, 2, 16, 128), device="cuda")
+    rng = np.random.default_rng(6 + n_h)
+    dims = mla.Dims(n_h, 512, 64, 128, 128)
+    u = rng.standard_normal((B, 2, n_h, 512)).astype(np.float32)
+    wuv = W.round_to_bf16((rng.standard_normal((n_h, 512, 128)) / np.sqrt(512)).astype(np.float32))
+    out = torch.full((B, 2, n_h, 128), float("nan"), device="cuda")
     mla.mla_out_proj(dims, torch.from_numpy(u).cuda(), torch.from_numpy(wuv).cuda().bfloat16(), out)
     torch.cuda.synchronize()
     ref = oracle.value_up_projection(u, wuv)
