@@ -133,25 +133,28 @@ static_assert(sizeof(DecodeSmemFp8) <= 160 * 1024, "LDS budget");
 // Cache layouts the kernel is compiled for.
 enum Layout : int {
   kContiguous = 0,   // [B][seq_stride] rows; a sequence's rows (plus one stage) span < 4 GiB
-  kPaged = 1,        // block table, block_size >= T (a stage meets at most two blocks)
+  kPaged = 1,        // block table, block_size a multiple of T (a stage lies in one block)
   kAnyLayout = 2,    // any block size: per-token row lookup
 };
 
-// Paged addressing of consecutive stages of T tokens (block_size >= T, so a
-// stage meets at most two blocks, k0 from row r0 on, then k1).  Stages come in
-// order, T tokens apart, so (k0, r0) follows from the previous stage without a
-// division (a restart recomputes it).  The block ids come from a window of 64
-// ids, one per lane (`ids`), reloaded when a stage leaves it (one vector load,
-// waited for right there: a wait placed by the compiler at the uses of `ids`
-// would sit on every stage's path and drain the stage loads in flight each
-// time; this one runs once per 64 blocks).  locate() gives the byte
-// offsets, from the resource base at block blk_lo, of the stage's rows: row
-// t < span + 1 of the stage is at off(t), rows past the segment end repeat its
-// last row (uint32 arithmetic, exact modulo 2^32).
+// Paged addressing of consecutive stages of T tokens.  The block size is a
+// multiple of T and every stage starts at a token that is a multiple of T
+// (the kernel starts a segment's stages at the multiple of T at or below its
+// first token), so a stage lies in one block: block k0 from row r0 on, with
+// r0 + T <= block_size.  Stages come in order, T tokens apart, so (k0, r0)
+// follows from the previous stage without a division (a restart recomputes
+// it).  The block ids come from a window of 64 ids, one per lane (`ids`),
+// reloaded when a stage leaves it (one vector load, waited for right there: a
+// wait placed by the compiler at the uses of `ids` would sit on every stage's
+// path and drain the stage loads in flight each time; this one runs once per
+// 64 blocks).  locate() gives the byte offset, from the resource base at block
+// blk_lo, of the stage's first row: row t < span + 1 of the stage is at
+// off0 + t * rb, rows past the segment end repeat its last row (uint32
+// arithmetic, exact modulo 2^32).
 struct PagedCursor {
   int ids, kbase;              // lane l holds the id of block kbase + l of the sequence
   int ntok, nk, nr;            // the next stage's first token, its block index and row in it
-  uint32_t off0, off1;         // row r0 of block k0; block k1 shifted back by bs - r0 rows
+  uint32_t off0;               // row r0 of block k0
   int r0, span, bs;
   uint32_t rb;                 // row bytes
 
@@ -172,28 +175,25 @@ struct PagedCursor {
     const int k0 = nk;
     r0 = nr;
     span = T - 1 < tok_end - 1 - tok0 ? T - 1 : tok_end - 1 - tok0;   // last row, from tok0
-    const int k1 = k0 + (r0 + span >= bs ? 1 : 0);
     ntok = tok0 + T;
     nr = r0 + T;
-    if (nr >= bs) {   // block_size >= T: at most one block boundary per stage
-      nr -= bs;
+    if (nr == bs) {   // the next stage starts the next block
+      nr = 0;
       ++nk;
     }
-    if (k0 < kbase || k1 - kbase >= 64) {
+    if (k0 < kbase || k0 - kbase >= 64) {
       kbase = k0;
       const int k = k0 + lane;
       ids = k <= (tok_end - 1) / bs ? c.block_table[(int64_t)b * c.max_blocks + k] : 0;
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
     }
     const int blk0 = __builtin_amdgcn_readlane(ids, k0 - kbase);
-    const int blk1 = __builtin_amdgcn_readlane(ids, k1 - kbase);
     off0 = (uint32_t)(blk0 - blk_lo) * block_bytes + (uint32_t)r0 * rb;
-    off1 = (uint32_t)(blk1 - blk_lo) * block_bytes - (uint32_t)(bs - r0) * rb;
   }
   // byte offset of stage row t (clamped to the segment's last row) plus `byte`
   __device__ __forceinline__ uint32_t row(int t, uint32_t byte) const {
     const int tt = t < span ? t : span;
-    return (r0 + tt < bs ? off0 : off1) + (uint32_t)tt * rb + byte;
+    return off0 + (uint32_t)tt * rb + byte;
   }
 };
 
@@ -205,7 +205,7 @@ struct PagedCursor {
 // Contiguous caches use buffer loads: the resource (SGPRs) spans the
 // segment's rows of one sequence, so tokens past the segment end fall out of
 // range and read as zeros (never the cache's padding); each lane keeps one
-// 32-bit offset.  Paged caches (block_size >= T) clamp such tokens to the last
+// 32-bit offset.  Paged caches (block_size a multiple of T) clamp such tokens to the last
 // row of the segment and also use buffer loads, from a resource that starts at
 // the lowest block of the segment (blk_lo); the caller takes this layout only
 // when every block of the segment lies within 4 GiB of that one (else the
@@ -553,10 +553,14 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
   const bool active = row0 < rows;
   const int jq = active ? row0 / a.n_h : 0;   // query token of this wave's QK rows
 
-  // one segment (tokens t0..t1-1 of sequence b, partial slot `slot`), its cache
-  // rows read through the stage loader of layout SL
-  auto segment = [&](auto layout_tag, int b, int t0, int t1, int slot, int blk_lo) {
+  // one segment (tokens t0_seg..t1-1 of sequence b, partial slot `slot`), its
+  // cache rows read through the stage loader of layout SL.  Stages cover T
+  // tokens from t0; in the paged layout t0 is the multiple of T at or below
+  // t0_seg (so that no stage meets two blocks) and the scores of the tokens
+  // before t0_seg, all in stage 0, are masked.
+  auto segment = [&](auto layout_tag, int b, int t0_seg, int t1, int slot, int blk_lo) {
     constexpr int SL = decltype(layout_tag)::value;
+    const int t0 = SL == kPaged ? (t0_seg & ~(T - 1)) : t0_seg;
     // ---- query operand (B of QK^T): row row0 + l32, k = 16*ks + 8*h .. +8
     bf16x8 qreg[KSTEPS];
     int limit = t1;
@@ -691,9 +695,11 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
       // Softmax of the raw scores in s_nx in small pieces of a few VALU ops,
       // one after each PV MFMA of the previous stage, so that the VALU work
       // runs while the matrix core is busy.  Two schedules:
-      //  - masked (stages that reach the row's limit; 30 pieces): 0-7 mask
-      //    scores of tokens at or past the limit (lim = limit minus the lane's
-      //    base token; INT_MIN masks all, leaving the weights zero), 8-11 lane
+      //  - masked (stages that reach the row's limit, and stage 0; 30 pieces):
+      //    0-7 mask scores of tokens at or past the limit (lim = limit minus the
+      //    lane's base token; INT_MIN masks all, leaving the weights zero) and,
+      //    in stage 0, of tokens before the segment's first (lo = t0_seg minus
+      //    the lane's base token), 8-11 lane
       //    maximum, 12 row maximum (the two lanes holding a row exchange
       //    theirs), 13 reference update, 14-29 one weight exp2(s*scale - m_ref);
       //  - visible (every token of the stage visible; 27 pieces), staggered so
@@ -706,12 +712,12 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
       float psum[2] = {0.f, 0.f};
       float t4[4];
       unsigned sw_mt[2];
-      auto sm_piece = [&](int k, int lim) {
+      auto sm_piece = [&](int k, int lim, int lo) {
         if (k < 8) {
 #pragma unroll
           for (int e = 2 * k; e < 2 * k + 2; ++e) {
             const int rel = 8 * (e >> 2) + (e & 3);      // token of s_nx[e] minus the lane's base token
-            s_nx[e] = rel < lim ? s_nx[e] : -INFINITY;
+            s_nx[e] = (rel < lim && rel >= lo) ? s_nx[e] : -INFINITY;
           }
         } else if (k < 12) {
           const int j = k - 8;
@@ -776,11 +782,12 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
         if (nst > 1) convert_stage(1, last);
       }
       lds_barrier();
-      if (active && t0 < limit) {
+      if (active && t0_seg < limit) {
         qk(stage_buf(0), NoLoads{}, nullptr);
         const int lim = lane_lim(t0);
+        const int lo = t0_seg - t0 - 4 * h;
 #pragma unroll
-        for (int k = 0; k < PIECES_MASKED; ++k) sm_piece(k, lim);
+        for (int k = 0; k < PIECES_MASKED; ++k) sm_piece(k, lim, lo);
         l_run += psum[0] + psum[1];
       }
 
@@ -802,7 +809,7 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
             for (int hb = 0; hb < 4; ++hb) {
               pv_mfma(o[mb][hb], cur, pq[hb]);
               if (VISIBLE) sm_piece_visible(16 * q + 4 * mb + hb);
-              else sm_piece(16 * q + 4 * mb + hb, lim);
+              else sm_piece(16 * q + 4 * mb + hb, lim, 0);   // (stages past 0 start inside the segment)
               __builtin_amdgcn_sched_barrier(0);
             }
           }
@@ -968,7 +975,7 @@ static void launch_decode_layout(const DecodeArgs& a, const DecodeParams& p, int
   // buffer offsets are 32-bit: a sequence plus one stage of overrun must fit
   if (p.cache.block_size == 0 && stride_bytes + (int64_t)T * rb <= (int64_t)0xFFFFFFFF)
     hipLaunchKernelGGL((decode_mfma_kernel<kContiguous, FP8>), dim3(grid), dim3(NT), 0, stream, a);
-  else if (p.cache.block_size >= T)
+  else if (p.cache.block_size % T == 0)
     hipLaunchKernelGGL((decode_mfma_kernel<kPaged, FP8>), dim3(grid), dim3(NT), 0, stream, a);
   else
     hipLaunchKernelGGL((decode_mfma_kernel<kAnyLayout, FP8>), dim3(grid), dim3(NT), 0, stream, a);

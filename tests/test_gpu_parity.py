@@ -148,9 +148,11 @@ def test_v3_paged_nan_poisoned(num_splits):
 
 @pytest.mark.parametrize("block_size,num_splits", [(16, 1), (16, 5), (40, 1), (40, 4), (96, 3)])
 def test_v3_paged_block_sizes(block_size, num_splits):
-    """Blocks smaller than one 32-token stage (per-lane row addresses) and block
-    sizes that are not powers of two (a stage straddles two blocks at varying
-    offsets), NaN in every unused pool slot."""
+    """Block sizes that are not a multiple of the 32-token stage (16, 40: the
+    generic layout, per-lane row addresses) and one that is a multiple but not
+    a power of two (96: segments cut at tokens that are not multiples of 32,
+    so stage 0 starts before the segment's first token and masks the tokens
+    before it), NaN in every unused pool slot."""
     _need_gpu()
     from workloads.device import stage
     w = W.custom(name=f"v3_paged_b{block_size}", seed=30 + block_size, batch=3, n_q=1, ctx=None,

@@ -10,7 +10,8 @@ GPU needed), finds the stage loops in the assembly (innermost loops that hold
 the MFMAs of a whole stage) and checks that those of the bf16 kernels, and the
 buffer-load (contiguous and paged) ones of the fp8 kernels, have no scratch
 access.  (The fp8 generic-layout loop does spill; that path only runs for
-paged caches whose blocks lie 4 GiB or more apart.)
+paged caches whose block size is not a multiple of 32 tokens or whose blocks
+lie 4 GiB or more apart.)
 """
 import os
 import re
