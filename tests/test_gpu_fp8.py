@@ -133,11 +133,14 @@ def test_fp8_v3_two_query_tokens(num_splits):
     _check(w, st, got)
 
 
-@pytest.mark.parametrize("block_size,num_splits", [(64, 1), (64, 3), (16, 1), (16, 5), (40, 4), (256, 2)])
+@pytest.mark.parametrize("block_size,num_splits",
+                         [(64, 1), (64, 3), (16, 1), (16, 5), (40, 4), (96, 3), (96, 7), (256, 2)])
 def test_fp8_v3_paged(block_size, num_splits):
-    """Paged fp8 caches: 64-token blocks (buffer loads from the lowest block),
-    16-token blocks (per-lane row addresses), 40 (stages straddle blocks at
-    varying offsets) and 256; 0xFF in every unused pool byte."""
+    """Paged fp8 caches: block sizes that are multiples of 32 tokens (64, 96,
+    256: buffer loads from the lowest block; segments cut at tokens that are
+    not multiples of 32 start their stages below the cut and mask the tokens
+    before it), and 16 and 40 (the generic layout, per-lane row addresses);
+    0xFF in every unused pool byte."""
     _need_gpu()
     from workloads.device import stage
     w = _fp8(name=f"fp8_paged_b{block_size}", seed=46 + block_size, batch=4, n_q=1, ctx=None,

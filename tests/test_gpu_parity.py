@@ -146,13 +146,14 @@ def test_v3_paged_nan_poisoned(num_splits):
     _check(w, st, got)
 
 
-@pytest.mark.parametrize("block_size,num_splits", [(16, 1), (16, 5), (40, 1), (40, 4), (96, 3)])
+@pytest.mark.parametrize("block_size,num_splits", [(16, 1), (16, 5), (40, 1), (40, 4), (96, 3), (96, 11)])
 def test_v3_paged_block_sizes(block_size, num_splits):
     """Block sizes that are not a multiple of the 32-token stage (16, 40: the
     generic layout, per-lane row addresses) and one that is a multiple but not
-    a power of two (96: segments cut at tokens that are not multiples of 32,
-    so stage 0 starts before the segment's first token and masks the tokens
-    before it), NaN in every unused pool slot."""
+    a power of two (96; with 11 splits the batch is cut at tokens 77 and 27,
+    not multiples of 32, so stage 0 of the segments after the cuts starts
+    before their first token and masks the tokens before it), NaN in every
+    unused pool slot."""
     _need_gpu()
     from workloads.device import stage
     w = W.custom(name=f"v3_paged_b{block_size}", seed=30 + block_size, batch=3, n_q=1, ctx=None,
