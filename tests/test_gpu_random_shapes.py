@@ -42,6 +42,26 @@ def _decode_cases(n=len(BLOCKS)):
     return cases
 
 
+# paged caches whose block size is a multiple of the 32-token stage, with many
+# splits: most segments then start at tokens that are not multiples of 32
+# (their first stage starts below the cut and masks the tokens before it)
+MANY_SPLIT_BLOCKS = (32, 64, 96, 128, 64, 96)
+
+
+def _many_split_cases():
+    rng = np.random.default_rng(0x5EC7)
+    cases = []
+    for k, block in enumerate(MANY_SPLIT_BLOCKS):
+        batch = int(rng.integers(2, 7))
+        n_q = int(rng.integers(1, 4))
+        ctx = [int(rng.integers(n_q, 900)) for _ in range(batch)]
+        splits = int(rng.integers(10, 61))
+        fp8 = k % 3 == 2
+        cases.append(pytest.param(100 + k, batch, n_q, ctx, block, splits, fp8,
+                                  id=f"m{k}-B{batch}-q{n_q}-blk{block}-s{splits}{'-fp8' if fp8 else ''}"))
+    return cases
+
+
 def _prefill_cases(n=5):
     rng = np.random.default_rng(0xBEE5)
     cases = []
@@ -53,7 +73,7 @@ def _prefill_cases(n=5):
     return cases
 
 
-@pytest.mark.parametrize("k,batch,n_q,ctx,block,splits,fp8", _decode_cases())
+@pytest.mark.parametrize("k,batch,n_q,ctx,block,splits,fp8", _decode_cases() + _many_split_cases())
 def test_random_decode_shape(k, batch, n_q, ctx, block, splits, fp8):
     par._need_gpu()
     from workloads.device import stage
