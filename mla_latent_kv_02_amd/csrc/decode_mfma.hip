@@ -927,16 +927,23 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(DecodeArgs a) {
       // this wave's block is in (only this wave reads it; the clobber keeps
       // the reads below the writes and the next block's writes below the reads)
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      // instruction it stores rows 2 it + oh of the block, 16 bytes per lane
+      // instruction it stores rows 2 it + oh of the block, 16 bytes per lane;
+      // the 16 reads go out together, then the stores (one read at a time,
+      // each store waited for its read's full latency)
       float* const ub = a.u_part + ((int64_t)slot * rows + grow0 + 32 * hb) * DC + 128 * wave;
       const int lo = oh * DC + 4 * ol32;
+      f32x4 v[16];
 #pragma unroll
       for (int it = 0; it < 16; ++it) {
         const int rr = 2 * it + oh;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(ob + 512 * rr + ((ol32 ^ rr) << 4));
-        if (grow0 + 32 * hb + rr < rows) *reinterpret_cast<f32x4*>(ub + 2 * DC * it + lo) = v;
-        __builtin_amdgcn_sched_barrier(0);
+        v[it] = *reinterpret_cast<const f32x4*>(ob + 512 * rr + ((ol32 ^ rr) << 4));
       }
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int rr = 2 * it + oh;
+        if (grow0 + 32 * hb + rr < rows) *reinterpret_cast<f32x4*>(ub + 2 * DC * it + lo) = v[it];
+      }
+      __builtin_amdgcn_sched_barrier(0);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
     // (the segment walker's barrier after this call keeps the ring and the
