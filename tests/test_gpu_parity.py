@@ -380,6 +380,42 @@ def test_combine_out_proj_against_oracle(num_splits, n_h, B):
     assert base <= slots
 
 
+@pytest.mark.parametrize("n_h,B", [(16, 40), (128, 45)])
+def test_merge_without_lse_output(n_h, B):
+    """mla_combine and mla_combine_out_proj with no lse output (a NULL pointer
+    at the C ABI): the other outputs are bit-identical to the calls with one,
+    for workgroups of one row block (16 heads) and of two (128 heads)."""
+    _need_gpu()
+    import mla_latent_kv_02_amd as mla
+    rng = np.random.default_rng(77 + n_h)
+    d_c, d_v, n_q, num_splits = 512, 128, 2, 7
+    dims = mla.Dims(n_h, d_c, 64, 128, d_v)
+    ctx = torch.from_numpy(rng.integers(1, 4000, size=B).astype(np.int32)).cuda()
+    slots = mla.mla_num_partials(B, num_splits)
+    lse = rng.standard_normal((slots, n_q, n_h)) * 4
+    ref = lse + rng.standard_normal((slots, n_q, n_h))
+    u_part = torch.from_numpy((rng.standard_normal((slots, n_q, n_h, d_c)) * np.exp(lse - ref)[..., None])
+                              .astype(np.float32)).cuda()
+    rl = torch.from_numpy(np.stack([ref, lse], axis=-1).astype(np.float32)).cuda()
+    wuv = torch.from_numpy(W.round_to_bf16((rng.standard_normal((n_h, d_c, d_v)) / np.sqrt(d_c))
+                                           .astype(np.float32))).cuda().bfloat16()
+    outs = []
+    for with_lse in (True, False):
+        u = torch.full((B, n_q, n_h, d_c), float("nan"), device="cuda")
+        o = torch.full((B, n_q, n_h, d_v), float("nan"), device="cuda")
+        l1 = torch.full((B, n_q, n_h), float("nan"), device="cuda") if with_lse else None
+        l2 = torch.full((B, n_q, n_h), float("nan"), device="cuda") if with_lse else None
+        mla.mla_combine(dims, ctx, num_splits, u_part, rl, u, l1)
+        mla.mla_combine_out_proj(dims, ctx, num_splits, u_part, rl, wuv, o, l2)
+        torch.cuda.synchronize()
+        outs.append((u.cpu(), o.cpu()))
+        if with_lse:
+            assert torch.isfinite(l1).all() and torch.allclose(l1, l2, rtol=1e-5, atol=1e-5)
+    assert torch.isfinite(outs[0][0]).all() and torch.isfinite(outs[0][1]).all()
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1], outs[1][1])
+
+
 # 16 heads x 10 rows: workgroups of one row block; 128 heads x 90 rows:
 # workgroups of two, the last one's second block past the batch end
 @pytest.mark.parametrize("n_h,B", [(16, 5), (128, 45)])
