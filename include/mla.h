@@ -96,6 +96,8 @@ typedef struct {
  * ctx_lens [B]: number of cached tokens of each sequence (the query tokens'
  * own rows included).  `data` must be 16-byte aligned.  A contiguous cache
  * needs seq_stride >= one row (d_c + d_rope elements; the fp8 row's bytes).
+ * Any block size is accepted; the decode's fast paged path takes block sizes
+ * that are multiples of 32 tokens (others read rows one by one, slower).
  *
  * fp8 cache (dtype MLA_FP8_E4M3; [Huny], serving checklist, fp8 KV-cache item
  * and [Paldyn], KV-cache quantisation: per-block scales rather than one
